@@ -1,0 +1,288 @@
+#!/usr/bin/env python3
+"""Benchmark of the write-time FP8 ring KV-cache hot path on one MI355X.
+
+One step = one layer call of the path, the unit the Runway Characters pages count 240 of per
+chunk (abstract of arXiv 2611.05642): kv_ring_write of 757 new tokens (RoPE + per-head FP8)
+into a full 5,788-slot ring, then ring_attention of 757 queries over all 5,788 slots, with 24
+heads x head_dim 128 as one GPU's share.  Inputs are seeded synthetic N(0,1) bfloat16 tensors
+already resident in device memory.  `value` is steps per second, i.e. ring_attention calls per
+second including their write.
+
+Also reported (one JSON line on stdout; progress on stderr):
+  attention   the main attention kernel alone, timed with HIP events recorded on its launch
+              stream around each launch (53.84 GFLOP algorithmic per call: 4 * 757 * 5788 *
+              128 * 24), as a fraction of the FP8 matrix-core peak -> the `roofline` object;
+  write       kv_ring_write per call (14.10 MB algorithmic: bf16 K and V read, FP8 codes and
+              per-slot scales written) as a fraction of HBM peak;
+  delta_rotate kv_ring_delta_rotate of one full ring (36.67 MB algorithmic: K codes and
+              scales read and written);
+  chunk       240 (write + attention) calls over 60 rings, 4 passes, as one chunk;
+  cpu_baseline the CPU oracle on the same step (full call), on the host's cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "ring_attention calls/s at 757×5788×d128 (%FP8 MFMA peak); kv write GB/s"
+H, S, D, N = 24, 5788, 128, 757
+ROPE_POS = 16384
+FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 matrix-core peak
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E peak
+ATT_FLOP = 4.0 * N * S * D * H
+WRITE_BYTES = 2 * N * H * D * 2 + 2 * N * H * D + 2 * N * H * 4
+ROTATE_BYTES = 2 * (H * S * D + H * S * 4)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--no-chunk", action="store_true", help="skip the 240-call chunk measurement")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of heads on one GPU; --gpus {args.gpus} is not "
+              "supported (the path shards by heads with no exchange; see the design notes).",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import fp8_ring_kv_write_amd as kv
+    from workloads import normal_bf16, tensor_seed, steady_ring_schedule
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    tab = torch.from_numpy(kv.rope_table(ROPE_POS, D)).to(dev)
+    ring = kv.Ring(H, S, D, dev)
+    sched = steady_ring_schedule(S, N, 8)
+    filled = 0
+    for c, w in enumerate(sched):
+        kv.kv_ring_write(ring, to_dev(normal_bf16(tensor_seed("single_call", c, 1), (N, H, D))),
+                         to_dev(normal_bf16(tensor_seed("single_call", c, 2), (N, H, D))),
+                         w.start_slot, w.pos0, tab)
+        filled = min(filled + N, S)
+    head = (sched[-1].start_slot + N) % S
+    assert (head, filled) == (268, S)
+    # the step rewrites the newest chunk's slots (as each denoising pass does) and attends
+    start, pos0 = sched[-1].start_slot, sched[-1].pos0
+    k_new = to_dev(normal_bf16(tensor_seed("single_call", 100, 1), (N, H, D)))
+    v_new = to_dev(normal_bf16(tensor_seed("single_call", 100, 2), (N, H, D)))
+    q = to_dev(normal_bf16(tensor_seed("single_call", 99, 0), (N, H, D)))
+    scale = 1.0 / math.sqrt(D)
+    ws_w = torch.empty(kv.workspace_bytes(kv.OP_WRITE, H, S, D, N), dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(kv.workspace_bytes(kv.OP_ATTENTION, H, S, D, N), dtype=torch.uint8, device=dev)
+    ws_r = torch.empty(kv.workspace_bytes(kv.OP_DELTA_ROTATE, H, S, D, 0), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((H, N), dtype=torch.float32, device=dev)
+
+    def step():
+        kv.kv_ring_write(ring, k_new, v_new, start, pos0, tab, workspace=ws_w, stream=stream)
+        kv.ring_attention(ring, head, filled, q, pos0, tab, scale, out=out, lse=lse, workspace=ws_a,
+                          stream=stream)
+
+    # ---------------------------------------------------------------- the timed steps
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1) / args.steps
+    ms_per_step = wall * 1000.0 / args.steps
+    log(f"step: {ms_per_step * 1000:.1f} us wall, {gpu_ms * 1000:.1f} us GPU")
+
+    # ---------------------------------------------------------------- attention kernel alone
+    reps = max(50, args.steps // 2)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    calls = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for b, a in evs:        # torch creates the HIP event on its first record(); the library then
+        b.record(stream)    # re-records the same events around the attention kernel
+        a.record(stream)
+    for b, a in evs[:5]:
+        kv.set_attention_events(b, a)
+        kv.ring_attention(ring, head, filled, q, pos0, tab, scale, out=out, lse=lse, workspace=ws_a, stream=stream)
+    torch.cuda.synchronize()
+    for (b, a), (cb, ca) in zip(evs, calls):
+        kv.set_attention_events(b, a)
+        cb.record(stream)
+        kv.ring_attention(ring, head, filled, q, pos0, tab, scale, out=out, lse=lse, workspace=ws_a, stream=stream)
+        ca.record(stream)
+    kv.set_attention_events(None, None)
+    torch.cuda.synchronize()
+    att_us = 1000.0 * sum(b.elapsed_time(a) for b, a in evs) / reps
+    call_us = 1000.0 * sum(b.elapsed_time(a) for b, a in calls) / reps
+    att_tflops = ATT_FLOP / (att_us * 1e-6) / 1e12
+    log(f"attention kernel {att_us:.1f} us ({att_tflops:.0f} TFLOP/s), whole call {call_us:.1f} us")
+
+    # ---------------------------------------------------------------- write alone
+    wev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for _ in range(5):
+        kv.kv_ring_write(ring, k_new, v_new, start, pos0, tab, workspace=ws_w, stream=stream)
+    for b, a in wev:
+        b.record(stream)
+        kv.kv_ring_write(ring, k_new, v_new, start, pos0, tab, workspace=ws_w, stream=stream)
+        a.record(stream)
+    torch.cuda.synchronize()
+    write_us = 1000.0 * sum(b.elapsed_time(a) for b, a in wev) / reps
+    write_gbps = WRITE_BYTES / (write_us * 1e-6) / 1e9
+    log(f"write {write_us:.1f} us ({write_gbps:.0f} GB/s)")
+
+    # ---------------------------------------------------------------- delta rotation of one ring
+    rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i, (b, a) in enumerate(rev):
+        b.record(stream)
+        kv.kv_ring_delta_rotate(ring, head, filled, -4000 if i % 2 == 0 else 4000, workspace=ws_r, stream=stream)
+        a.record(stream)
+    torch.cuda.synchronize()
+    rot_us = 1000.0 * sum(b.elapsed_time(a) for b, a in rev) / reps
+    rot_gbps = ROTATE_BYTES / (rot_us * 1e-6) / 1e9
+    log(f"delta rotate {rot_us:.1f} us ({rot_gbps:.0f} GB/s)")
+
+    # ---------------------------------------------------------------- a 240-call chunk over 60 rings
+    chunk = None
+    if not args.no_chunk:
+        layers, passes = 60, 4
+        rings = [ring]
+        for _ in range(layers - 1):
+            r = kv.Ring(H, S, D, dev)
+            r.k.copy_(ring.k)
+            r.v.copy_(ring.v)
+            r.k_scale.copy_(ring.k_scale)
+            r.v_scale.copy_(ring.v_scale)
+            rings.append(r)
+        gen = torch.Generator(device=dev)
+        inputs = []
+        for p in range(passes):
+            for l in range(layers):
+                gen.manual_seed(tensor_seed("full_chunk", p, l))
+                inputs.append(tuple(torch.randn((N, H, D), generator=gen, device=dev).to(torch.bfloat16)
+                                    for _ in range(3)))
+
+        def run_chunk():
+            for p in range(passes):
+                for l in range(layers):
+                    kk, vv, qq = inputs[p * layers + l]
+                    kv.kv_ring_write(rings[l], kk, vv, start, pos0, tab, workspace=ws_w, stream=stream)
+                    kv.ring_attention(rings[l], head, filled, qq, pos0, tab, scale, out=out, lse=lse,
+                                      workspace=ws_a, stream=stream)
+
+        run_chunk()
+        torch.cuda.synchronize()
+        reps_c = 5
+        t0 = time.perf_counter()
+        for _ in range(reps_c):
+            run_chunk()
+        torch.cuda.synchronize()
+        chunk_ms = (time.perf_counter() - t0) * 1000.0 / reps_c
+        chunk = {"calls": passes * layers, "layers": layers, "passes": passes, "ms": round(chunk_ms, 3)}
+        log(f"chunk of 240 calls: {chunk_ms:.2f} ms")
+        del inputs, rings
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(np, sched, k_new, v_new, q, start, pos0, scale)
+
+    value = 1000.0 / ms_per_step
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "calls/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3",
+        "data": "synthetic: seeded N(0,1) bfloat16 Q/K/V, ring pre-filled by 8 writes",
+        "config": {
+            "workload": "one layer call: kv_ring_write of 757 tokens + ring_attention of 757 queries "
+                        "over a full 5788-slot FP8 ring, 24 heads x d128 (one GPU's share)",
+            "heads": H, "slots": S, "head_dim": D, "new_tokens": N, "queries": N,
+        },
+        "gpu_ms_per_step": round(gpu_ms, 5),
+        "attention": {"kernel_us": round(att_us, 2), "call_us": round(call_us, 2),
+                      "tflops": round(att_tflops, 1), "frac_fp8_peak": round(att_tflops / FP8_PEAK_TFLOPS, 4),
+                      "calls_per_s": round(1e6 / call_us, 1)},
+        "write": {"us": round(write_us, 2), "GBps": round(write_gbps, 1),
+                  "frac_hbm_peak": round(write_gbps / HBM_PEAK_GBPS, 4), "bytes": WRITE_BYTES},
+        "delta_rotate": {"us": round(rot_us, 2), "GBps": round(rot_gbps, 1),
+                         "frac_hbm_peak": round(rot_gbps / HBM_PEAK_GBPS, 4), "bytes": ROTATE_BYTES},
+        "chunk": chunk,
+        "roofline": {"bound": "mfma", "achieved": round(att_tflops, 1), "peak": FP8_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(att_tflops / FP8_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "attn_main<128>", "flop_per_launch": ATT_FLOP},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def cpu_baseline(np, sched, k_new, v_new, q, start, pos0, scale):
+    """The oracle (as it stands) on the same step: write of 757 tokens + attention of 757
+    queries over the full ring, 24 heads.  Ring prefill is not timed."""
+    import oracle
+    from workloads import normal_bf16, tensor_seed
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    table = oracle.rope_table(ROPE_POS, D)
+    ring = oracle.OracleRing(H, S, D)
+    filled = 0
+    for c, w in enumerate(sched):
+        oracle.ring_write(ring, normal_bf16(tensor_seed("single_call", c, 1), (N, H, D)),
+                          normal_bf16(tensor_seed("single_call", c, 2), (N, H, D)), w.start_slot, w.pos0, table)
+        filled = min(filled + N, S)
+    head = (sched[-1].start_slot + N) % S
+    kb = k_new.view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+    vb = v_new.view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+    qb = q.view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.ring_write(ring, kb, vb, start, pos0, table)
+        oracle.ring_attention(ring, head, filled, qb, pos0, table, scale)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el > 10.0 or reps >= 5:
+            break
+    log(f"cpu oracle: {el / reps:.2f} s per step on {threads} threads")
+    return {"value": round(reps / el, 4), "unit": "calls/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} full steps (write 757 tokens + attention 757x5788, 24 heads x d128), "
+                      "numpy float64 attention"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,28 @@
+"""MI355X FP8 ring KV cache: Python binding of libkvring.so.
+
+Argument marshalling only -- every step of the write, the delta rotation and the attention
+runs in the HIP kernels behind the C ABI (include/kvring.h).  PyTorch provides device memory
+and streams.  Importing this package loads the library and fails loudly when it is missing;
+there is no fallback of any kind.
+"""
+
+from ._lib import (  # noqa: F401
+    KvRingError,
+    Ring,
+    OP_WRITE,
+    OP_DELTA_ROTATE,
+    OP_ATTENTION,
+    TILE,
+    library_path,
+    codes_bytes,
+    v_pos,
+    rope_table,
+    workspace_bytes,
+    kv_ring_write,
+    kv_ring_delta_rotate,
+    ring_attention,
+    fp8_encode,
+    set_attention_events,
+    status_string,
+    lib,
+)

@@ -1,0 +1,199 @@
+"""ctypes binding of the C ABI in include/kvring.h (same names, same arguments)."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(HERE, "libkvring.so")
+
+OP_WRITE, OP_DELTA_ROTATE, OP_ATTENTION = 1, 2, 3
+TILE = 128
+
+
+class KvRingError(RuntimeError):
+    """A C-ABI call returned a negative status."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
+        ("heads", ctypes.c_int32),
+        ("slots", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+    ]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: build it first (python -m fp8_ring_kv_write_amd.build "
+            "or __graft_entry__.build()).  There is no fallback path.")
+    L = ctypes.CDLL(_LIB_PATH)
+    i32, i64, vp, f32, f64, sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float,
+                                  ctypes.c_double, ctypes.c_size_t)
+    dp = ctypes.POINTER(_Desc)
+    sig = {
+        "kv_ring_codes_bytes": (i64, [i32, i32, i32]),
+        "kv_ring_v_pos": (i32, [i32]),
+        "kv_ring_rope_table": (ctypes.c_int, [vp, i64, i32, f64]),
+        "kv_ring_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
+        "kv_ring_write": (ctypes.c_int, [dp, vp, vp, i32, i32, i64, vp, i64, vp, sz, vp]),
+        "kv_ring_delta_rotate": (ctypes.c_int, [dp, i32, i32, i64, f64, vp, sz, vp]),
+        "ring_attention": (ctypes.c_int, [dp, i32, i32, vp, i32, i64, vp, i64, f32, vp, vp, vp, sz, vp]),
+        "kv_ring_fp8_encode": (ctypes.c_int, [vp, vp, i64, vp]),
+        "kv_ring_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "kv_ring_set_attention_events": (ctypes.c_int, [vp, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    return L
+
+
+lib = _load()
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def status_string(status: int) -> str:
+    return lib.kv_ring_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise KvRingError(fn, status)
+
+
+def codes_bytes(heads: int, slots: int, head_dim: int) -> int:
+    return int(lib.kv_ring_codes_bytes(heads, slots, head_dim))
+
+
+def v_pos(u: int) -> int:
+    return int(lib.kv_ring_v_pos(u))
+
+
+def rope_table(n_pos: int, head_dim: int, base: float = 10000.0) -> np.ndarray:
+    """Host float32 [n_pos, head_dim/2, 2] cos/sin table filled by the library."""
+    out = np.empty((n_pos, head_dim // 2, 2), dtype=np.float32)
+    _check("kv_ring_rope_table", lib.kv_ring_rope_table(out.ctypes.data, n_pos, head_dim, base))
+    return out
+
+
+def workspace_bytes(op: int, heads: int, slots: int, head_dim: int, n: int) -> int:
+    return int(lib.kv_ring_workspace_bytes(op, heads, slots, head_dim, n))
+
+
+def _stream(stream, device) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t) -> int:
+    return int(t.data_ptr())
+
+
+class Ring:
+    """Device buffers of one ring (one layer, `heads` heads), allocated with torch.
+
+    k, v: uint8 code buffers in the library layout; k_scale, v_scale: float32 [heads, slots].
+    Fresh rings hold zero codes and unit scales."""
+
+    def __init__(self, heads: int, slots: int, head_dim: int, device="cuda"):
+        import torch
+        nbytes = codes_bytes(heads, slots, head_dim)
+        if nbytes <= 0:
+            raise ValueError("unsupported ring shape")
+        self.heads, self.slots, self.head_dim = heads, slots, head_dim
+        self.tiles = (slots + TILE - 1) // TILE
+        self.device = torch.device(device)
+        self.k = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
+        self.v = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
+        self.k_scale = torch.ones((heads, slots), dtype=torch.float32, device=self.device)
+        self.v_scale = torch.ones((heads, slots), dtype=torch.float32, device=self.device)
+        self._desc = _Desc(_ptr(self.k), _ptr(self.v), _ptr(self.k_scale), _ptr(self.v_scale),
+                           heads, slots, head_dim)
+
+    @property
+    def desc(self):
+        return ctypes.byref(self._desc)
+
+
+def _ws(ws, need: int, device):
+    import torch
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    return ws, int(ws.numel() * ws.element_size())
+
+
+def kv_ring_write(ring: Ring, k_new, v_new, start_slot: int, pos0: int, rope, workspace=None,
+                  stream=None) -> None:
+    """k_new, v_new: bfloat16 [n, heads, head_dim] device tensors; rope: device float32 table."""
+    n = int(k_new.shape[0])
+    need = workspace_bytes(OP_WRITE, ring.heads, ring.slots, ring.head_dim, max(n, 1))
+    ws, wsb = _ws(workspace, need, ring.device)
+    _check("kv_ring_write", lib.kv_ring_write(
+        ring.desc, _ptr(k_new), _ptr(v_new), n, start_slot, pos0, _ptr(rope), int(rope.shape[0]),
+        _ptr(ws), wsb, _stream(stream, ring.device)))
+
+
+def kv_ring_delta_rotate(ring: Ring, ring_head: int, filled: int, delta: int,
+                         rope_base: float = 10000.0, workspace=None, stream=None) -> None:
+    need = workspace_bytes(OP_DELTA_ROTATE, ring.heads, ring.slots, ring.head_dim, 0)
+    ws, wsb = _ws(workspace, need, ring.device)
+    _check("kv_ring_delta_rotate", lib.kv_ring_delta_rotate(
+        ring.desc, ring_head, filled, delta, rope_base, _ptr(ws), wsb, _stream(stream, ring.device)))
+
+
+def ring_attention(ring: Ring, ring_head: int, filled: int, q, q_pos0: int, rope,
+                   softmax_scale: float, out=None, lse=None, workspace=None, stream=None):
+    """q: bfloat16 [nq, heads, head_dim].  Returns (out bfloat16 [nq, heads, head_dim],
+    lse float32 [heads, nq])."""
+    import torch
+    nq = int(q.shape[0])
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((ring.heads, nq), dtype=torch.float32, device=q.device)
+    need = workspace_bytes(OP_ATTENTION, ring.heads, ring.slots, ring.head_dim, max(nq, 1))
+    ws, wsb = _ws(workspace, need, ring.device)
+    _check("ring_attention", lib.ring_attention(
+        ring.desc, ring_head, filled, _ptr(q), nq, q_pos0, _ptr(rope), int(rope.shape[0]),
+        float(softmax_scale), _ptr(out), _ptr(lse), _ptr(ws), wsb, _stream(stream, ring.device)))
+    return out, lse
+
+
+def fp8_encode(x, out=None, stream=None):
+    """E4M3 codes of a float32 device tensor with the kernels' encoder."""
+    import torch
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _check("kv_ring_fp8_encode", lib.kv_ring_fp8_encode(_ptr(x), _ptr(out), int(x.numel()),
+                                                        _stream(stream, x.device)))
+    return out
+
+
+def set_attention_events(before=None, after=None) -> None:
+    """Record torch.cuda.Event `before`/`after` around each later ring_attention call's main
+    kernel (both None: off).  The events must have been recorded once through torch (which
+    creates the underlying HIP event lazily).  Profiling aid; see include/kvring.h."""
+    b = None if before is None else int(before.cuda_event)
+    a = None if after is None else int(after.cuda_event)
+    if (before is not None or after is not None) and not (a and b):
+        raise ValueError("record the events once (event.record()) before handing them over")
+    lib.kv_ring_set_attention_events(b if (a and b) else None, a if (a and b) else None)

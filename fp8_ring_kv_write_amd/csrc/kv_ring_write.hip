@@ -1,0 +1,251 @@
+// kv_ring_write: write-time RoPE + per-head FP8 quantisation of new K/V tokens into the ring
+// (Runway Characters abstract: RoPE and FP8 quantisation applied once per write into a ring
+// cache; cpdf.ai blog, section "Como rodar 57B em tempo real com batch size 1").
+//
+// Two bandwidth-bound passes, no atomics:
+//   1. rope_absmax_partials: each work-group takes 32 tokens x 1 head, rotates K, and writes
+//      the max |K'| and max |V| of its rows to a per-(tensor, head, group) partial;
+//   2. write_quantize: each work-group takes one aligned 32-slot chunk of the ring x 1 head,
+//      reduces the head's partials to the write's absmax, rotates and quantises again, and
+//      stores K codes row-major and V codes into the transposed tile layout.
+// The second read of the bf16 inputs is served mostly from the L2 / infinity cache.
+//
+// Arithmetic is float32 with every product and sum rounded separately (the translation
+// unit is compiled with -ffp-contract=off) so the codes match the CPU oracle bit for bit.
+
+#include "kvring_common.hpp"
+#include "kvring_internal.hpp"
+
+namespace kvring {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// Load CPT bf16 channels starting at `p` (16-byte aligned) into floats.
+template <int CPT>
+__device__ inline void load_bf16(const uint16_t* p, float (&x)[CPT]) {
+  const uint4* q = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+  for (int j = 0; j < CPT / 8; ++j) {
+    uint4 w = q[j];
+    uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[8 * j + 2 * e] = __uint_as_float(ws[e] << 16);
+      x[8 * j + 2 * e + 1] = __uint_as_float(ws[e] & 0xFFFF0000u);
+    }
+  }
+}
+
+// Rotate CPT channels (CPT/2 interleaved pairs) with the table row of this position.
+// `tab` points at the (cos, sin) of the first pair; 16-byte aligned.
+template <int CPT>
+__device__ inline void rope_pairs(float (&x)[CPT], const float* tab) {
+  const float4* t4 = reinterpret_cast<const float4*>(tab);
+#pragma unroll
+  for (int j = 0; j < CPT / 4; ++j) {
+    float4 t = t4[j];  // cos0 sin0 cos1 sin1 for pairs 2j, 2j+1
+    float cs[2][2] = {{t.x, t.y}, {t.z, t.w}};
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int p = 2 * j + e;
+      const float xe = x[2 * p], xo = x[2 * p + 1];
+      const float c = cs[e][0], s = cs[e][1];
+      x[2 * p] = xe * c - xo * s;
+      x[2 * p + 1] = xe * s + xo * c;
+    }
+  }
+}
+
+template <int CPT>
+__device__ inline float absmax(const float (&x)[CPT]) {
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) m = __builtin_fmaxf(m, __builtin_fabsf(x[j]));
+  return m;
+}
+
+// Pass 1.  grid = (ceil(n/32), heads, tensors); tensor 0 is rotated (K or Q), tensor 1 (V) is
+// not.  partial layout [tensor][heads][ngroups].
+template <int D>
+__global__ __launch_bounds__(kThreads) void rope_absmax_partials(
+    const uint16_t* __restrict__ x0, const uint16_t* __restrict__ x1, int32_t n, int32_t heads,
+    int64_t pos0, const float* __restrict__ rope, float* __restrict__ partial) {
+  constexpr int CPT = D / 8;
+  __shared__ float red[4];
+  const int grp = blockIdx.x, h = blockIdx.y, tensor = blockIdx.z;
+  const int i = grp * kChunk + (threadIdx.x >> 3);
+  const int cg = threadIdx.x & 7;
+  float m = 0.0f;
+  if (i < n) {
+    const uint16_t* src = (tensor == 0 ? x0 : x1) + ((int64_t)i * heads + h) * D + cg * CPT;
+    float x[CPT];
+    load_bf16<CPT>(src, x);
+    if (tensor == 0) rope_pairs<CPT>(x, rope + ((pos0 + i) * (D / 2) + cg * (CPT / 2)) * 2);
+    m = absmax<CPT>(x);
+  }
+  m = block_max_256(m, red);
+  if (threadIdx.x == 0) partial[((int64_t)tensor * heads + h) * gridDim.x + grp] = m;
+}
+
+struct WriteGeom {
+  int32_t n, start, slots, heads;
+  int32_t chunk_a0, n_chunks_a;  // first chunk of the run [start, min(start+n, slots))
+  int32_t n_partial_groups;      // partial groups per (tensor, head) from pass 1
+  int64_t tiles;
+  int64_t pos0;
+};
+
+// Pass 2.  grid = (chunks touched by the write, heads).
+template <int D>
+__global__ __launch_bounds__(kThreads) void write_quantize(
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const float* __restrict__ rope, const float* __restrict__ partial, WriteGeom g,
+    uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, float* __restrict__ k_scale,
+    float* __restrict__ v_scale) {
+  constexpr int CPT = D / 8;
+  __shared__ float red[2][4];
+  __shared__ __align__(16) uint8_t vlds[kChunk][D];
+  const int h = blockIdx.y;
+  const int chunk = blockIdx.x < g.n_chunks_a ? g.chunk_a0 + blockIdx.x : blockIdx.x - g.n_chunks_a;
+
+  // the write's per-head absmax of K' and V from the pass-1 partials
+  float ak = 0.0f, av = 0.0f;
+  for (int j = threadIdx.x; j < g.n_partial_groups; j += kThreads) {
+    ak = __builtin_fmaxf(ak, partial[(int64_t)h * g.n_partial_groups + j]);
+    av = __builtin_fmaxf(av, partial[((int64_t)g.heads + h) * g.n_partial_groups + j]);
+  }
+  ak = block_max_256(ak, red[0]);
+  av = block_max_256(av, red[1]);
+  float sk, ik, sv, iv;
+  scale_from_absmax(ak, sk, ik);
+  scale_from_absmax(av, sv, iv);
+
+  const int t = threadIdx.x >> 3, cg = threadIdx.x & 7;
+  const int slot = chunk * kChunk + t;
+  int i = slot - g.start;
+  i = i < 0 ? i + g.slots : i;
+  const bool mine = slot < g.slots && i < g.n;
+  if (mine) {
+    const int64_t src = ((int64_t)i * g.heads + h) * D + cg * CPT;
+    float x[CPT];
+    load_bf16<CPT>(k_new + src, x);
+    rope_pairs<CPT>(x, rope + ((g.pos0 + i) * (D / 2) + cg * (CPT / 2)) * 2);
+    uint32_t w[CPT / 4];
+#pragma unroll
+    for (int j = 0; j < CPT / 4; ++j)
+      w[j] = e4m3x4(x[4 * j] * ik, x[4 * j + 1] * ik, x[4 * j + 2] * ik, x[4 * j + 3] * ik);
+    uint8_t* dst = kc + ((int64_t)h * g.tiles * kTile + slot) * D + cg * CPT;
+    if constexpr (CPT == 16) {
+      *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+      *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+    }
+    load_bf16<CPT>(v_new + src, x);
+#pragma unroll
+    for (int j = 0; j < CPT / 4; ++j)
+      w[j] = e4m3x4(x[4 * j] * iv, x[4 * j + 1] * iv, x[4 * j + 2] * iv, x[4 * j + 3] * iv);
+    uint32_t* vl = reinterpret_cast<uint32_t*>(&vlds[t][cg * CPT]);
+#pragma unroll
+    for (int j = 0; j < CPT / 4; ++j) vl[j] = w[j];
+    if (cg == 0) {
+      k_scale[(int64_t)h * g.slots + slot] = sk;
+      v_scale[(int64_t)h * g.slots + slot] = sv;
+    }
+  }
+  __syncthreads();
+
+  // V: transposed tile rows.  Work item = (channel d, group of 4 consecutive slots q); the
+  // four slots land in 4 consecutive bytes of row d.
+  const int64_t tile = (int64_t)chunk * kChunk / kTile;
+  const int u0 = (chunk * kChunk) % kTile;
+  for (int item = threadIdx.x; item < D * (kChunk / 4); item += kThreads) {
+    const int d = item >> 3, q = item & 7;
+    uint8_t* row = vc + (((int64_t)h * g.tiles + tile) * D + d) * kTile + vt_pos(u0 + 4 * q);
+    uint32_t word = 0;
+    int nmine = 0;
+    bool m4[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int s = chunk * kChunk + 4 * q + r;
+      int ii = s - g.start;
+      ii = ii < 0 ? ii + g.slots : ii;
+      m4[r] = s < g.slots && ii < g.n;
+      nmine += m4[r];
+      word |= uint32_t(vlds[4 * q + r][d]) << (8 * r);
+    }
+    if (nmine == 4) {
+      *reinterpret_cast<uint32_t*>(row) = word;
+    } else if (nmine > 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (m4[r]) row[r] = uint8_t(word >> (8 * r));
+    }
+  }
+}
+
+}  // namespace
+
+int64_t write_workspace_floats(int32_t heads, int32_t n) {
+  return 2LL * heads * ((n + kChunk - 1) / kChunk);
+}
+
+hipError_t launch_write(const kv_ring_desc& r, const uint16_t* k_new, const uint16_t* v_new,
+                        int32_t n, int32_t start_slot, int64_t pos0, const float* rope,
+                        float* ws, hipStream_t stream) {
+  const int ngroups = (n + kChunk - 1) / kChunk;
+  dim3 g1(ngroups, r.heads, 2);
+  if (r.head_dim == 128)
+    hipLaunchKernelGGL(rope_absmax_partials<128>, g1, dim3(kThreads), 0, stream, k_new, v_new, n,
+                       r.heads, pos0, rope, ws);
+  else
+    hipLaunchKernelGGL(rope_absmax_partials<64>, g1, dim3(kThreads), 0, stream, k_new, v_new, n,
+                       r.heads, pos0, rope, ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  WriteGeom g;
+  g.n = n;
+  g.start = start_slot;
+  g.slots = r.slots;
+  g.heads = r.heads;
+  g.tiles = tile_count(r.slots);
+  g.pos0 = pos0;
+  g.n_partial_groups = ngroups;
+  const int end_a = start_slot + n < r.slots ? start_slot + n : r.slots;
+  g.chunk_a0 = start_slot / kChunk;
+  g.n_chunks_a = (end_a - 1) / kChunk - g.chunk_a0 + 1;
+  int n_chunks_b = 0;
+  if (start_slot + n > r.slots) {
+    const int end_b = start_slot + n - r.slots;  // run [0, end_b)
+    n_chunks_b = (end_b - 1) / kChunk + 1;
+    // a chunk holding both the end of the wrapped run and the start of the first run is
+    // handled once, by the first run's work-group
+    if ((end_b - 1) / kChunk == g.chunk_a0) n_chunks_b -= 1;
+  }
+  dim3 g2(g.n_chunks_a + n_chunks_b, r.heads);
+  if (r.head_dim == 128)
+    hipLaunchKernelGGL(write_quantize<128>, g2, dim3(kThreads), 0, stream, k_new, v_new, rope, ws,
+                       g, r.k, r.v, r.k_scale, r.v_scale);
+  else
+    hipLaunchKernelGGL(write_quantize<64>, g2, dim3(kThreads), 0, stream, k_new, v_new, rope, ws,
+                       g, r.k, r.v, r.k_scale, r.v_scale);
+  return hipGetLastError();
+}
+
+// Q partials for the attention prologue reuse pass 1 (tensor 0 only).
+hipError_t launch_q_absmax(const uint16_t* q, int32_t nq, int32_t heads, int32_t head_dim,
+                           int64_t q_pos0, const float* rope, float* partial, hipStream_t stream) {
+  const int ngroups = (nq + kChunk - 1) / kChunk;
+  dim3 g1(ngroups, heads, 1);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(rope_absmax_partials<128>, g1, dim3(kThreads), 0, stream, q, q, nq, heads,
+                       q_pos0, rope, partial);
+  else
+    hipLaunchKernelGGL(rope_absmax_partials<64>, g1, dim3(kThreads), 0, stream, q, q, nq, heads,
+                       q_pos0, rope, partial);
+  return hipGetLastError();
+}
+
+}  // namespace kvring

@@ -1,0 +1,176 @@
+// C ABI of the FP8 ring KV cache: argument checks, host-side tables, workspace sizing, and
+// dispatch to the kernels.  No entry point allocates device memory or synchronises.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/kvring.h"
+#include "kvring_common.hpp"
+#include "kvring_internal.hpp"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_ring(const kv_ring_desc* r) {
+  if (!r) return KV_RING_ERR_NULL;
+  if (!r->k || !r->v || !r->k_scale || !r->v_scale) return KV_RING_ERR_NULL;
+  if (r->heads < 1 || r->heads > 65535 || r->slots < 1 || r->slots > (1 << 20)) return KV_RING_ERR_SHAPE;
+  if (r->head_dim != 64 && r->head_dim != 128) return KV_RING_ERR_SHAPE;
+  if (!aligned(r->k, 16) || !aligned(r->v, 16) || !aligned(r->k_scale, 4) || !aligned(r->v_scale, 4))
+    return KV_RING_ERR_ALIGN;
+  return KV_RING_OK;
+}
+
+int check_workspace(void* ws, size_t have, size_t need) {
+  if (need == 0) return KV_RING_OK;
+  if (!ws) return KV_RING_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return KV_RING_ERR_ALIGN;
+  if (have < need) return KV_RING_ERR_WORKSPACE;
+  return KV_RING_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? KV_RING_OK : KV_RING_ERR_LAUNCH; }
+
+double rope_theta(int32_t i, int32_t head_dim, double base) {
+  return std::pow(base, -(2.0 * i) / (double)head_dim);
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t kv_ring_codes_bytes(int32_t heads, int32_t slots, int32_t head_dim) {
+  if (heads < 1 || slots < 1 || (head_dim != 64 && head_dim != 128)) return 0;
+  return (int64_t)heads * kvring::tile_count(slots) * kvring::kTile * head_dim;
+}
+
+int32_t kv_ring_v_pos(int32_t u) { return (u < 0 || u >= kvring::kTile) ? -1 : kvring::vt_pos(u); }
+
+int kv_ring_rope_table(float* host_out, int64_t n_pos, int32_t head_dim, double base) {
+  if (!host_out) return KV_RING_ERR_NULL;
+  if (n_pos < 1 || (head_dim != 64 && head_dim != 128) || !(base > 0.0)) return KV_RING_ERR_SHAPE;
+  const int32_t half = head_dim / 2;
+  for (int32_t i = 0; i < half; ++i) {
+    const double th = rope_theta(i, head_dim, base);
+    for (int64_t p = 0; p < n_pos; ++p) {
+      const double ang = (double)p * th;
+      host_out[(p * half + i) * 2] = (float)std::cos(ang);
+      host_out[(p * half + i) * 2 + 1] = (float)std::sin(ang);
+    }
+  }
+  return KV_RING_OK;
+}
+
+size_t kv_ring_workspace_bytes(int32_t op, int32_t heads, int32_t slots, int32_t head_dim, int32_t n) {
+  if (heads < 1 || slots < 1 || (head_dim != 64 && head_dim != 128)) return 0;
+  switch (op) {
+    case KV_RING_OP_WRITE:
+      if (n < 1) return 0;
+      return sizeof(float) * (size_t)kvring::write_workspace_floats(heads, n);
+    case KV_RING_OP_DELTA_ROTATE:
+      return sizeof(float) * (size_t)kvring::rotate_workspace_floats(heads, slots);
+    case KV_RING_OP_ATTENTION:
+      if (n < 0) return 0;
+      if (n == 0) return 16;
+      return sizeof(float) * (size_t)kvring::attention_workspace_floats(heads, slots, head_dim, n);
+    default:
+      return 0;
+  }
+}
+
+int kv_ring_write(const kv_ring_desc* ring, const void* k_new, const void* v_new, int32_t n,
+                  int32_t start_slot, int64_t pos0, const float* rope_table, int64_t rope_n_pos,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_ring(ring);
+  if (st) return st;
+  if (!k_new || !v_new || !rope_table) return KV_RING_ERR_NULL;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(rope_table, 16)) return KV_RING_ERR_ALIGN;
+  if (n < 1 || n > ring->slots || start_slot < 0 || start_slot >= ring->slots) return KV_RING_ERR_RANGE;
+  if (pos0 < 0 || rope_n_pos < 1 || pos0 > rope_n_pos - n) return KV_RING_ERR_POSITION;
+  st = check_workspace(workspace, workspace_bytes,
+                       kv_ring_workspace_bytes(KV_RING_OP_WRITE, ring->heads, ring->slots, ring->head_dim, n));
+  if (st) return st;
+  return status_of(kvring::launch_write(*ring, static_cast<const uint16_t*>(k_new),
+                                        static_cast<const uint16_t*>(v_new), n, start_slot, pos0,
+                                        rope_table, static_cast<float*>(workspace),
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int kv_ring_delta_rotate(const kv_ring_desc* ring, int32_t ring_head, int32_t filled, int64_t delta,
+                         double rope_base, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_ring(ring);
+  if (st) return st;
+  if (ring_head < 0 || ring_head >= ring->slots || filled < 0 || filled > ring->slots) return KV_RING_ERR_RANGE;
+  if (!(rope_base > 0.0)) return KV_RING_ERR_SHAPE;
+  if (delta <= -(int64_t(1) << 31) || delta >= (int64_t(1) << 31)) return KV_RING_ERR_POSITION;
+  st = check_workspace(workspace, workspace_bytes,
+                       kv_ring_workspace_bytes(KV_RING_OP_DELTA_ROTATE, ring->heads, ring->slots, ring->head_dim, 0));
+  if (st) return st;
+  kvring::DeltaTable tab;
+  std::memset(&tab, 0, sizeof(tab));
+  for (int32_t i = 0; i < ring->head_dim / 2; ++i) {
+    const double ang = (double)delta * rope_theta(i, ring->head_dim, rope_base);
+    tab.cs[i][0] = (float)std::cos(ang);
+    tab.cs[i][1] = (float)std::sin(ang);
+  }
+  return status_of(kvring::launch_delta_rotate(*ring, ring_head, filled, tab, static_cast<float*>(workspace),
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int ring_attention(const kv_ring_desc* ring, int32_t ring_head, int32_t filled, const void* q,
+                   int32_t nq, int64_t q_pos0, const float* rope_table, int64_t rope_n_pos,
+                   float softmax_scale, void* out, float* lse, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  int st = check_ring(ring);
+  if (st) return st;
+  if (nq < 0 || ring_head < 0 || ring_head >= ring->slots || filled < 0 || filled > ring->slots)
+    return KV_RING_ERR_RANGE;
+  if (nq == 0) return KV_RING_OK;   // empty tensors may carry NULL data pointers
+  if (!q || !rope_table || !out || !lse) return KV_RING_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(rope_table, 16) || !aligned(out, 8) || !aligned(lse, 4)) return KV_RING_ERR_ALIGN;
+  if (q_pos0 < 0 || rope_n_pos < 1 || q_pos0 > rope_n_pos - nq) return KV_RING_ERR_POSITION;
+  if (!std::isfinite(softmax_scale)) return KV_RING_ERR_RANGE;
+  st = check_workspace(workspace, workspace_bytes,
+                       kv_ring_workspace_bytes(KV_RING_OP_ATTENTION, ring->heads, ring->slots, ring->head_dim, nq));
+  if (st) return st;
+  return status_of(kvring::launch_attention(*ring, ring_head, filled, static_cast<const uint16_t*>(q), nq,
+                                            q_pos0, rope_table, softmax_scale, static_cast<uint16_t*>(out),
+                                            lse, static_cast<float*>(workspace),
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int kv_ring_fp8_encode(const float* x, uint8_t* out, int64_t n, void* stream) {
+  if (n < 0) return KV_RING_ERR_RANGE;
+  if (n == 0) return KV_RING_OK;
+  if (!x || !out) return KV_RING_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(out, 16)) return KV_RING_ERR_ALIGN;
+  return status_of(kvring::launch_fp8_encode(x, out, n, static_cast<hipStream_t>(stream)));
+}
+
+int kv_ring_set_attention_events(void* before, void* after) {
+  if (before && after)
+    kvring::set_attention_events(before, after);
+  else
+    kvring::set_attention_events(nullptr, nullptr);
+  return KV_RING_OK;
+}
+
+const char* kv_ring_status_string(int status) {
+  switch (status) {
+    case KV_RING_OK: return "ok";
+    case KV_RING_ERR_NULL: return "a required pointer is NULL";
+    case KV_RING_ERR_ALIGN: return "a pointer is not aligned as documented";
+    case KV_RING_ERR_SHAPE: return "heads, slots or head_dim unsupported";
+    case KV_RING_ERR_RANGE: return "n, start_slot, ring_head, filled or nq out of range";
+    case KV_RING_ERR_POSITION: return "a position falls outside the rotary table";
+    case KV_RING_ERR_WORKSPACE: return "workspace missing or too small";
+    case KV_RING_ERR_LAUNCH: return "a kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

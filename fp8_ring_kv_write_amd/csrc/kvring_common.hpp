@@ -1,0 +1,94 @@
+// Shared device helpers for the FP8 ring KV-cache kernels (gfx950).
+//
+// Cache layout in HBM (per ring = one layer, one GPU's share of heads):
+//   K codes  [heads][tiles*128][head_dim]   row-major, one 128-slot tile after another
+//   V codes  [heads][tiles][head_dim][128]  each 128-slot tile stored transposed, with the
+//                                           slots of a row permuted into the order the
+//                                           PV matrix-core operand reads them (see vt_pos)
+//   scales   [heads][slots] float32         dequantisation scale of the write that filled
+//                                           each slot (k_scale, v_scale)
+// tiles = ceil(slots / 128); slots past `slots` in the last tile are never valid.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvring {
+
+constexpr int kTile = 128;          // slots per ring tile
+constexpr int kChunk = 32;          // slots per write/rotate work-group chunk
+constexpr float kE4M3Max = 448.0f;
+constexpr float kScaleFloor = 0x1p-100f;
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+__host__ __device__ inline int64_t tile_count(int32_t slots) { return (slots + kTile - 1) / kTile; }
+
+// Position of slot u (0..127 inside a tile) inside a transposed V row.  The PV product
+// reads, in lane group g (0..3) and operand byte s (0..31), the slot 16*(s/4) + 4*g + s%4;
+// storing that slot at byte 32*g + s makes each lane's 32-byte operand contiguous.
+__host__ __device__ inline int vt_pos(int u) {
+  const int b = u >> 4, g = (u >> 2) & 3, r = u & 3;
+  return 32 * g + 4 * b + r;
+}
+
+// bfloat16 bit pattern -> float32 (exact).
+__device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// E4M3 (OCP, "fn") encode of two float32 values already scaled into range: round to nearest
+// even, saturate to +-448 (the clamp makes the saturation explicit), sign kept.  Returns the
+// two codes in the low 16 bits (first value in bits 0..7).
+__device__ inline uint32_t e4m3x2(float a, float b) {
+  a = __builtin_fminf(__builtin_fmaxf(a, -kE4M3Max), kE4M3Max);
+  b = __builtin_fminf(__builtin_fmaxf(b, -kE4M3Max), kE4M3Max);
+  return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)) & 0xFFFFu;
+}
+
+// Four values -> four codes packed in one dword (first value in the low byte).
+__device__ inline uint32_t e4m3x4(float a, float b, float c, float d) {
+  a = __builtin_fminf(__builtin_fmaxf(a, -kE4M3Max), kE4M3Max);
+  b = __builtin_fminf(__builtin_fmaxf(b, -kE4M3Max), kE4M3Max);
+  c = __builtin_fminf(__builtin_fmaxf(c, -kE4M3Max), kE4M3Max);
+  d = __builtin_fminf(__builtin_fmaxf(d, -kE4M3Max), kE4M3Max);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return uint32_t(w);
+}
+
+// E4M3 decode of the code in byte `sel` (0..3) of w (exact; hardware conversion).
+__device__ inline float e4m3_decode(uint32_t w, int sel) {
+  v2f two = __builtin_amdgcn_cvt_pk_f32_fp8(int(w >> (16 * (sel >> 1))), false);
+  return (sel & 1) ? two[1] : two[0];
+}
+
+// Per-head (scale, inverse) from the absmax, both correctly rounded float32 divisions.
+__device__ inline void scale_from_absmax(float amax, float& scale, float& inv) {
+  const float a = __builtin_fmaxf(amax, kScaleFloor);
+  scale = a / kE4M3Max;
+  inv = kE4M3Max / a;
+}
+
+// Max over a work-group of 256 threads; `red` is LDS scratch of >= 4 floats.  Every thread
+// gets the result.
+__device__ inline float block_max_256(float v, float* red) {
+  for (int off = 32; off > 0; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, 64));
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+}
+
+// Whether `slot` holds a token of the ring whose valid interval is the `filled` slots just
+// before `head` (oldest first).
+__device__ inline bool slot_valid(int slot, int head, int filled, int slots) {
+  if (slot < 0 || slot >= slots) return false;
+  int rel = slot - (head - filled);
+  rel = rel < 0 ? rel + slots : rel;
+  rel = rel >= slots ? rel - slots : rel;
+  return rel < filled;
+}
+
+}  // namespace kvring

@@ -1,0 +1,39 @@
+// Internal launch interface between the C ABI (kvring_abi.cpp) and the kernels.
+// Arguments have been validated by the caller; every function only enqueues work on
+// `stream` and returns the HIP status of the launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvring.h"
+
+namespace kvring {
+
+// Floats of workspace each operation needs (see kv_ring_workspace_bytes).
+int64_t write_workspace_floats(int32_t heads, int32_t n);
+int64_t rotate_workspace_floats(int32_t heads, int32_t slots);
+int64_t attention_workspace_floats(int32_t heads, int32_t slots, int32_t head_dim, int32_t nq);
+int attention_splits(int32_t heads, int32_t slots, int32_t nq);
+
+hipError_t launch_write(const kv_ring_desc& r, const uint16_t* k_new, const uint16_t* v_new,
+                        int32_t n, int32_t start_slot, int64_t pos0, const float* rope,
+                        float* ws, hipStream_t stream);
+
+struct DeltaTable {  // cos/sin of delta * theta_i for i < head_dim/2, float32
+  float cs[64][2];
+};
+
+hipError_t launch_delta_rotate(const kv_ring_desc& r, int32_t ring_head, int32_t filled,
+                               const DeltaTable& tab, float* ws, hipStream_t stream);
+
+hipError_t launch_attention(const kv_ring_desc& r, int32_t ring_head, int32_t filled,
+                            const uint16_t* q, int32_t nq, int64_t q_pos0, const float* rope,
+                            float softmax_scale, uint16_t* out, float* lse, float* ws,
+                            hipStream_t stream);
+
+void set_attention_events(void* before, void* after);
+
+hipError_t launch_fp8_encode(const float* x, uint8_t* out, int64_t n, hipStream_t stream);
+
+}  // namespace kvring

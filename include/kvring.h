@@ -1,0 +1,177 @@
+/*
+ * kvring.h -- C ABI of the MI355X (gfx950) FP8 ring KV cache.
+ *
+ * What it computes (Runway Characters: Serving a 57B Video Diffusion Transformer for
+ * Real-Time Conversation, arXiv 2611.05642):
+ *   - abstract: each of the 240 attention calls of a four-frame chunk reads a 5,788-slot KV
+ *     cache of which 757 tokens are new; the whole-cache work that used to repeat in every
+ *     call is moved to write time: a ring cache, RoPE and FP8 quantisation applied once per
+ *     write, and a delta rotation of the cache when positions reset;
+ *   - cpdf.ai blog, section "Como rodar 57B em tempo real com batch size 1": rotary positions
+ *     and FP8 quantisation are applied as a frame enters the cache, and the ring lets the
+ *     window advance without copies;
+ *   - cpdf.ai blog, section "Blackwell, escalabilidade e limites do decodificador": the
+ *     attention kernel reads the FP8 cache with per-head scales.
+ *
+ * Readings where the pages are silent (the CPU oracle states the same ones):
+ *   - RoPE: 1-D positions, interleaved channel pairs (2i, 2i+1), theta_i = base^(-2i/D),
+ *     x' = x cos - y sin, y' = x sin + y cos in float32 with every operation rounded; cos/sin
+ *     come from a float64 C-library table rounded once to float32 (kv_ring_rope_table);
+ *   - FP8 is OCP E4M3 (max 448), round to nearest even, saturating;
+ *   - scales are per head and per write: A = max |x| over the write's tokens and channels of a
+ *     head (K after rotation, V as is), floored at 2^-100; scale = A/448, stored for every slot
+ *     the write fills; codes = e4m3(x * (448/A));
+ *   - the ring's valid slots are the `filled` slots just before `ring_head`, oldest first;
+ *   - attention is non-causal over all valid slots, one KV head per query head; queries are
+ *     rotated at their positions and quantised to FP8 with one scale per head per call.
+ *
+ * Conventions for every entry point:
+ *   - pointers named "device" are HIP device memory owned by the caller; the library never
+ *     allocates, frees or keeps them;
+ *   - work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the call
+ *     returns without synchronising;
+ *   - the return value is KV_RING_OK (0) or a negative status; arguments are checked before
+ *     anything is enqueued, and on an argument error nothing is launched and nothing written;
+ *   - no call allocates memory: scratch space is the caller's `workspace`, sized by
+ *     kv_ring_workspace_bytes; the workspace must not be shared by calls that may overlap.
+ */
+#ifndef KVRING_H
+#define KVRING_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  KV_RING_OK = 0,
+  KV_RING_ERR_NULL = -1,       /* a required pointer is NULL                         */
+  KV_RING_ERR_ALIGN = -2,      /* a pointer is not aligned as documented               */
+  KV_RING_ERR_SHAPE = -3,      /* heads, slots or head_dim unsupported                 */
+  KV_RING_ERR_RANGE = -4,      /* n, start_slot, ring_head, filled or nq out of range  */
+  KV_RING_ERR_POSITION = -5,   /* a position falls outside the rotary table            */
+  KV_RING_ERR_WORKSPACE = -6,  /* workspace NULL or smaller than required              */
+  KV_RING_ERR_LAUNCH = -7      /* a kernel launch failed (HIP error)                   */
+};
+
+enum { KV_RING_OP_WRITE = 1, KV_RING_OP_DELTA_ROTATE = 2, KV_RING_OP_ATTENTION = 3 };
+
+/*
+ * One ring (one layer, one GPU's share of heads).  All four buffers are device memory of the
+ * caller, 16-byte aligned.  With T = ceil(slots / 128) tiles:
+ *   k        K codes, T*128*head_dim bytes per head, [heads][T*128][head_dim]: slot s of head h
+ *            at byte (h*T*128 + s)*head_dim;
+ *   v        V codes, the same size, each 128-slot tile stored transposed:
+ *            [heads][T][head_dim][128]; channel d of slot s of head h is at byte
+ *            ((h*T + s/128)*head_dim + d)*128 + kv_ring_v_pos(s % 128);
+ *   k_scale  float32 [heads][slots], the dequantisation scale of the write that filled a slot;
+ *   v_scale  float32 [heads][slots].
+ * Limits: 1 <= heads <= 65535, 1 <= slots <= 1048576, head_dim in {64, 128}.
+ * Bytes of the last tile past `slots` are padding and never read as data.
+ */
+typedef struct kv_ring_desc {
+  uint8_t *k;
+  uint8_t *v;
+  float *k_scale;
+  float *v_scale;
+  int32_t heads;
+  int32_t slots;
+  int32_t head_dim;
+} kv_ring_desc;
+
+/* Bytes of one of the two code buffers (k or v): heads * ceil(slots/128) * 128 * head_dim. */
+int64_t kv_ring_codes_bytes(int32_t heads, int32_t slots, int32_t head_dim);
+
+/* Byte position of slot u (0..127 within its tile) inside a transposed V row:
+ * pos(u) = 32*((u >> 2) & 3) + 4*(u >> 4) + (u & 3), a permutation of 0..127 under which
+ * each lane of the PV matrix-core product reads its 32 slots as 32 contiguous bytes.
+ * Returns -1 outside 0..127. */
+int32_t kv_ring_v_pos(int32_t u);
+
+/*
+ * Fill a host float32 table [n_pos][head_dim/2][2] with cos and sin of p * theta_i for
+ * positions p in 0..n_pos-1: theta_i = pow(base, -(2i)/head_dim), angle = (double)p*theta_i,
+ * each value computed in double by the C library and rounded once to float.  The caller
+ * copies it to the device and passes it to kv_ring_write and ring_attention.
+ * Errors: NULL out, n_pos < 1, head_dim not in {64, 128}, base <= 0.
+ */
+int kv_ring_rope_table(float *host_out, int64_t n_pos, int32_t head_dim, double base);
+
+/* Workspace bytes for `op` (KV_RING_OP_*) with n = new tokens (write), unused (delta
+ * rotate) or nq = queries (attention).  Returns 0 for an unknown op or invalid shape. */
+size_t kv_ring_workspace_bytes(int32_t op, int32_t heads, int32_t slots, int32_t head_dim,
+                               int32_t n);
+
+/*
+ * Write n new tokens into the ring (abstract: RoPE and FP8 quantisation applied once per
+ * write; cpdf.ai blog, "Como rodar 57B...": done as the frame enters the cache).
+ *   k_new, v_new  device bfloat16 [n][heads][head_dim], 16-byte aligned; token i has
+ *                 absolute position pos0 + i and goes to slot (start_slot + i) % slots;
+ *   rope_table    device float32 table from kv_ring_rope_table with rope_n_pos positions;
+ * K is rotated, K and V each get one scale per head over this write, codes and scales are
+ * stored.  The caller then sets ring_head = (start_slot + n) % slots and
+ * filled = min(filled + n, slots).
+ * Errors: NULL pointers, misalignment, 1 <= n <= slots, 0 <= start_slot < slots,
+ * 0 <= pos0 and pos0 + n <= rope_n_pos, workspace too small.
+ */
+int kv_ring_write(const kv_ring_desc *ring, const void *k_new, const void *v_new, int32_t n,
+                  int32_t start_slot, int64_t pos0, const float *rope_table, int64_t rope_n_pos,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Delta rotation when positions reset (abstract: a delta rotation of the cache instead of
+ * re-rotating it): every valid K slot is dequantised, rotated by delta positions (cos/sin of
+ * delta * theta_i from the C library, in double, rounded to float) and requantised with one
+ * new scale per head over all valid slots.  V and invalid slots are untouched.
+ *   ring_head, filled  the ring's valid interval (0 <= ring_head < slots, 0 <= filled <= slots);
+ *   delta              position offset, |delta| < 2^31; rope_base > 0.
+ * The caller continues positions from old + delta.
+ */
+int kv_ring_delta_rotate(const kv_ring_desc *ring, int32_t ring_head, int32_t filled,
+                         int64_t delta, double rope_base, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
+/*
+ * Attention of nq new queries over every valid slot of the ring (abstract: 757 new-token
+ * queries against the 5,788-slot cache, 240 calls per chunk; cpdf.ai blog, "Blackwell...":
+ * FP8 attention with per-head scales).
+ *   q            device bfloat16 [nq][heads][head_dim], 16-byte aligned; query i at position
+ *                q_pos0 + i (rotated, then quantised with one FP8 scale per head);
+ *   softmax_scale  multiplies q.k (normally 1/sqrt(head_dim));
+ *   out          device bfloat16 [nq][heads][head_dim], 8-byte aligned;
+ *   lse          device float32 [heads][nq]: natural-log softmax denominator plus row max.
+ * With filled == 0 the output is 0 and lse is -inf.  nq == 0 is a no-op.
+ * Errors: NULL pointers, misalignment, nq < 0, ring_head/filled out of range, positions
+ * outside the table, workspace too small.
+ */
+int ring_attention(const kv_ring_desc *ring, int32_t ring_head, int32_t filled, const void *q,
+                   int32_t nq, int64_t q_pos0, const float *rope_table, int64_t rope_n_pos,
+                   float softmax_scale, void *out, float *lse, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
+/*
+ * The E4M3 encoder the kernels use, exposed so it can be checked exhaustively: out[i] =
+ * e4m3(x[i]) with round to nearest even and saturation to +-448 (x finite).  x and out are
+ * device pointers, 16-byte aligned; n >= 0.
+ */
+int kv_ring_fp8_encode(const float *x, uint8_t *out, int64_t n, void *stream);
+
+/*
+ * Profiling aid.  When both handles are non-NULL, each later ring_attention call records
+ * `before` (a hipEvent_t) on its stream immediately before launching its main attention kernel
+ * and `after` immediately after it, so the caller can time that kernel alone with
+ * hipEventElapsedTime.  Passing NULLs turns it off.  The setting is process-wide and not
+ * synchronised: set it from the thread that issues the calls being timed.
+ */
+int kv_ring_set_attention_events(void *before, void *after);
+
+/* Static description of a status code. */
+const char *kv_ring_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVRING_H */

@@ -1,0 +1,85 @@
+"""Helpers shared by the GPU tests: build the same seeded workload for the HIP library and
+the CPU oracle, and read the library's ring back in the oracle's logical layout.
+
+The layout conversion follows the description in include/kvring.h; it is test code, not part
+of either implementation."""
+
+from __future__ import annotations
+
+import numpy as np
+
+TILE = 128
+
+
+def v_pos_formula(u: np.ndarray) -> np.ndarray:
+    u = np.asarray(u)
+    return 32 * ((u >> 2) & 3) + 4 * (u >> 4) + (u & 3)
+
+
+def logical_codes(k_buf: np.ndarray, v_buf: np.ndarray, heads: int, slots: int, head_dim: int):
+    """Library code buffers (flat uint8) -> K, V codes [heads, slots, head_dim]."""
+    tiles = (slots + TILE - 1) // TILE
+    k = k_buf.reshape(heads, tiles * TILE, head_dim)[:, :slots, :]
+    v4 = v_buf.reshape(heads, tiles, head_dim, TILE)
+    perm = v_pos_formula(np.arange(TILE))
+    v = v4[:, :, :, perm].transpose(0, 1, 3, 2).reshape(heads, tiles * TILE, head_dim)[:, :slots, :]
+    return np.ascontiguousarray(k), np.ascontiguousarray(v)
+
+
+def ring_to_host(ring):
+    """(K codes, V codes, k_scale, v_scale) of a library Ring, logical layout, numpy."""
+    k, v = logical_codes(ring.k.cpu().numpy(), ring.v.cpu().numpy(), ring.heads, ring.slots, ring.head_dim)
+    return k, v, ring.k_scale.cpu().numpy(), ring.v_scale.cpu().numpy()
+
+
+def poison_free_slots_gpu(ring, valid: np.ndarray):
+    """Write NaN codes (0x7F into K, 0xFF into V) and NaN scales into every slot outside `valid`
+    (including the padding of the last tile)."""
+    import torch
+    H, S, D = ring.heads, ring.slots, ring.head_dim
+    tiles = (S + TILE - 1) // TILE
+    free = np.setdiff1d(np.arange(tiles * TILE), valid)
+    kb = ring.k.view(H, tiles * TILE, D)
+    kb[:, torch.from_numpy(free).to(kb.device), :] = 0x7F
+    vb = ring.v.view(H, tiles, D, TILE)
+    for s in free.tolist():
+        vb[:, s // TILE, :, int(v_pos_formula(s % TILE))] = 0xFF
+    fs = free[free < S]
+    nan = torch.tensor(float("nan"), device=ring.k_scale.device)
+    ring.k_scale[:, torch.from_numpy(fs).to(kb.device)] = nan
+    ring.v_scale[:, torch.from_numpy(fs).to(kb.device)] = nan
+
+
+def to_dev_bf16(bits: np.ndarray, device="cuda"):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+def bf16_dev_to_f64(t) -> np.ndarray:
+    import torch
+    return t.view(torch.int16).cpu().numpy().view(np.uint16).astype(np.uint32).__lshift__(16).view(np.float32).astype(np.float64)
+
+
+def attention_errors(out: np.ndarray, ref: np.ndarray):
+    """Per head: infinity-norm relative error max|o - ref| / max|ref| and L2 relative error.
+    out, ref: [nq, heads, D]."""
+    inf_rel = np.abs(out - ref).max(axis=(0, 2)) / np.maximum(np.abs(ref).max(axis=(0, 2)), 1e-30)
+    l2_rel = np.sqrt(((out - ref) ** 2).sum(axis=(0, 2)) / np.maximum((ref ** 2).sum(axis=(0, 2)), 1e-300))
+    return inf_rel, l2_rel
+
+
+def mfma_lse_bound(q_hat_h: np.ndarray, k_hat_h: np.ndarray, softmax_scale: float) -> np.ndarray:
+    """Bound on |LSE error| per query caused by the FP8 matrix core's grouped accumulation.
+
+    The 16x16x128 FP8 MFMA of gfx950 adds the products of each group of 8 consecutive
+    contraction elements (here: channels 8m .. 8m+7) keeping about 13 bits below the group's
+    largest product, so a group's sum is off by at most 8 * 2^-12 * its largest |product|.
+    Since |d lse / d s_j| = p_j sums to 1, |delta lse_i| <= max_j |delta s_ij|.
+
+    q_hat_h [nq, D], k_hat_h [n, D] (dequantised float64 values of one head) -> [nq]."""
+    nq, d = q_hat_h.shape
+    out = np.zeros(nq)
+    for i in range(nq):
+        prod = np.abs(k_hat_h * q_hat_h[i][None, :]).reshape(k_hat_h.shape[0], d // 8, 8)
+        out[i] = softmax_scale * (8 * 2.0 ** -12 * prod.max(axis=2).sum(axis=1)).max()
+    return out

@@ -1,0 +1,133 @@
+"""Host-only checks of the C ABI (no kernel is launched): the library loads, exports every
+function include/kvring.h declares, its host helpers agree with the oracle, and argument
+errors are reported before anything could reach the device."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvring.h")
+
+
+@pytest.fixture(scope="module")
+def kv():
+    import fp8_ring_kv_write_amd as kv
+    return kv
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for n in ("kv_ring_write", "kv_ring_delta_rotate", "ring_attention"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function(kv):
+    lib = ctypes.CDLL(kv.library_path())
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_rope_table_matches_oracle_bit_for_bit(kv):
+    from oracle import rope_table
+    for d in (64, 128):
+        ours = kv.rope_table(300, d)
+        ref = rope_table(300, d)
+        assert ours.tobytes() == ref.tobytes()
+
+
+def test_v_pos_is_the_documented_permutation(kv):
+    pos = [kv.v_pos(u) for u in range(128)]
+    assert sorted(pos) == list(range(128))
+    for u in range(128):
+        assert pos[u] == 32 * ((u >> 2) & 3) + 4 * (u >> 4) + (u & 3)
+    # lane group g of the PV product reads slots 16*(s/4) + 4g + s%4 at bytes 32g + s
+    for g in range(4):
+        assert [pos[16 * (s // 4) + 4 * g + s % 4] for s in range(32)] == list(range(32 * g, 32 * g + 32))
+    assert kv.v_pos(-1) == -1 and kv.v_pos(128) == -1
+
+
+def test_sizes(kv):
+    assert kv.codes_bytes(24, 5788, 128) == 24 * 46 * 128 * 128
+    assert kv.codes_bytes(1, 64, 64) == 128 * 64
+    assert kv.codes_bytes(0, 64, 64) == 0 and kv.codes_bytes(1, 64, 96) == 0
+    for op in (kv.OP_WRITE, kv.OP_DELTA_ROTATE, kv.OP_ATTENTION):
+        assert kv.workspace_bytes(op, 24, 5788, 128, 757) > 0
+        assert kv.workspace_bytes(op, 24, 5788, 128, 757) % 4 == 0
+    assert kv.workspace_bytes(99, 24, 5788, 128, 757) == 0
+
+
+def test_status_strings(kv):
+    assert kv.status_string(0) == "ok"
+    for s in range(-7, 0):
+        assert kv.status_string(s) != "unknown status"
+
+
+def test_argument_errors_are_reported_before_any_launch(kv):
+    """Fake (never dereferenced) aligned addresses: every call below must be rejected by the
+    argument checks, so no kernel is enqueued."""
+    from fp8_ring_kv_write_amd._lib import _Desc
+    L = kv.lib
+    F = 1 << 20   # an aligned fake address
+    good = _Desc(F, F, F, F, 2, 64, 64)
+    d = ctypes.byref
+    ws = kv.workspace_bytes(kv.OP_WRITE, 2, 64, 64, 16)
+    # write
+    assert L.kv_ring_write(None, F, F, 16, 0, 0, F, 128, F, ws, None) == -1
+    assert L.kv_ring_write(d(_Desc(0, F, F, F, 2, 64, 64)), F, F, 16, 0, 0, F, 128, F, ws, None) == -1
+    assert L.kv_ring_write(d(_Desc(F, F, F, F, 2, 64, 96)), F, F, 16, 0, 0, F, 128, F, ws, None) == -3
+    assert L.kv_ring_write(d(_Desc(F + 1, F, F, F, 2, 64, 64)), F, F, 16, 0, 0, F, 128, F, ws, None) == -2
+    assert L.kv_ring_write(d(good), F + 2, F, 16, 0, 0, F, 128, F, ws, None) == -2
+    assert L.kv_ring_write(d(good), F, F, 0, 0, 0, F, 128, F, ws, None) == -4
+    assert L.kv_ring_write(d(good), F, F, 65, 0, 0, F, 128, F, ws, None) == -4
+    assert L.kv_ring_write(d(good), F, F, 16, 64, 0, F, 128, F, ws, None) == -4
+    assert L.kv_ring_write(d(good), F, F, 16, -1, 0, F, 128, F, ws, None) == -4
+    assert L.kv_ring_write(d(good), F, F, 16, 0, 120, F, 128, F, ws, None) == -5
+    assert L.kv_ring_write(d(good), F, F, 16, 0, -1, F, 128, F, ws, None) == -5
+    assert L.kv_ring_write(d(good), F, F, 16, 0, 0, F, 128, None, ws, None) == -6
+    assert L.kv_ring_write(d(good), F, F, 16, 0, 0, F, 128, F, ws - 4, None) == -6
+    # delta rotate
+    wr = kv.workspace_bytes(kv.OP_DELTA_ROTATE, 2, 64, 64, 0)
+    assert L.kv_ring_delta_rotate(d(good), 64, 10, 5, 10000.0, F, wr, None) == -4
+    assert L.kv_ring_delta_rotate(d(good), 0, 65, 5, 10000.0, F, wr, None) == -4
+    assert L.kv_ring_delta_rotate(d(good), 0, 10, 5, 0.0, F, wr, None) == -3
+    assert L.kv_ring_delta_rotate(d(good), 0, 10, 1 << 31, 10000.0, F, wr, None) == -5
+    assert L.kv_ring_delta_rotate(d(good), 0, 10, 5, 10000.0, F, wr - 4, None) == -6
+    # attention
+    wa = kv.workspace_bytes(kv.OP_ATTENTION, 2, 64, 64, 16)
+    assert L.ring_attention(d(good), 0, 10, None, 16, 0, F, 128, 0.125, F, F, F, wa, None) == -1
+    assert L.ring_attention(d(good), 0, 10, F, -1, 0, F, 128, 0.125, F, F, F, wa, None) == -4
+    assert L.ring_attention(d(good), 0, 65, F, 16, 0, F, 128, 0.125, F, F, F, wa, None) == -4
+    assert L.ring_attention(d(good), 64, 10, F, 16, 0, F, 128, 0.125, F, F, F, wa, None) == -4
+    assert L.ring_attention(d(good), 0, 10, F, 16, 113, F, 128, 0.125, F, F, F, wa, None) == -5
+    assert L.ring_attention(d(good), 0, 10, F, 16, 0, F, 128, float("nan"), F, F, F, wa, None) == -4
+    assert L.ring_attention(d(good), 0, 10, F, 16, 0, F, 128, 0.125, F + 4, F, F, wa, None) == -2
+    assert L.ring_attention(d(good), 0, 10, F, 16, 0, F, 128, 0.125, F, F, F, wa - 4, None) == -6
+    assert L.ring_attention(d(good), 0, 10, F, 0, 0, F, 128, 0.125, F, F, F, wa, None) == 0  # no-op
+    assert L.ring_attention(d(good), 0, 10, None, 0, 0, None, 128, 0.125, None, None, None, 0, None) == 0
+    # encoder
+    assert L.kv_ring_fp8_encode(F, F, -1, None) == -4
+    assert L.kv_ring_fp8_encode(None, F, 5, None) == -1
+    assert L.kv_ring_fp8_encode(F + 4, F, 5, None) == -2
+    assert L.kv_ring_fp8_encode(F, F, 0, None) == 0
+    assert L.kv_ring_rope_table(None, 10, 64, 10000.0) == -1
+
+
+def test_product_path_has_no_oracle_import():
+    """The package never imports the oracle (the oracle is test infrastructure)."""
+    pkg = os.path.join(ROOT, "fp8_ring_kv_write_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
