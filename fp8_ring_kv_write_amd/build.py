@@ -30,6 +30,8 @@ def command(out: str = LIB, extra: list[str] | None = None) -> list[str]:
     return [
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # matrix-core results in ordinary VGPRs where they fit: the softmax reads every score
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-Wall", "-Wno-unused-function",
         *[os.path.join(CSRC, s) for s in SOURCES], "-o", out, *(extra or []),
     ]

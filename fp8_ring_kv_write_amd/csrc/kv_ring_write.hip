@@ -68,13 +68,18 @@ __device__ inline float absmax(const float (&x)[CPT]) {
 
 // Pass 1.  grid = (ceil(n/32), heads, tensors); tensor 0 is rotated (K or Q), tensor 1 (V) is
 // not.  partial layout [tensor][heads][ngroups].
+// `zero`/`nzero`: int counters that work-group (0, 0, 0) clears for a kernel launched after this
+// one on the same stream (the attention's row counters); NULL/0 when unused.
 template <int D>
 __global__ __launch_bounds__(kThreads) void rope_absmax_partials(
     const uint16_t* __restrict__ x0, const uint16_t* __restrict__ x1, int32_t n, int32_t heads,
-    int64_t pos0, const float* __restrict__ rope, float* __restrict__ partial) {
+    int64_t pos0, const float* __restrict__ rope, float* __restrict__ partial, int* zero,
+    int32_t nzero) {
   constexpr int CPT = D / 8;
   __shared__ float red[4];
   const int grp = blockIdx.x, h = blockIdx.y, tensor = blockIdx.z;
+  if (grp == 0 && h == 0 && tensor == 0)
+    for (int j = threadIdx.x; j < nzero; j += kThreads) zero[j] = 0;
   const int i = grp * kChunk + (threadIdx.x >> 3);
   const int cg = threadIdx.x & 7;
   float m = 0.0f;
@@ -198,10 +203,10 @@ hipError_t launch_write(const kv_ring_desc& r, const uint16_t* k_new, const uint
   dim3 g1(ngroups, r.heads, 2);
   if (r.head_dim == 128)
     hipLaunchKernelGGL(rope_absmax_partials<128>, g1, dim3(kThreads), 0, stream, k_new, v_new, n,
-                       r.heads, pos0, rope, ws);
+                       r.heads, pos0, rope, ws, nullptr, 0);
   else
     hipLaunchKernelGGL(rope_absmax_partials<64>, g1, dim3(kThreads), 0, stream, k_new, v_new, n,
-                       r.heads, pos0, rope, ws);
+                       r.heads, pos0, rope, ws, nullptr, 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -236,15 +241,16 @@ hipError_t launch_write(const kv_ring_desc& r, const uint16_t* k_new, const uint
 
 // Q partials for the attention prologue reuse pass 1 (tensor 0 only).
 hipError_t launch_q_absmax(const uint16_t* q, int32_t nq, int32_t heads, int32_t head_dim,
-                           int64_t q_pos0, const float* rope, float* partial, hipStream_t stream) {
+                           int64_t q_pos0, const float* rope, float* partial, int* zero,
+                           int32_t nzero, hipStream_t stream) {
   const int ngroups = (nq + kChunk - 1) / kChunk;
   dim3 g1(ngroups, heads, 1);
   if (head_dim == 128)
     hipLaunchKernelGGL(rope_absmax_partials<128>, g1, dim3(kThreads), 0, stream, q, q, nq, heads,
-                       q_pos0, rope, partial);
+                       q_pos0, rope, partial, zero, nzero);
   else
     hipLaunchKernelGGL(rope_absmax_partials<64>, g1, dim3(kThreads), 0, stream, q, q, nq, heads,
-                       q_pos0, rope, partial);
+                       q_pos0, rope, partial, zero, nzero);
   return hipGetLastError();
 }
 

@@ -133,7 +133,7 @@ int ring_attention(const kv_ring_desc* ring, int32_t ring_head, int32_t filled, 
   if (!q || !rope_table || !out || !lse) return KV_RING_ERR_NULL;
   if (!aligned(q, 16) || !aligned(rope_table, 16) || !aligned(out, 8) || !aligned(lse, 4)) return KV_RING_ERR_ALIGN;
   if (q_pos0 < 0 || rope_n_pos < 1 || q_pos0 > rope_n_pos - nq) return KV_RING_ERR_POSITION;
-  if (!std::isfinite(softmax_scale)) return KV_RING_ERR_RANGE;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0f)) return KV_RING_ERR_RANGE;
   st = check_workspace(workspace, workspace_bytes,
                        kv_ring_workspace_bytes(KV_RING_OP_ATTENTION, ring->heads, ring->slots, ring->head_dim, nq));
   if (st) return st;

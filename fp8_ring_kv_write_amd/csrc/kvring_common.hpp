@@ -23,6 +23,8 @@ constexpr float kScaleFloor = 0x1p-100f;
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
+typedef short v2s __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
 
 __host__ __device__ inline int64_t tile_count(int32_t slots) { return (slots + kTile - 1) / kTile; }
 

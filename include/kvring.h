@@ -139,12 +139,12 @@ int kv_ring_delta_rotate(const kv_ring_desc *ring, int32_t ring_head, int32_t fi
  * FP8 attention with per-head scales).
  *   q            device bfloat16 [nq][heads][head_dim], 16-byte aligned; query i at position
  *                q_pos0 + i (rotated, then quantised with one FP8 scale per head);
- *   softmax_scale  multiplies q.k (normally 1/sqrt(head_dim));
+ *   softmax_scale  multiplies q.k, finite and > 0 (normally 1/sqrt(head_dim));
  *   out          device bfloat16 [nq][heads][head_dim], 8-byte aligned;
  *   lse          device float32 [heads][nq]: natural-log softmax denominator plus row max.
  * With filled == 0 the output is 0 and lse is -inf.  nq == 0 is a no-op.
- * Errors: NULL pointers, misalignment, nq < 0, ring_head/filled out of range, positions
- * outside the table, workspace too small.
+ * Errors: NULL pointers, misalignment, nq < 0, ring_head/filled out of range, softmax_scale not
+ * finite and positive, positions outside the table, workspace too small.
  */
 int ring_attention(const kv_ring_desc *ring, int32_t ring_head, int32_t filled, const void *q,
                    int32_t nq, int64_t q_pos0, const float *rope_table, int64_t rope_n_pos,

@@ -111,6 +111,8 @@ def test_argument_errors_are_reported_before_any_launch(kv):
     assert L.ring_attention(d(good), 64, 10, F, 16, 0, F, 128, 0.125, F, F, F, wa, None) == -4
     assert L.ring_attention(d(good), 0, 10, F, 16, 113, F, 128, 0.125, F, F, F, wa, None) == -5
     assert L.ring_attention(d(good), 0, 10, F, 16, 0, F, 128, float("nan"), F, F, F, wa, None) == -4
+    assert L.ring_attention(d(good), 0, 10, F, 16, 0, F, 128, 0.0, F, F, F, wa, None) == -4
+    assert L.ring_attention(d(good), 0, 10, F, 16, 0, F, 128, -0.1, F, F, F, wa, None) == -4
     assert L.ring_attention(d(good), 0, 10, F, 16, 0, F, 128, 0.125, F + 4, F, F, wa, None) == -2
     assert L.ring_attention(d(good), 0, 10, F, 16, 0, F, 128, 0.125, F, F, F, wa - 4, None) == -6
     assert L.ring_attention(d(good), 0, 10, F, 0, 0, F, 128, 0.125, F, F, F, wa, None) == 0  # no-op
