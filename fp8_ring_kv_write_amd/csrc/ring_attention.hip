@@ -5,7 +5,7 @@
 //
 // Three launches per call:
 //   1. rope_absmax_partials (shared with the write): per-(head, 32-query group) max |RoPE(q)|;
-//   2. attn_stream: a persistent grid of one 4-wavefront work-group per compute unit.  The work
+//   2. attn_stream: a persistent grid of one 8-wavefront work-group per compute unit.  The work
 //      is the set of units (row, tile), a row being 128 queries of one head and a tile 128 ring
 //      slots; each work-group takes an equal contiguous range of units, so a row may be split
 //      between work-groups.  A row held by one work-group is finished in place; the segments of
@@ -17,12 +17,12 @@
 //
 // Per tile: K tile and transposed V tile are copied straight from HBM into LDS with
 // global_load_lds (16 bytes per lane, XOR-swizzled 16-byte chunks, double-buffered so the next
-// tile's copy overlaps this tile's math).  Each wavefront owns 32 queries:
-//   S^T = K Q^T           8 x 2 MFMA 16x16x128 FP8 (fp32 accumulate)
+// tile's copy overlaps this tile's math).  Each wavefront owns 16 queries:
+//   S^T = K Q^T           8 MFMA 16x16x128 FP8 (fp32 accumulate)
 //   online softmax        log2 domain, lazily rescaled (the running max may lag the true max
 //                         by up to 2^4, so P <= 16)
 //   P = hi + lo           hi = e4m3(P), lo = e4m3((P - hi) * 2^8)
-//   O^T += V^T P^T        8 x 2 x 2 MFMA 16x16x128 FP8; the B-operand exponent scale carries
+//   O^T += V^T P^T        8 x 2 MFMA 16x16x128 FP8; the B-operand exponent scale carries
 //                         the tile's power-of-two V-scale factor (and 2^-8 for lo)
 // Computing S^T rather than S leaves one query per lane with its keys in registers, which is
 // exactly the B-operand layout of the PV product: probabilities never leave their lane.
@@ -43,9 +43,10 @@ hipError_t launch_q_absmax(const uint16_t* q, int32_t nq, int32_t heads, int32_t
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;   // 256
-constexpr int kRowQ = 32 * kWaves;      // 128 queries per row
+constexpr int kWaves = 8;               // 2 wavefronts per SIMD
+constexpr int kQB = 1;                  // 16-query blocks per wavefront
+constexpr int kThreads = 64 * kWaves;   // 512
+constexpr int kRowQ = 16 * kQB * kWaves;  // 128 queries per row
 constexpr int kMaxGrid = 256;
 constexpr float kTau = 4.0f;            // lazy rescale threshold, log2 units
 constexpr float kLog2e = 1.4426950408889634f;
@@ -205,10 +206,10 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
     scale_from_absmax(qa, q_scale, q_inv);
     const float c0 = a.score_scale * q_scale;
 
-    v8i qop[2];
+    v8i qop[kQB];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int i = qt * kRowQ + w * 32 + qb * 16 + li;
+    for (int qb = 0; qb < kQB; ++qb) {
+      const int i = qt * kRowQ + w * (16 * kQB) + qb * 16 + li;
       uint32_t wd[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       if (i < a.nq && g_live) {
         const uint16_t* src = a.q + ((int64_t)i * a.heads + head) * D + 32 * g;
@@ -236,13 +237,16 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
       for (int j = 0; j < 8; ++j) qop[qb][j] = int(wd[j]);
     }
 
-    float m_run[2] = {-INFINITY, -INFINITY};
-    float l_run[2] = {0.0f, 0.0f};   // this lane's share of the row sums
-    v4f acc[2][NDB];
+    float m_run[kQB];
+    float l_run[kQB];   // this lane's share of the row sums
+    v4f acc[kQB][NDB];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < kQB; ++qb) {
+      m_run[qb] = -INFINITY;
+      l_run[qb] = 0.0f;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) acc[qb][db] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    }
 
     auto phys = [&](int k) -> int64_t { return k < a.n1 ? a.first1 + k : a.first2 + (k - a.n1); };
 
@@ -293,24 +297,29 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
         __syncthreads();
       }
 
-      // ---- S^T blocks: rows = 16 slots, columns = 16 queries
-      v4f sacc[2][8];
+      // ---- S^T blocks: rows = 16 slots, columns = 16 queries.  All operand reads are issued
+      // before the products so that LDS latency is paid once per tile.
+      v4f sacc[kQB][8];
       const uint8_t* kt = sm.k[b];
+      v8i kop[8];
 #pragma unroll
       for (int bb = 0; bb < 8; ++bb) {
         const int u = 16 * bb + li;
-        v8i kop = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+        kop[bb] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
         if (g_live) {
           const uint4 x0 = *reinterpret_cast<const uint4*>(kt + u * D + (((2 * g) ^ (u % NCH)) << 4));
           const uint4 x1 = *reinterpret_cast<const uint4*>(kt + u * D + (((2 * g + 1) ^ (u % NCH)) << 4));
-          kop = v8i{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
+          kop[bb] = v8i{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
         }
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) sacc[qb][bb] = mfma_fp8(kop, qop[qb], v4f{0, 0, 0, 0}, 127);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int bb = 0; bb < 8; ++bb)
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) sacc[qb][bb] = mfma_fp8(kop[bb], qop[qb], v4f{0, 0, 0, 0}, 127);
 
       __builtin_amdgcn_sched_barrier(0);
-      v8i phi[2], plo[2];
+      v8i phi[kQB], plo[kQB];
       int sc_hi, sc_lo;
       if (fast) {
         // one K scale and one V scale over the tile: P' = P * f, f = vs0 * 2^-e in [0.5, 1),
@@ -323,7 +332,7 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
         sc_hi = 127 + e;
         sc_lo = 127 + e - 8;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < kQB; ++qb) {
           float rmax = sacc[qb][0][0];
 #pragma unroll
           for (int bb = 0; bb < 8; ++bb)
@@ -367,7 +376,7 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
         sc_hi = 127 + e;
         sc_lo = 127 + e - 8;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < kQB; ++qb) {
           float tmax = -INFINITY;
 #pragma unroll
           for (int bb = 0; bb < 8; ++bb) {
@@ -410,29 +419,36 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
 
-      // ---- O^T blocks: rows = 16 channels, columns = 16 queries
+      // ---- O^T blocks: rows = 16 channels, columns = 16 queries.  Operand reads first; then
+      // the hi products of all blocks and the lo products, so that each lo product (same
+      // accumulator) follows its hi product by 8 independent ones.
       const uint8_t* vt = sm.v[b];
+      v8i vop[NDB];
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const int d = 16 * db + li;
         const uint4 x0 = *reinterpret_cast<const uint4*>(vt + d * kTile + (((2 * g) ^ (d & 7)) << 4));
         const uint4 x1 = *reinterpret_cast<const uint4*>(vt + d * kTile + (((2 * g + 1) ^ (d & 7)) << 4));
-        v8i vop = v8i{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          acc[qb][db] = mfma_fp8(vop, phi[qb], acc[qb][db], sc_hi);
-          acc[qb][db] = mfma_fp8(vop, plo[qb], acc[qb][db], sc_lo);
-        }
+        vop[db] = v8i{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[qb][db] = mfma_fp8(vop[db], phi[qb], acc[qb][db], sc_hi);
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[qb][db] = mfma_fp8(vop[db], plo[qb], acc[qb][db], sc_lo);
 
       __builtin_amdgcn_s_waitcnt(0);   // this thread's copies of the next tile have landed
       __syncthreads();                 // everyone's have, and buffer b is free again
     }
 
     // ---- segment result: direct output, or partial + merge by the last work-group of the row
-    float lt[2];
+    float lt[kQB];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < kQB; ++qb) {
       lt[qb] = l_run[qb];
       lt[qb] += __shfl_xor(lt[qb], 16, 64);
       lt[qb] += __shfl_xor(lt[qb], 32, 64);
@@ -441,8 +457,8 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
       // split row: unnormalised partial result; attn_combine merges the row after this kernel
       const int64_t slot0 = ((int64_t)row * a.max_seg + seg) * kRowQ;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int ql = w * 32 + qb * 16 + li;
+      for (int qb = 0; qb < kQB; ++qb) {
+        const int ql = w * (16 * kQB) + qb * 16 + li;
         float* po = a.part_o + (slot0 + ql) * D + 4 * g;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
@@ -453,8 +469,8 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
       }
     } else {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int i = qt * kRowQ + w * 32 + qb * 16 + li;
+      for (int qb = 0; qb < kQB; ++qb) {
+        const int i = qt * kRowQ + w * (16 * kQB) + qb * 16 + li;
         if (i >= a.nq) continue;
         const float il = lt[qb] > 0.0f ? 1.0f / lt[qb] : 0.0f;
         uint16_t* dst = a.out + ((int64_t)i * a.heads + head) * D + 4 * g;
