@@ -39,6 +39,13 @@ ROPE_POS = 16384
 FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 matrix-core peak
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E peak
 ATT_FLOP = 4.0 * N * S * D * H
+ATT_KERNEL = "attn_stream<128>"
+# HBM bytes per launch of the main attention kernel from two rocprofv3 --pmc passes
+# (FETCH_SIZE, WRITE_SIZE) over this workload, each divided by the factor the same counter
+# reads for a torch copy of --calibrate-copy bytes.  Valid only for the kernel sources whose
+# hash is recorded; reported as null otherwise.
+ATT_TRAFFIC = {"sources": "4a3c2222daf93678", "bytes": 172_616_000,
+               "read_bytes": 147_060_000, "write_bytes": 25_560_000}
 WRITE_BYTES = 2 * N * H * D * 2 + 2 * N * H * D + 2 * N * H * 4
 ROTATE_BYTES = 2 * (H * S * D + H * S * 4)
 
@@ -54,6 +61,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-chunk", action="store_true", help="skip the 240-call chunk measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="also run one plain device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of heads on one GPU; --gpus {args.gpus} is not "
@@ -96,6 +105,14 @@ def main() -> int:
     ws_r = torch.empty(kv.workspace_bytes(kv.OP_DELTA_ROTATE, H, S, D, 0), dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
     lse = torch.empty((H, N), dtype=torch.float32, device=dev)
+
+    if args.calibrate_copy > 0:
+        src = torch.empty(args.calibrate_copy, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step():
         kv.kv_ring_write(ring, k_new, v_new, start, pos0, tab, workspace=ws_w, stream=stream)
@@ -241,12 +258,30 @@ def main() -> int:
                          "frac_hbm_peak": round(rot_gbps / HBM_PEAK_GBPS, 4), "bytes": ROTATE_BYTES},
         "chunk": chunk,
         "roofline": {"bound": "mfma", "achieved": round(att_tflops, 1), "peak": FP8_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(att_tflops / FP8_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "attn_main<128>", "flop_per_launch": ATT_FLOP},
+                     "unit": "TFLOP/s", "frac": round(att_tflops / FP8_PEAK_TFLOPS, 4),
+                     "traffic": attention_traffic(), "kernel": ATT_KERNEL, "flop_per_launch": ATT_FLOP},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def kernel_sources_hash() -> str:
+    """blake2b of the sources the main attention kernel is compiled from."""
+    import hashlib
+    h = hashlib.blake2b(digest_size=8)
+    for f in ("ring_attention.hip", "kvring_common.hpp", "kvring_internal.hpp"):
+        with open(os.path.join(ROOT, "fp8_ring_kv_write_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def attention_traffic():
+    """Counter-measured HBM bytes per launch of the main attention kernel, or None when the
+    kernel sources changed since the counters were taken."""
+    if ATT_TRAFFIC is None or ATT_TRAFFIC["sources"] != kernel_sources_hash():
+        return None
+    return ATT_TRAFFIC["bytes"]
 
 
 def cpu_baseline(np, sched, k_new, v_new, q, start, pos0, scale):
