@@ -15,7 +15,6 @@ from ._lib import (  # noqa: F401
     TILE,
     library_path,
     codes_bytes,
-    v_pos,
     rope_table,
     workspace_bytes,
     kv_ring_write,

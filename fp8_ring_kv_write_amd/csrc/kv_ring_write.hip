@@ -162,12 +162,12 @@ __global__ __launch_bounds__(kThreads) void write_quantize(
   __syncthreads();
 
   // V: transposed tile rows.  Work item = (channel d, group of 4 consecutive slots q); the
-  // four slots land in 4 consecutive bytes of row d.
+  // chunk's 32 slots are 32 consecutive bytes of row d.
   const int64_t tile = (int64_t)chunk * kChunk / kTile;
   const int u0 = (chunk * kChunk) % kTile;
   for (int item = threadIdx.x; item < D * (kChunk / 4); item += kThreads) {
     const int d = item >> 3, q = item & 7;
-    uint8_t* row = vc + (((int64_t)h * g.tiles + tile) * D + d) * kTile + vt_pos(u0 + 4 * q);
+    uint8_t* row = vc + (((int64_t)h * g.tiles + tile) * D + d) * kTile + u0 + 4 * q;
     uint32_t word = 0;
     int nmine = 0;
     bool m4[4];

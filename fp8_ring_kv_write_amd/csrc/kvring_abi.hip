@@ -48,7 +48,6 @@ int64_t kv_ring_codes_bytes(int32_t heads, int32_t slots, int32_t head_dim) {
   return (int64_t)heads * kvring::tile_count(slots) * kvring::kTile * head_dim;
 }
 
-int32_t kv_ring_v_pos(int32_t u) { return (u < 0 || u >= kvring::kTile) ? -1 : kvring::vt_pos(u); }
 
 int kv_ring_rope_table(float* host_out, int64_t n_pos, int32_t head_dim, double base) {
   if (!host_out) return KV_RING_ERR_NULL;

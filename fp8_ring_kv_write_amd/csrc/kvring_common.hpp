@@ -2,9 +2,8 @@
 //
 // Cache layout in HBM (per ring = one layer, one GPU's share of heads):
 //   K codes  [heads][tiles*128][head_dim]   row-major, one 128-slot tile after another
-//   V codes  [heads][tiles][head_dim][128]  each 128-slot tile stored transposed, with the
-//                                           slots of a row permuted into the order the
-//                                           PV matrix-core operand reads them (see vt_pos)
+//   V codes  [heads][tiles][head_dim][128]  each 128-slot tile stored transposed
+//                                           (channel-major, slots in order)
 //   scales   [heads][slots] float32         dequantisation scale of the write that filled
 //                                           each slot (k_scale, v_scale)
 // tiles = ceil(slots / 128); slots past `slots` in the last tile are never valid.
@@ -27,14 +26,6 @@ typedef short v2s __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
 __host__ __device__ inline int64_t tile_count(int32_t slots) { return (slots + kTile - 1) / kTile; }
-
-// Position of slot u (0..127 inside a tile) inside a transposed V row.  The PV product
-// reads, in lane group g (0..3) and operand byte s (0..31), the slot 16*(s/4) + 4*g + s%4;
-// storing that slot at byte 32*g + s makes each lane's 32-byte operand contiguous.
-__host__ __device__ inline int vt_pos(int u) {
-  const int b = u >> 4, g = (u >> 2) & 3, r = u & 3;
-  return 32 * g + 4 * b + r;
-}
 
 // bfloat16 bit pattern -> float32 (exact).
 __device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }

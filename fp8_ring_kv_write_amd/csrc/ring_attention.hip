@@ -44,9 +44,9 @@ hipError_t launch_q_absmax(const uint16_t* q, int32_t nq, int32_t heads, int32_t
 namespace {
 
 constexpr int kWaves = 8;               // 2 wavefronts per SIMD
-constexpr int kQB = 1;                  // 16-query blocks per wavefront
 constexpr int kThreads = 64 * kWaves;   // 512
-constexpr int kRowQ = 16 * kQB * kWaves;  // 128 queries per row
+constexpr int kRowQ = 16 * kWaves;      // 128 queries per row, 16 per wavefront
+constexpr int kBufs = 4;                // LDS tile buffers: tiles k-1, k, k+1 in use, k+2 landing
 constexpr int kMaxGrid = 256;
 constexpr float kTau = 4.0f;            // lazy rescale threshold, log2 units
 constexpr float kLog2e = 1.4426950408889634f;
@@ -75,13 +75,15 @@ struct AttnArgs {
 
 template <int D>
 struct Smem {
-  uint8_t k[2][kTile * D];
-  uint8_t v[2][D * kTile];
-  float ks[2][kTile];
-  float vs[2][kTile];
-  float ckf[kTile];   // general path: c0 * k_scale of valid slots, 0 otherwise
-  float nb[kTile];    // general path: 0 for valid slots, -inf otherwise
-  float vf[kTile];    // general path: v_scale of valid slots, 0 otherwise
+  uint8_t k[kBufs][kTile * D];
+  uint8_t v[kBufs][D * kTile];
+  float ks[kBufs][kTile];
+  float vs[kBufs][kTile];
+  float ck[kBufs][kTile];   // per slot: c0 * k_scale (valid) or 0
+  float nb[kBufs][kTile];   // per slot: log2(v_scale) (valid) or -inf
+  float iv[kBufs][kTile];   // per slot: 1 / v_scale (valid) or 0
+  int eg[kBufs][4];         // exponent of the largest valid v_scale per 32 slots (-128: none)
+  int uni[kBufs][2];        // per 64 slots: all valid, one K scale and one V scale (1) or not
   float red[kWaves];
 };
 
@@ -93,6 +95,14 @@ __device__ inline uint16_t f32_to_bf16(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);
   return uint16_t(u >> 16);
+}
+
+// max over lanes l, l^16, l^32, l^48 (the four lane groups holding one query's scores)
+__device__ inline float max_over_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __builtin_fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // Valid slot range(s) of tile t as u-intervals [lo1, hi1) and [lo2, hi2) within 0..127.
@@ -117,52 +127,290 @@ __device__ inline TileValid tile_valid(int64_t t, int head, int filled, int slot
   return v;
 }
 
-// Issue the asynchronous copies of ring tile t (K, transposed V, both scale rows) into buffer b.
-// The per-lane offsets are recomputed on every call from a lane index the compiler cannot
-// treat as loop-invariant, so they do not stay live in registers across the tile loop.
+// K tile rows in LDS: row u's 16-byte chunk c sits at position c ^ k_swz(u).  The QK product
+// reads, for score block bb, the rows 32*(l>>2) + 4*bb + (l&3) in lanes l = 0..15 (see
+// k_row); the swizzle spreads those 16 rows over all LDS banks.
 template <int D>
-__device__ inline void issue_tile(const AttnArgs& a, Smem<D>& sm, int b, int64_t t, int h,
-                                  int w, int lane_in) {
-  constexpr int NCH = D / 16;                   // 16-byte chunks per K row
-  constexpr int KCH = kTile * NCH;              // chunks per K tile (= per V tile)
-  int lane = lane_in;
-  asm volatile("" : "+v"(lane));
+__device__ inline int k_swz(int u) {
+  if constexpr (D == 128) return ((u & 3) | (((u >> 5) & 1) << 2)) ^ ((u >> 6) & 1);
+  else return (u >> 5) & 3;
+}
+
+// Tile row (slot) that lane li (0..15) feeds into the QK product of score block bb.  Output
+// row 4g+r of that block is then slot 32g + 4bb + r: lane group g ends up holding slots
+// 32g .. 32g+31 of its query across the 8 blocks -- in order, which is the B-operand layout
+// of the PV product over a tile whose V rows are stored in slot order.
+__device__ inline int k_row(int bb, int li) { return 32 * (li >> 2) + 4 * bb + (li & 3); }
+
+// Per-lane byte offsets of a wavefront's share of one tile copy: chunk c = (j*8 + w)*64 + lane
+// of the K tile (row c / NCH, LDS position c % NCH, holding the row's chunk p ^ k_swz(row)) and
+// of the transposed V tile (row c / 8, LDS position c % 8, holding chunk p ^ (row % 8)); and the
+// slot of the scale row a lane of wavefronts 0..3 copies.  Loop-invariant, computed once.
+template <int D>
+struct CopyOffs {
+  uint32_t k[(kTile * D / 16) / kThreads], v[(kTile * D / 16) / kThreads];
+  int su;
+};
+
+template <int D>
+__device__ inline CopyOffs<D> copy_offsets(int w, int lane) {
+  constexpr int NCH = D / 16;
+  CopyOffs<D> o;
+#pragma unroll
+  for (int j = 0; j < (kTile * NCH) / kThreads; ++j) {
+    const unsigned c = unsigned((j * kWaves + w) * 64 + lane);
+    const unsigned u = c / NCH;
+    o.k[j] = u * D + (((c % NCH) ^ unsigned(k_swz<D>(int(u)))) << 4);
+    o.v[j] = (c >> 3) * kTile + (((c & 7u) ^ ((c >> 3) & 7u)) << 4);
+  }
+  o.su = (w & 1) * 64 + lane;
+  return o;
+}
+
+// Issue the asynchronous copies of ring tile t (K, transposed V, both scale rows) into buffer b.
+template <int D>
+__device__ inline void issue_tile(const AttnArgs& a, Smem<D>& sm, const CopyOffs<D>& co, int b,
+                                  int64_t t, int h, int w) {
+  constexpr int NCH = D / 16;
   const uint8_t* kbase = a.kc + ((int64_t)h * a.tiles + t) * (kTile * D);   // uniform
   const uint8_t* vbase = a.vc + ((int64_t)h * a.tiles + t) * (D * kTile);   // uniform
 #pragma unroll
-  for (int j = 0; j < KCH / kThreads; ++j) {
+  for (int j = 0; j < (kTile * NCH) / kThreads; ++j) {
     const int c0 = (j * kWaves + w) * 64;      // first chunk of this wavefront's copy
-    const int c = c0 + lane;
-    // K: LDS chunk c = row u, position p holds the row's chunk p ^ (u % NCH)
-    const uint32_t koff = uint32_t((c / NCH) * D + (((c % NCH) ^ ((c / NCH) % NCH)) << 4));
-    __builtin_amdgcn_global_load_lds(kbase + koff, (lds_ptr)&sm.k[b][c0 * 16], 16, 0, 0);
-    // V: LDS chunk c = row d, position p holds the row's chunk p ^ (d % 8)
-    const uint32_t voff = uint32_t((c >> 3) * kTile + (((c & 7) ^ ((c >> 3) & 7)) << 4));
-    __builtin_amdgcn_global_load_lds(vbase + voff, (lds_ptr)&sm.v[b][c0 * 16], 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(kbase + co.k[j], (lds_ptr)&sm.k[b][c0 * 16], 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vbase + co.v[j], (lds_ptr)&sm.v[b][c0 * 16], 16, 0, 0);
   }
   if (w < 4) {   // wavefronts 0,1: K scales; 2,3: V scales (64 slots each)
-    const int u = (w & 1) * 64 + lane;
-    const int slot = min(int(t) * kTile + u, a.slots - 1);   // in bounds; padding masked later
+    const int slot = min(int(t) * kTile + co.su, a.slots - 1);   // in bounds; padding masked later
     const float* src = ((w < 2) ? a.k_scale : a.v_scale) + (int64_t)h * a.slots + slot;
     float* dst = (w < 2) ? &sm.ks[b][(w & 1) * 64] : &sm.vs[b][(w & 1) * 64];
     __builtin_amdgcn_global_load_lds(src, (lds_ptr)dst, 4, 0, 0);
   }
 }
 
+// Per-slot factors of the tile in buffer b, and zeroed K and V bytes for invalid slots (so that
+// whatever they hold -- NaN codes included -- never reaches a product).  Wavefronts 0 and 1 take
+// one slot per lane; the zeroing (tiles with invalid slots only) is shared by all and followed
+// by a barrier.  With vmax = f * 2^e (f in [0.5, 1)) the largest valid V scale of the tile, the
+// probabilities enter the PV product as P * v_scale * 2^-e <= P, and the product's B-operand
+// scale multiplies back by 2^e (one exponent per tile: the scale of the FP8 matrix product
+// applies per 32-element block of its contraction, and a block gathers 16-slot pieces of two
+// lane groups).
+template <int D>
+__device__ inline void prep_tile(Smem<D>& sm, int b, const TileValid& tvd, float c0, int tid) {
+  constexpr int NCH = D / 16;
+  if (tid < kTile) {
+    const int u = tid;
+    const bool ok = tvd.has(u);
+    const float vsu = sm.vs[b][u];
+    float vmax = ok ? vsu : 0.0f;
+#pragma unroll
+    for (int off = 16; off > 0; off >>= 1) vmax = __builtin_fmaxf(vmax, __shfl_xor(vmax, off, 64));
+    int e = -128;
+    if (vmax > 0.0f) {
+      (void)__builtin_frexpf(vmax, &e);
+      e = max(-110, min(120, e));
+    }
+    sm.ck[b][u] = ok ? c0 * sm.ks[b][u] : 0.0f;
+    sm.nb[b][u] = ok ? __log2f(vsu) : -INFINITY;
+    sm.iv[b][u] = ok ? 1.0f / vsu : 0.0f;
+    if ((u & 31) == 0) sm.eg[b][u >> 5] = e;
+    const bool same = ok && sm.ks[b][u] == sm.ks[b][0] && vsu == sm.vs[b][0];
+    const bool all_same = __all(same);
+    if ((u & 63) == 0) sm.uni[b][u >> 6] = all_same ? 1 : 0;
+  }
+  if (tvd.count() < kTile) {
+    uint8_t* kw = sm.k[b];
+    for (int c = tid; c < kTile * NCH; c += kThreads)   // whole 16-byte chunks of K rows
+      if (!tvd.has(c / NCH)) *reinterpret_cast<uint4*>(kw + c * 16) = make_uint4(0, 0, 0, 0);
+    uint8_t* vw = sm.v[b];
+    for (int c = tid; c < D * 8; c += kThreads) {        // 16-byte chunks of V rows
+      const int u0 = ((c & 7) ^ ((c >> 3) & 7)) * 16;    // first slot of the chunk
+      uint4 x = *reinterpret_cast<uint4*>(vw + c * 16);
+      uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk)
+        if (!tvd.has(u0 + kk)) xw[kk >> 2] &= ~(0xFFu << (8 * (kk & 3)));
+      *reinterpret_cast<uint4*>(vw + c * 16) = make_uint4(xw[0], xw[1], xw[2], xw[3]);
+    }
+    __syncthreads();
+  }
+}
+
+// Per-lane LDS byte offsets (within one buffer) of the two 16-byte halves of a lane's A
+// operand for score block 0 (K) and channel block 0 (V).  Block bb / db adds bb*4*D bytes
+// (K: rows k_row(bb, li) = k_row(0, li) + 4bb, whose swizzle does not depend on bb) and
+// db*16*128 bytes (V rows 16db + li, swizzled by li % 8).
+struct LaneOffs {
+  int k0, k1, v0, v1;
+};
+
+template <int D>
+__device__ inline LaneOffs lane_offsets(int lane) {
+  const int g = lane >> 4, li = lane & 15;
+  const int u = k_row(0, li);
+  const int sw = k_swz<D>(u);
+  LaneOffs o;
+  o.k0 = u * D + (((2 * g) ^ sw) << 4);
+  o.k1 = u * D + (((2 * g + 1) ^ sw) << 4);
+  o.v0 = li * kTile + (((2 * g) ^ (li & 7)) << 4);
+  o.v1 = li * kTile + (((2 * g + 1) ^ (li & 7)) << 4);
+  return o;
+}
+
+// A operand of score block bb (16 K rows) / of channel block db (16 transposed V rows).
+template <int D>
+__device__ inline v8i k_operand(const uint8_t* kt, const LaneOffs& o, int bb, int g) {
+  if (D != 128 && g >= 2) return v8i{0, 0, 0, 0, 0, 0, 0, 0};   // head_dim 64: upper half zero
+  const uint4 x0 = *reinterpret_cast<const uint4*>(kt + o.k0 + bb * 4 * D);
+  const uint4 x1 = *reinterpret_cast<const uint4*>(kt + o.k1 + bb * 4 * D);
+  return v8i{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
+}
+
+__device__ inline v8i v_operand(const uint8_t* vt, const LaneOffs& o, int db) {
+  const uint4 x0 = *reinterpret_cast<const uint4*>(vt + o.v0 + db * 16 * kTile);
+  const uint4 x1 = *reinterpret_cast<const uint4*>(vt + o.v1 + db * 16 * kTile);
+  return v8i{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
+}
+
 // P (<= 16, non-negative) -> FP8 hi part and FP8 lo part of (P - hi) * 2^8, four values per dword.
-__device__ inline int2 split_p(const float (&p)[4]) {
-  int hw = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+// old: any two dwords (dead values); each conversion pair writes both halves of its dword.
+__device__ inline int2 split_p(const float (&p)[4], int2 old) {
+  int hw = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], old.x, false);
   hw = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], hw, true);
   const v2f h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
   const v2f h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
-  v2s lw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, p[0] - h01[0], p[1] - h01[1], 0x1p-8f, false);
+  v2s lw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(__builtin_bit_cast(v2s, old.y),
+                                                    p[0] - h01[0], p[1] - h01[1], 0x1p-8f, false);
   lw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lw, p[2] - h23[0], p[3] - h23[1], 0x1p-8f, true);
   return make_int2(hw, int(uint32_t(uint16_t(lw[0])) | (uint32_t(uint16_t(lw[1])) << 16)));
 }
 
+// Running softmax state and output accumulator of one wavefront (16 queries; lane (g, li)
+// holds query li's channels 16*db + 4g .. +3 of every channel block db).
+template <int D>
+struct RowState {
+  v4f acc[D / 16];
+  float m;   // running max (log2 units), identical in the 4 lanes of a query
+  float l;   // this lane's share of the running sum
+};
+
+// Probabilities of one tile as the B operand of the PV product, with their exponent scales.
+struct PTile {
+  v8i hi, lo;
+  int sc_hi, sc_lo;
+};
+
+// One pipeline step of a wavefront:
+//   softmax of tile k   (raw scores s; factors in LDS buffer bk) -> probabilities pc
+//   PV of tile k-1      (probabilities pp; V in LDS buffer bp), interleaved with the softmax
+//   QK of tile k+1      (K in LDS buffer bn) -> raw scores, into s
+// The PV products do not depend on tile k, so the matrix cores work while the vector units
+// form tile k's probabilities.  A rescale found by tile k's max is applied to the accumulator
+// after the PV of tile k-1, whose probabilities were formed against the old max.
+//
+// Per score (slot j, query i):  t = raw * ck_j + nb_j, the log2-domain score plus log2 of the
+// slot's V scale; P' = 2^(t - e - m) goes to the PV product (whose B-operand scale is 2^e) and
+// P' * iv_j * 2^e = 2^(score - m) to the row sum.  The running max m tracks max (t - e).
+template <int D>
+__device__ __forceinline__ void pipeline_step(const Smem<D>& sm, int bk, int bp, int bn, int g,
+                                              const LaneOffs& lo, const v8i& qop, v4f (&sc)[8],
+                                              const PTile& pp, PTile& pc, RowState<D>& st) {
+  constexpr int NDB = D / 16;
+  const uint8_t* vt = sm.v[bp];
+  const uint8_t* kt = sm.k[bn];
+  const int4 egv = *reinterpret_cast<const int4*>(&sm.eg[bk][0]);
+  int e = max(max(egv.x, egv.y), max(egv.z, egv.w));
+  e = e == -128 ? 0 : e;
+  const float fe = float(e);
+  pc.sc_hi = 127 + e;
+  pc.sc_lo = 127 + e - 8;
+
+  // ---- tile k: scores with their factors, max, rescale decision.  A uniform tile (all slots
+  // valid, one K scale, one V scale) keeps its raw scores: t = raw * c + b for every slot.
+  const int2 un = *reinterpret_cast<const int2*>(&sm.uni[bk][0]);
+  float cf = 1.0f, bf = 0.0f, tmax;
+  if (un.x & un.y) {
+    cf = sm.ck[bk][0];
+    bf = sm.nb[bk][0];
+    float rmax = sc[0][0];
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rmax = __builtin_fmaxf(rmax, sc[bb][r]);
+    tmax = max_over_groups(rmax) * cf + bf - fe;
+  } else {
+    tmax = -INFINITY;
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb) {
+      const float4 ck = *reinterpret_cast<const float4*>(&sm.ck[bk][32 * g + 4 * bb]);
+      const float4 nb = *reinterpret_cast<const float4*>(&sm.nb[bk][32 * g + 4 * bb]);
+      sc[bb][0] = __builtin_fmaf(sc[bb][0], ck.x, nb.x);
+      sc[bb][1] = __builtin_fmaf(sc[bb][1], ck.y, nb.y);
+      sc[bb][2] = __builtin_fmaf(sc[bb][2], ck.z, nb.z);
+      sc[bb][3] = __builtin_fmaf(sc[bb][3], ck.w, nb.w);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tmax = __builtin_fmaxf(tmax, sc[bb][r]);
+    }
+    tmax = max_over_groups(tmax) - fe;
+  }
+  const bool need = __any(tmax > st.m + kTau);
+  float alpha = 1.0f;
+  if (need) {
+    const float m_new = __builtin_fmaxf(st.m, tmax);
+    alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(st.m - m_new);
+    st.m = m_new;
+  }
+  const float bm = bf - ((st.m == -INFINITY ? 0.0f : st.m) + fe);   // P' = 2^(s * cf + bm)
+
+  // ---- PV(k-1) interleaved with tile k's probabilities.  V operands are read from LDS one
+  // block ahead; the scheduling barriers keep the blocks in order so that few are live.
+  float lsum = 0.0f;
+  v8i vo_n = v_operand(vt, lo, 0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int s8 = 0; s8 < 8; ++s8) {
+    const int db = s8 * NDB / 8;                 // channel block of this step (D = 64: every other)
+    const bool pv = (s8 * NDB) % 8 == 0;
+    v8i vo = vo_n;
+    if (pv && db + 1 < NDB) vo_n = v_operand(vt, lo, db + 1);
+    if (pv) st.acc[db] = mfma_fp8(vo, pp.hi, st.acc[db], pp.sc_hi);
+    const float4 iv = *reinterpret_cast<const float4*>(&sm.iv[bk][32 * g + 4 * s8]);
+    const float ivr[4] = {iv.x, iv.y, iv.z, iv.w};
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[s8][r], cf, bm));
+      lsum = __builtin_fmaf(p[r], ivr[r], lsum);
+    }
+    int2 hl = split_p(p, make_int2(pc.hi[s8], pc.lo[s8]));
+    // pin the block's vector work here, between its two products (otherwise it is sunk
+    // below the branches that follow, away from the products it should overlap)
+    asm volatile("" : "+v"(hl.x), "+v"(hl.y), "+v"(lsum));
+    pc.hi[s8] = hl.x;
+    pc.lo[s8] = hl.y;
+    if (pv) st.acc[db] = mfma_fp8(vo, pp.lo, st.acc[db], pp.sc_lo);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // ---- QK(k+1): the raw scores of the next tile replace this tile's
+  v8i ko_n = k_operand<D>(kt, lo, 0, g);
+#pragma unroll
+  for (int bb = 0; bb < 8; ++bb) {
+    const v8i ko = ko_n;
+    if (bb + 1 < 8) ko_n = k_operand<D>(kt, lo, bb + 1, g);
+    sc[bb] = mfma_fp8(ko, qop, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 127);
+  }
+  if (need) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) st.acc[db] *= alpha;
+    st.l *= alpha;
+  }
+  st.l += lsum * __builtin_ldexpf(1.0f, e);
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
-  constexpr int NCH = D / 16;
   constexpr int NDB = D / 16;
   __shared__ __align__(16) Smem<D> sm;
 
@@ -177,20 +425,24 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
   };
   int64_t ub = (int64_t)v * a.units / a.grid;
   const int64_t ue = (int64_t)(v + 1) * a.units / a.grid;
+  const int tid = int(threadIdx.x);
+  const int lane = tid & 63, g = lane >> 4, li = lane & 15;
+  const CopyOffs<D> co = copy_offsets<D>(w, lane);
+  const LaneOffs lo = lane_offsets<D>(lane);
 
   while (ub < ue) {
-    // lane-derived values are recomputed per segment from an opaque copy of the thread index, so
-    // that the compiler does not hoist dozens of per-lane addresses out of this loop
-    int tid = int(threadIdx.x);
-    asm volatile("" : "+v"(tid));
-    const int lane = tid & 63, g = lane >> 4, li = lane & 15;
     const bool g_live = (D == 128) || (g < 2);
     const int row = int(ub / a.tv);
     const int k0 = int(ub % a.tv);
     const int k1 = int(min<int64_t>(a.tv, k0 + (ue - ub)));
+    const int nt = k1 - k0;
     const int head = row / a.qtiles, qt = row % a.qtiles;
     const int seg = v - owner((int64_t)row * a.tv);
     const int nseg = owner((int64_t)row * a.tv + a.tv - 1) - owner((int64_t)row * a.tv) + 1;
+    auto phys = [&](int k) -> int64_t { return k < a.n1 ? a.first1 + k : a.first2 + (k - a.n1); };
+
+    // first tile's copies go out before the query preparation
+    issue_tile<D>(a, sm, co, 0, phys(k0), head, w);
 
     // ---- query scale of the head, then this wavefront's quantised queries
     float qa = 0.0f;
@@ -198,6 +450,11 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
       qa = __builtin_fmaxf(qa, a.q_partial[(int64_t)head * a.n_qgroups + j]);
     for (int off = 32; off > 0; off >>= 1) qa = __builtin_fmaxf(qa, __shfl_xor(qa, off, 64));
     if (lane == 0) sm.red[w] = qa;
+    // the PV of the first step reads "tile k-1" from the last buffer: zeros
+    {
+      uint4* vz = reinterpret_cast<uint4*>(sm.v[kBufs - 1]);
+      for (int c = tid; c < D * kTile / 16; c += kThreads) vz[c] = make_uint4(0, 0, 0, 0);
+    }
     __syncthreads();
     qa = sm.red[0];
 #pragma unroll
@@ -206,10 +463,9 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
     scale_from_absmax(qa, q_scale, q_inv);
     const float c0 = a.score_scale * q_scale;
 
-    v8i qop[kQB];
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      const int i = qt * kRowQ + w * (16 * kQB) + qb * 16 + li;
+    v8i qop;
+    {
+      const int i = qt * kRowQ + w * 16 + li;
       uint32_t wd[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       if (i < a.nq && g_live) {
         const uint16_t* src = a.q + ((int64_t)i * a.heads + head) * D + 32 * g;
@@ -225,268 +481,104 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
             const float xe = __uint_as_float(bw[p] << 16), xo = __uint_as_float(bw[p] & 0xFFFF0000u);
-            const float c = cs[p][0], s = cs[p][1];
-            y[2 * p] = (xe * c - xo * s) * q_inv;
-            y[2 * p + 1] = (xe * s + xo * c) * q_inv;
+            const float cc = cs[p][0], ss = cs[p][1];
+            y[2 * p] = (xe * cc - xo * ss) * q_inv;
+            y[2 * p + 1] = (xe * ss + xo * cc) * q_inv;
           }
           wd[2 * j] = e4m3x4(y[0], y[1], y[2], y[3]);
           wd[2 * j + 1] = e4m3x4(y[4], y[5], y[6], y[7]);
         }
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) qop[qb][j] = int(wd[j]);
+      for (int j = 0; j < 8; ++j) qop[j] = int(wd[j]);
     }
 
-    float m_run[kQB];
-    float l_run[kQB];   // this lane's share of the row sums
-    v4f acc[kQB][NDB];
+    RowState<D> st;
+    st.m = -INFINITY;
+    st.l = 0.0f;
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      m_run[qb] = -INFINITY;
-      l_run[qb] = 0.0f;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) acc[qb][db] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    }
+    for (int db = 0; db < NDB; ++db) st.acc[db] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    PTile pa, pb;
+    pa.hi = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    pa.lo = pa.hi;
+    pa.sc_hi = pa.sc_lo = 127;
+    pb = pa;
+    v4f sc[8];
 
-    auto phys = [&](int k) -> int64_t { return k < a.n1 ? a.first1 + k : a.first2 + (k - a.n1); };
-
-    issue_tile<D>(a, sm, 0, phys(k0), head, w, lane);
+    // ---- prologue: tile k0 resident and prepared, its raw scores in sa
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (nt > 1) issue_tile<D>(a, sm, co, 1, phys(k0 + 1), head, w);
+    prep_tile(sm, 0, tile_valid(phys(k0), a.ring_head, a.filled, a.slots), c0, tid);
+    __syncthreads();
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb)
+      sc[bb] = mfma_fp8(k_operand<D>(sm.k[0], lo, bb, g), qop, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 127);
 
-    for (int k = k0; k < k1; ++k) {
-      const int b = (k - k0) & 1;
-      const int64_t t = phys(k);
-      if (k + 1 < k1) issue_tile<D>(a, sm, b ^ 1, phys(k + 1), head, w, lane);
-
-      const TileValid tvd = tile_valid(t, a.ring_head, a.filled, a.slots);
-      const bool full = tvd.count() == kTile;
-      const float ks0 = sm.ks[b][0], vs0 = sm.vs[b][0];
-      const bool same = sm.ks[b][lane] == ks0 && sm.ks[b][lane + 64] == ks0 &&
-                        sm.vs[b][lane] == vs0 && sm.vs[b][lane + 64] == vs0;
-      const bool fast = full && __all(same);
-      if (!fast) {
-        // general path (ring edges, partially filled rings, write boundaries): one cooperative
-        // pass stores per-slot factors and zeroes the K/V bytes of invalid slots in LDS before
-        // any product reads them, so the math below is branch-free.  `fast` is the same in
-        // every wavefront (same LDS data), so the barrier is reached by all.
-        for (int u = tid; u < kTile; u += kThreads) {
-          const bool ok = tvd.has(u);
-          sm.ckf[u] = ok ? c0 * sm.ks[b][u] : 0.0f;
-          sm.nb[u] = ok ? 0.0f : -INFINITY;
-          sm.vf[u] = ok ? sm.vs[b][u] : 0.0f;
-        }
-        if (!full) {
-          uint8_t* kw = sm.k[b];
-          for (int c = tid; c < kTile * NCH; c += kThreads)   // whole 16-byte chunks of K rows
-            if (!tvd.has(c / NCH)) *reinterpret_cast<uint4*>(kw + c * 16) = make_uint4(0, 0, 0, 0);
-          uint8_t* vw = sm.v[b];
-          for (int c = tid; c < D * 8; c += kThreads) {        // 16-byte chunks of V rows
-            const int pos0 = ((c & 7) ^ ((c >> 3) & 7)) * 16;   // row position of the chunk's bytes
-            uint4 x = *reinterpret_cast<uint4*>(vw + c * 16);
-            uint32_t xw[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-            for (int kk = 0; kk < 16; ++kk) {
-              const int pp = pos0 + kk;
-              const int u = 16 * ((pp & 31) >> 2) + 4 * (pp >> 5) + (pp & 3);   // inverse of vt_pos
-              if (!tvd.has(u)) xw[kk >> 2] &= ~(0xFFu << (8 * (kk & 3)));
-            }
-            *reinterpret_cast<uint4*>(vw + c * 16) = make_uint4(xw[0], xw[1], xw[2], xw[3]);
-          }
-        }
-        __syncthreads();
-      }
-
-      // ---- S^T blocks: rows = 16 slots, columns = 16 queries.  All operand reads are issued
-      // before the products so that LDS latency is paid once per tile.
-      v4f sacc[kQB][8];
-      const uint8_t* kt = sm.k[b];
-      v8i kop[8];
-#pragma unroll
-      for (int bb = 0; bb < 8; ++bb) {
-        const int u = 16 * bb + li;
-        kop[bb] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-        if (g_live) {
-          const uint4 x0 = *reinterpret_cast<const uint4*>(kt + u * D + (((2 * g) ^ (u % NCH)) << 4));
-          const uint4 x1 = *reinterpret_cast<const uint4*>(kt + u * D + (((2 * g + 1) ^ (u % NCH)) << 4));
-          kop[bb] = v8i{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int bb = 0; bb < 8; ++bb)
-#pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) sacc[qb][bb] = mfma_fp8(kop[bb], qop[qb], v4f{0, 0, 0, 0}, 127);
-
-      __builtin_amdgcn_sched_barrier(0);
-      v8i phi[kQB], plo[kQB];
-      int sc_hi, sc_lo;
-      if (fast) {
-        // one K scale and one V scale over the tile: P' = P * f, f = vs0 * 2^-e in [0.5, 1),
-        // folded into the exponent; the MFMA B-scale multiplies back by 2^e
-        int e = 0;
-        const float f = __builtin_frexpf(vs0, &e);
-        const float lf = __log2f(f);
-        const float inv_f = 1.0f / f;
-        const float c = c0 * ks0;
-        sc_hi = 127 + e;
-        sc_lo = 127 + e - 8;
-#pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) {
-          float rmax = sacc[qb][0][0];
-#pragma unroll
-          for (int bb = 0; bb < 8; ++bb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) rmax = __builtin_fmaxf(rmax, sacc[qb][bb][r]);
-          rmax = __builtin_fmaxf(rmax, __shfl_xor(rmax, 16, 64));
-          rmax = __builtin_fmaxf(rmax, __shfl_xor(rmax, 32, 64));
-          const float tmax = rmax * c;
-          if (__any(tmax > m_run[qb] + kTau)) {
-            const float m_new = __builtin_fmaxf(m_run[qb], tmax);
-            const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-            m_run[qb] = m_new;
-            l_run[qb] *= alpha;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) acc[qb][db] *= alpha;
-          }
-          const float bias = lf - m_run[qb];
-          float lsum = 0.0f;
-#pragma unroll
-          for (int bb = 0; bb < 8; ++bb) {
-            float p[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][bb][r], c, bias));
-              lsum += p[r];
-            }
-            const int2 hl = split_p(p);
-            phi[qb][bb] = hl.x;
-            plo[qb][bb] = hl.y;
-          }
-          l_run[qb] += lsum * inv_f;
-        }
-      } else {
-        // general path: per-slot factors prepared in LDS before the QK product (see above)
-        float vm = __builtin_fmaxf(sm.vf[lane], sm.vf[lane + 64]);
-        for (int off = 32; off > 0; off >>= 1) vm = __builtin_fmaxf(vm, __shfl_xor(vm, off, 64));
-        int e = 0;
-        if (vm > 0.0f) (void)__builtin_frexpf(vm, &e);
-        e = max(-120, min(120, e));
-        const float finv = __builtin_ldexpf(1.0f, -e);
-        sc_hi = 127 + e;
-        sc_lo = 127 + e - 8;
-#pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) {
-          float tmax = -INFINITY;
-#pragma unroll
-          for (int bb = 0; bb < 8; ++bb) {
-            const float4 ck = *reinterpret_cast<const float4*>(&sm.ckf[16 * bb + 4 * g]);
-            const float4 nb = *reinterpret_cast<const float4*>(&sm.nb[16 * bb + 4 * g]);
-            sacc[qb][bb][0] = __builtin_fmaf(sacc[qb][bb][0], ck.x, nb.x);
-            sacc[qb][bb][1] = __builtin_fmaf(sacc[qb][bb][1], ck.y, nb.y);
-            sacc[qb][bb][2] = __builtin_fmaf(sacc[qb][bb][2], ck.z, nb.z);
-            sacc[qb][bb][3] = __builtin_fmaf(sacc[qb][bb][3], ck.w, nb.w);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) tmax = __builtin_fmaxf(tmax, sacc[qb][bb][r]);
-          }
-          tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-          tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-          if (__any(tmax > m_run[qb] + kTau)) {
-            const float m_new = __builtin_fmaxf(m_run[qb], tmax);
-            const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-            m_run[qb] = m_new;
-            l_run[qb] *= alpha;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) acc[qb][db] *= alpha;
-          }
-          const float m_use = m_run[qb] == -INFINITY ? 0.0f : m_run[qb];
-#pragma unroll
-          for (int bb = 0; bb < 8; ++bb) {
-            const float4 vv = *reinterpret_cast<const float4*>(&sm.vf[16 * bb + 4 * g]);
-            const float vr[4] = {vv.x, vv.y, vv.z, vv.w};
-            float p[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float pr = __builtin_amdgcn_exp2f(sacc[qb][bb][r] - m_use);
-              l_run[qb] += pr;
-              p[r] = pr * (vr[r] * finv);
-            }
-            const int2 hl = split_p(p);
-            phi[qb][bb] = hl.x;
-            plo[qb][bb] = hl.y;
-          }
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-
-      // ---- O^T blocks: rows = 16 channels, columns = 16 queries.  Operand reads first; then
-      // the hi products of all blocks and the lo products, so that each lo product (same
-      // accumulator) follows its hi product by 8 independent ones.
+    // ---- pipeline over the segment's tiles; two steps per trip so that the two probability
+    // tiles swap roles without register copies
+    auto step = [&](int j, const PTile& pprev, PTile& pcur) {
+      const int bk = j & (kBufs - 1), bn = (j + 1) & (kBufs - 1), bp = (j + kBufs - 1) & (kBufs - 1);
+      __builtin_amdgcn_s_waitcnt(0);   // this thread's copies of tile k+1 have landed
+      __syncthreads();                 // everyone's have; buffer of tile k+2 is free
+      if (j + 2 < nt) issue_tile<D>(a, sm, co, (j + 2) & (kBufs - 1), phys(k0 + j + 2), head, w);
+      if (j + 1 < nt) prep_tile(sm, bn, tile_valid(phys(k0 + j + 1), a.ring_head, a.filled, a.slots), c0, tid);
+      pipeline_step<D>(sm, bk, bp, bn, g, lo, qop, sc, pprev, pcur, st);
+    };
+    auto final_pv = [&](int b, const PTile& pt) {
       const uint8_t* vt = sm.v[b];
-      v8i vop[NDB];
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const int d = 16 * db + li;
-        const uint4 x0 = *reinterpret_cast<const uint4*>(vt + d * kTile + (((2 * g) ^ (d & 7)) << 4));
-        const uint4 x1 = *reinterpret_cast<const uint4*>(vt + d * kTile + (((2 * g + 1) ^ (d & 7)) << 4));
-        vop[db] = v8i{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
+        const v8i vo = v_operand(vt, lo, db);
+        st.acc[db] = mfma_fp8(vo, pt.hi, st.acc[db], pt.sc_hi);
+        st.acc[db] = mfma_fp8(vo, pt.lo, st.acc[db], pt.sc_lo);
       }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) acc[qb][db] = mfma_fp8(vop[db], phi[qb], acc[qb][db], sc_hi);
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) acc[qb][db] = mfma_fp8(vop[db], plo[qb], acc[qb][db], sc_lo);
-
-      __builtin_amdgcn_s_waitcnt(0);   // this thread's copies of the next tile have landed
-      __syncthreads();                 // everyone's have, and buffer b is free again
+    };
+    for (int j = 0;;) {
+      step(j, pa, pb);
+      if (++j == nt) {
+        final_pv((j - 1) & (kBufs - 1), pb);
+        break;
+      }
+      step(j, pb, pa);
+      if (++j == nt) {
+        final_pv((j - 1) & (kBufs - 1), pa);
+        break;
+      }
     }
 
-    // ---- segment result: direct output, or partial + merge by the last work-group of the row
-    float lt[kQB];
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      lt[qb] = l_run[qb];
-      lt[qb] += __shfl_xor(lt[qb], 16, 64);
-      lt[qb] += __shfl_xor(lt[qb], 32, 64);
-    }
+    // ---- segment result: direct output, or partial for attn_combine
+    float lt = st.l;
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
     if (nseg > 1) {
-      // split row: unnormalised partial result; attn_combine merges the row after this kernel
       const int64_t slot0 = ((int64_t)row * a.max_seg + seg) * kRowQ;
+      const int ql = w * 16 + li;
+      float* po = a.part_o + (slot0 + ql) * D + 4 * g;
 #pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) {
-        const int ql = w * (16 * kQB) + qb * 16 + li;
-        float* po = a.part_o + (slot0 + ql) * D + 4 * g;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const v4f o = acc[qb][db];
-          *reinterpret_cast<float4*>(po + 16 * db) = make_float4(o[0], o[1], o[2], o[3]);
-        }
-        if (g == 0) *reinterpret_cast<float2*>(a.part_ml + (slot0 + ql) * 2) = make_float2(m_run[qb], lt[qb]);
+      for (int db = 0; db < NDB; ++db) {
+        const v4f o = st.acc[db];
+        *reinterpret_cast<float4*>(po + 16 * db) = make_float4(o[0], o[1], o[2], o[3]);
       }
+      if (g == 0) *reinterpret_cast<float2*>(a.part_ml + (slot0 + ql) * 2) = make_float2(st.m, lt);
     } else {
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) {
-        const int i = qt * kRowQ + w * (16 * kQB) + qb * 16 + li;
-        if (i >= a.nq) continue;
-        const float il = lt[qb] > 0.0f ? 1.0f / lt[qb] : 0.0f;
+      const int i = qt * kRowQ + w * 16 + li;
+      if (i < a.nq) {
+        const float il = lt > 0.0f ? 1.0f / lt : 0.0f;
         uint16_t* dst = a.out + ((int64_t)i * a.heads + head) * D + 4 * g;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const v4f o = acc[qb][db];
+          const v4f o = st.acc[db];
           const uint32_t lo = uint32_t(f32_to_bf16(o[0] * il)) | (uint32_t(f32_to_bf16(o[1] * il)) << 16);
           const uint32_t hi = uint32_t(f32_to_bf16(o[2] * il)) | (uint32_t(f32_to_bf16(o[3] * il)) << 16);
           *reinterpret_cast<uint2*>(dst + 16 * db) = make_uint2(lo, hi);
         }
         if (g == 0)
-          a.lse[(int64_t)head * a.nq + i] = lt[qb] > 0.0f ? (m_run[qb] + __log2f(lt[qb])) * kLn2 : -INFINITY;
+          a.lse[(int64_t)head * a.nq + i] = lt > 0.0f ? (st.m + __log2f(lt)) * kLn2 : -INFINITY;
       }
     }
     __syncthreads();   // LDS buffers are reused by the next segment
-    ub += k1 - k0;
+    ub += nt;
   }
 }
 

@@ -63,9 +63,9 @@ enum { KV_RING_OP_WRITE = 1, KV_RING_OP_DELTA_ROTATE = 2, KV_RING_OP_ATTENTION =
  * caller, 16-byte aligned.  With T = ceil(slots / 128) tiles:
  *   k        K codes, T*128*head_dim bytes per head, [heads][T*128][head_dim]: slot s of head h
  *            at byte (h*T*128 + s)*head_dim;
- *   v        V codes, the same size, each 128-slot tile stored transposed:
+ *   v        V codes, the same size, each 128-slot tile stored transposed (channel-major):
  *            [heads][T][head_dim][128]; channel d of slot s of head h is at byte
- *            ((h*T + s/128)*head_dim + d)*128 + kv_ring_v_pos(s % 128);
+ *            ((h*T + s/128)*head_dim + d)*128 + s % 128;
  *   k_scale  float32 [heads][slots], the dequantisation scale of the write that filled a slot;
  *   v_scale  float32 [heads][slots].
  * Limits: 1 <= heads <= 65535, 1 <= slots <= 1048576, head_dim in {64, 128}.
@@ -83,12 +83,6 @@ typedef struct kv_ring_desc {
 
 /* Bytes of one of the two code buffers (k or v): heads * ceil(slots/128) * 128 * head_dim. */
 int64_t kv_ring_codes_bytes(int32_t heads, int32_t slots, int32_t head_dim);
-
-/* Byte position of slot u (0..127 within its tile) inside a transposed V row:
- * pos(u) = 32*((u >> 2) & 3) + 4*(u >> 4) + (u & 3), a permutation of 0..127 under which
- * each lane of the PV matrix-core product reads its 32 slots as 32 contiguous bytes.
- * Returns -1 outside 0..127. */
-int32_t kv_ring_v_pos(int32_t u);
 
 /*
  * Fill a host float32 table [n_pos][head_dim/2][2] with cos and sin of p * theta_i for

@@ -11,18 +11,12 @@ import numpy as np
 TILE = 128
 
 
-def v_pos_formula(u: np.ndarray) -> np.ndarray:
-    u = np.asarray(u)
-    return 32 * ((u >> 2) & 3) + 4 * (u >> 4) + (u & 3)
-
-
 def logical_codes(k_buf: np.ndarray, v_buf: np.ndarray, heads: int, slots: int, head_dim: int):
     """Library code buffers (flat uint8) -> K, V codes [heads, slots, head_dim]."""
     tiles = (slots + TILE - 1) // TILE
     k = k_buf.reshape(heads, tiles * TILE, head_dim)[:, :slots, :]
     v4 = v_buf.reshape(heads, tiles, head_dim, TILE)
-    perm = v_pos_formula(np.arange(TILE))
-    v = v4[:, :, :, perm].transpose(0, 1, 3, 2).reshape(heads, tiles * TILE, head_dim)[:, :slots, :]
+    v = v4.transpose(0, 1, 3, 2).reshape(heads, tiles * TILE, head_dim)[:, :slots, :]
     return np.ascontiguousarray(k), np.ascontiguousarray(v)
 
 
@@ -43,7 +37,7 @@ def poison_free_slots_gpu(ring, valid: np.ndarray):
     kb[:, torch.from_numpy(free).to(kb.device), :] = 0x7F
     vb = ring.v.view(H, tiles, D, TILE)
     for s in free.tolist():
-        vb[:, s // TILE, :, int(v_pos_formula(s % TILE))] = 0xFF
+        vb[:, s // TILE, :, s % TILE] = 0xFF
     fs = free[free < S]
     nan = torch.tensor(float("nan"), device=ring.k_scale.device)
     ring.k_scale[:, torch.from_numpy(fs).to(kb.device)] = nan

@@ -46,17 +46,6 @@ def test_rope_table_matches_oracle_bit_for_bit(kv):
         assert ours.tobytes() == ref.tobytes()
 
 
-def test_v_pos_is_the_documented_permutation(kv):
-    pos = [kv.v_pos(u) for u in range(128)]
-    assert sorted(pos) == list(range(128))
-    for u in range(128):
-        assert pos[u] == 32 * ((u >> 2) & 3) + 4 * (u >> 4) + (u & 3)
-    # lane group g of the PV product reads slots 16*(s/4) + 4g + s%4 at bytes 32g + s
-    for g in range(4):
-        assert [pos[16 * (s // 4) + 4 * g + s % 4] for s in range(32)] == list(range(32 * g, 32 * g + 32))
-    assert kv.v_pos(-1) == -1 and kv.v_pos(128) == -1
-
-
 def test_sizes(kv):
     assert kv.codes_bytes(24, 5788, 128) == 24 * 46 * 128 * 128
     assert kv.codes_bytes(1, 64, 64) == 128 * 64
