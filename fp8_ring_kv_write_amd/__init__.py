@@ -15,6 +15,8 @@ from ._lib import (  # noqa: F401
     TILE,
     library_path,
     codes_bytes,
+    k_offset,
+    v_offset,
     rope_table,
     workspace_bytes,
     kv_ring_write,

@@ -45,6 +45,8 @@ def _load() -> ctypes.CDLL:
     dp = ctypes.POINTER(_Desc)
     sig = {
         "kv_ring_codes_bytes": (i64, [i32, i32, i32]),
+        "kv_ring_k_offset": (i64, [i64, i32, i32]),
+        "kv_ring_v_offset": (i64, [i64, i32, i32]),
         "kv_ring_rope_table": (ctypes.c_int, [vp, i64, i32, f64]),
         "kv_ring_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
         "kv_ring_write": (ctypes.c_int, [dp, vp, vp, i32, i32, i64, vp, i64, vp, sz, vp]),
@@ -79,6 +81,16 @@ def _check(fn: str, status: int) -> None:
 
 def codes_bytes(heads: int, slots: int, head_dim: int) -> int:
     return int(lib.kv_ring_codes_bytes(heads, slots, head_dim))
+
+
+def k_offset(slot: int, channel: int, head_dim: int) -> int:
+    """Byte offset of K channel `channel` of slot `slot` within one head's K codes (-1: invalid)."""
+    return int(lib.kv_ring_k_offset(slot, channel, head_dim))
+
+
+def v_offset(slot: int, channel: int, head_dim: int) -> int:
+    """Byte offset of V channel `channel` of slot `slot` within one head's V codes (-1: invalid)."""
+    return int(lib.kv_ring_v_offset(slot, channel, head_dim))
 
 
 def rope_table(n_pos: int, head_dim: int, base: float = 10000.0) -> np.ndarray:

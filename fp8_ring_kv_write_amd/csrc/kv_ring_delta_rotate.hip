@@ -64,7 +64,8 @@ __global__ __launch_bounds__(kThreads) void rotate_absmax_partials(
   float m = 0.0f;
   if (slot_valid(slot, g.head, g.filled, g.slots)) {
     uint32_t w[CPT / 4];
-    load_codes<CPT>(kc + ((int64_t)h * g.tiles * kTile + slot) * D + cg * CPT, w);
+    load_codes<CPT>(kc + (int64_t)h * g.tiles * kTile * D + k_code_offset(slot, (cg * CPT) & ~15, D) +
+                        ((cg * CPT) & 15), w);
     float x[CPT];
     dequant_rotate<CPT>(w, k_scale[(int64_t)h * g.slots + slot], tab, cg * (CPT / 2), x);
 #pragma unroll
@@ -90,7 +91,8 @@ __global__ __launch_bounds__(kThreads) void rotate_requantize(
 
   const int slot = chunk * kChunk + (threadIdx.x >> 3), cg = threadIdx.x & 7;
   if (!slot_valid(slot, g.head, g.filled, g.slots)) return;
-  uint8_t* p = kc + ((int64_t)h * g.tiles * kTile + slot) * D + cg * CPT;
+  uint8_t* p = kc + (int64_t)h * g.tiles * kTile * D + k_code_offset(slot, (cg * CPT) & ~15, D) +
+               ((cg * CPT) & 15);
   uint32_t w[CPT / 4];
   load_codes<CPT>(p, w);
   float* sp = k_scale + (int64_t)h * g.slots + slot;

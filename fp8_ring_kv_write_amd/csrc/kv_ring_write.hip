@@ -141,7 +141,9 @@ __global__ __launch_bounds__(kThreads) void write_quantize(
 #pragma unroll
     for (int j = 0; j < CPT / 4; ++j)
       w[j] = e4m3x4(x[4 * j] * ik, x[4 * j + 1] * ik, x[4 * j + 2] * ik, x[4 * j + 3] * ik);
-    uint8_t* dst = kc + ((int64_t)h * g.tiles * kTile + slot) * D + cg * CPT;
+    // channels cg*CPT .. +CPT-1: one 16-byte unit (head_dim 128) or half of one (64)
+    uint8_t* dst = kc + (int64_t)h * g.tiles * kTile * D + k_code_offset(slot, (cg * CPT) & ~15, D) +
+                   ((cg * CPT) & 15);
     if constexpr (CPT == 16) {
       *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
     } else {
@@ -161,31 +163,30 @@ __global__ __launch_bounds__(kThreads) void write_quantize(
   }
   __syncthreads();
 
-  // V: transposed tile rows.  Work item = (channel d, group of 4 consecutive slots q); the
-  // chunk's 32 slots are 32 consecutive bytes of row d.
-  const int64_t tile = (int64_t)chunk * kChunk / kTile;
-  const int u0 = (chunk * kChunk) % kTile;
-  for (int item = threadIdx.x; item < D * (kChunk / 4); item += kThreads) {
-    const int d = item >> 3, q = item & 7;
-    uint8_t* row = vc + (((int64_t)h * g.tiles + tile) * D + d) * kTile + u0 + 4 * q;
-    uint32_t word = 0;
+  // V: transposed.  Work item = (channel d, half r of the chunk): the chunk's slots 16r .. 16r+15
+  // of channel d form one 16-byte unit of the tile.
+  for (int item = threadIdx.x; item < D * 2; item += kThreads) {
+    const int d = item >> 1, r = item & 1;
+    const int s0 = chunk * kChunk + 16 * r;
+    uint8_t* unit = vc + (int64_t)h * g.tiles * kTile * D + v_code_offset(s0, d, D);
+    uint32_t word[4] = {0, 0, 0, 0};
     int nmine = 0;
-    bool m4[4];
+    bool mine16[16];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int s = chunk * kChunk + 4 * q + r;
+    for (int kk = 0; kk < 16; ++kk) {
+      const int s = s0 + kk;
       int ii = s - g.start;
       ii = ii < 0 ? ii + g.slots : ii;
-      m4[r] = s < g.slots && ii < g.n;
-      nmine += m4[r];
-      word |= uint32_t(vlds[4 * q + r][d]) << (8 * r);
+      mine16[kk] = s < g.slots && ii < g.n;
+      nmine += mine16[kk];
+      word[kk >> 2] |= uint32_t(vlds[16 * r + kk][d]) << (8 * (kk & 3));
     }
-    if (nmine == 4) {
-      *reinterpret_cast<uint32_t*>(row) = word;
-    } else if (nmine > 0) {
+    if (nmine == 16) {
+      *reinterpret_cast<uint4*>(unit) = make_uint4(word[0], word[1], word[2], word[3]);
+    } else if (nmine > 0) {   // the write's first or last chunk: only its own slots
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (m4[r]) row[r] = uint8_t(word >> (8 * r));
+      for (int kk = 0; kk < 16; ++kk)
+        if (mine16[kk]) unit[kk] = uint8_t(word[kk >> 2] >> (8 * (kk & 3)));
     }
   }
 }

@@ -48,6 +48,16 @@ int64_t kv_ring_codes_bytes(int32_t heads, int32_t slots, int32_t head_dim) {
   return (int64_t)heads * kvring::tile_count(slots) * kvring::kTile * head_dim;
 }
 
+int64_t kv_ring_k_offset(int64_t slot, int32_t channel, int32_t head_dim) {
+  if (slot < 0 || (head_dim != 64 && head_dim != 128) || channel < 0 || channel >= head_dim) return -1;
+  return kvring::k_code_offset(slot, channel & ~15, head_dim) + (channel & 15);
+}
+
+int64_t kv_ring_v_offset(int64_t slot, int32_t channel, int32_t head_dim) {
+  if (slot < 0 || (head_dim != 64 && head_dim != 128) || channel < 0 || channel >= head_dim) return -1;
+  return kvring::v_code_offset(slot & ~int64_t(15), channel, head_dim) + (slot & 15);
+}
+
 
 int kv_ring_rope_table(float* host_out, int64_t n_pos, int32_t head_dim, double base) {
   if (!host_out) return KV_RING_ERR_NULL;

@@ -1,12 +1,17 @@
 // Shared device helpers for the FP8 ring KV-cache kernels (gfx950).
 //
-// Cache layout in HBM (per ring = one layer, one GPU's share of heads):
-//   K codes  [heads][tiles*128][head_dim]   row-major, one 128-slot tile after another
-//   V codes  [heads][tiles][head_dim][128]  each 128-slot tile stored transposed
-//                                           (channel-major, slots in order)
-//   scales   [heads][slots] float32         dequantisation scale of the write that filled
-//                                           each slot (k_scale, v_scale)
-// tiles = ceil(slots / 128); slots past `slots` in the last tile are never valid.
+// Cache layout in HBM (per ring = one layer, one GPU's share of heads), tiles of 128 slots:
+//   K codes  [heads][tiles][128 * head_dim]  each tile a sequence of 16-byte units in the order
+//                                            the QK matrix-core product consumes them
+//                                            (k_code_offset)
+//   V codes  [heads][tiles][head_dim * 128]  each tile transposed (channel-major), 16-slot
+//                                            pieces in the order the PV product consumes them
+//                                            (v_code_offset)
+//   scales   [heads][slots] float32          dequantisation scale of the write that filled
+//                                            each slot (k_scale, v_scale)
+// tiles = ceil(slots / 128); slots past `slots` in the last tile are never valid.  With tiles in
+// consumption order, a tile moves to LDS as one linear copy and every operand read of the
+// attention kernel is one contiguous 1 KB wavefront read (LDS reads at full rate).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -26,6 +31,26 @@ typedef short v2s __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
 __host__ __device__ inline int64_t tile_count(int32_t slots) { return (slots + kTile - 1) / kTile; }
+
+// Byte offset, within one head's K codes, of channels c .. c+15 (c a multiple of 16) of slot s.
+// Unit ((bb*2 + r) * (D/32) + g) * 16 + li of a tile holds channels 32g + 16r .. +15 of tile
+// slot 32*(li/4) + 4*bb + li%4: what lane (g, li) feeds to the QK product of score block bb as
+// the r-th half of its operand.
+__host__ __device__ inline int64_t k_code_offset(int64_t s, int c, int D) {
+  const int u = int(s % kTile);
+  const int li = 4 * (u >> 5) + (u & 3), bb = (u >> 2) & 7, q = c >> 4, g = q >> 1, r = q & 1;
+  return (s / kTile) * kTile * D + int64_t((((bb * 2 + r) * (D / 32) + g) * 16 + li) * 16);
+}
+
+// Byte offset, within one head's V codes, of slots s .. s+15 (s a multiple of 16) of channel d.
+// Unit ((db*2 + r) * 4 + g) * 16 + li of a tile holds tile slots 32g + 16r .. +15 of channel
+// 16*db + li: what lane (g, li) feeds to the PV product of channel block db as the r-th half
+// of its operand.
+__host__ __device__ inline int64_t v_code_offset(int64_t s, int d, int D) {
+  const int u = int(s % kTile);
+  const int g = u >> 5, r = (u >> 4) & 1, db = d >> 4, li = d & 15;
+  return (s / kTile) * kTile * D + int64_t((((db * 2 + r) * 4 + g) * 16 + li) * 16);
+}
 
 // bfloat16 bit pattern -> float32 (exact).
 __device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }

@@ -46,7 +46,7 @@ namespace {
 constexpr int kWaves = 8;               // 2 wavefronts per SIMD
 constexpr int kThreads = 64 * kWaves;   // 512
 constexpr int kRowQ = 16 * kWaves;      // 128 queries per row, 16 per wavefront
-constexpr int kBufs = 4;                // LDS tile buffers: tiles k-1, k, k+1 in use, k+2 landing
+constexpr int kBufs = 3;                // LDS buffers per operand (see attn_stream's schedule)
 constexpr int kMaxGrid = 256;
 constexpr float kTau = 4.0f;            // lazy rescale threshold, log2 units
 constexpr float kLog2e = 1.4426950408889634f;
@@ -73,18 +73,20 @@ struct AttnArgs {
   float score_scale;           // softmax_scale * log2(e)
 };
 
+// LDS of a work-group.  Each array is its own LDS object, so that the compiler can tell reads of
+// the factor arrays from the asynchronous tile copies landing in the tile and scale buffers.
 template <int D>
 struct Smem {
-  uint8_t k[kBufs][kTile * D];
-  uint8_t v[kBufs][D * kTile];
-  float ks[kBufs][kTile];
-  float vs[kBufs][kTile];
-  float ck[kBufs][kTile];   // per slot: c0 * k_scale (valid) or 0
-  float nb[kBufs][kTile];   // per slot: log2(v_scale) (valid) or -inf
-  float iv[kBufs][kTile];   // per slot: 1 / v_scale (valid) or 0
-  int eg[kBufs][4];         // exponent of the largest valid v_scale per 32 slots (-128: none)
-  int uni[kBufs][2];        // per 64 slots: all valid, one K scale and one V scale (1) or not
-  float red[kWaves];
+  uint8_t (&k)[kBufs][kTile * D];   // K tile j of a segment in k[j % 3] (with ks, vs, factors)
+  uint8_t (&v)[kBufs][D * kTile];   // transposed V tile j in v[j % 3]
+  float (&ks)[kBufs][kTile];
+  float (&vs)[kBufs][kTile];
+  float (&ck)[kBufs][kTile];   // per slot: c0 * k_scale (valid) or 0
+  float (&nb)[kBufs][kTile];   // per slot: log2(v_scale) (valid) or -inf
+  float (&iv)[kBufs][kTile];   // per slot: 1 / v_scale (valid) or 0
+  int (&eg)[kBufs][4];         // exponent of the largest valid v_scale per 32 slots (-128: none)
+  int (&uni)[kBufs][2];        // per 64 slots: all valid, one K scale and one V scale (1) or not
+  float (&red)[kWaves];
 };
 
 __device__ inline v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c, int scale_b) {
@@ -127,75 +129,93 @@ __device__ inline TileValid tile_valid(int64_t t, int head, int filled, int slot
   return v;
 }
 
-// K tile rows in LDS: row u's 16-byte chunk c sits at position c ^ k_swz(u).  The QK product
-// reads, for score block bb, the rows 32*(l>>2) + 4*bb + (l&3) in lanes l = 0..15 (see
-// k_row); the swizzle spreads those 16 rows over all LDS banks.
-template <int D>
-__device__ inline int k_swz(int u) {
-  if constexpr (D == 128) return ((u & 3) | (((u >> 5) & 1) << 2)) ^ ((u >> 6) & 1);
-  else return (u >> 5) & 3;
-}
+// The QK product of score block bb takes, in lane li (0..15), tile slot 32*(li/4) + 4bb + li%4
+// (the K tile layout stores them in that order).  Output row 4g+r of the block is then slot
+// 32g + 4bb + r: lane group g ends up holding slots 32g .. 32g+31 of its query across the 8
+// blocks, in order -- the B-operand layout of the PV product.
 
-// Tile row (slot) that lane li (0..15) feeds into the QK product of score block bb.  Output
-// row 4g+r of that block is then slot 32g + 4bb + r: lane group g ends up holding slots
-// 32g .. 32g+31 of its query across the 8 blocks -- in order, which is the B-operand layout
-// of the PV product over a tile whose V rows are stored in slot order.
-__device__ inline int k_row(int bb, int li) { return 32 * (li >> 2) + 4 * bb + (li & 3); }
-
-// Per-lane byte offsets of a wavefront's share of one tile copy: chunk c = (j*8 + w)*64 + lane
-// of the K tile (row c / NCH, LDS position c % NCH, holding the row's chunk p ^ k_swz(row)) and
-// of the transposed V tile (row c / 8, LDS position c % 8, holding chunk p ^ (row % 8)); and the
-// slot of the scale row a lane of wavefronts 0..3 copies.  Loop-invariant, computed once.
+// Per-lane byte offsets of a wavefront's share of one tile copy (tiles are stored in the order
+// the products consume them, so both K and V copies are linear: unit (j*8 + w)*64 + lane), and
+// the slot of the scale a lane copies (lanes 0..31; wavefronts 0-3: K scales, 4-7: V scales).
 template <int D>
 struct CopyOffs {
-  uint32_t k[(kTile * D / 16) / kThreads], v[(kTile * D / 16) / kThreads];
+  static constexpr int kLoads = (kTile * D / 16) / kThreads;   // 16-byte copies per lane per tile
   int su;
 };
 
 template <int D>
 __device__ inline CopyOffs<D> copy_offsets(int w, int lane) {
-  constexpr int NCH = D / 16;
   CopyOffs<D> o;
-#pragma unroll
-  for (int j = 0; j < (kTile * NCH) / kThreads; ++j) {
-    const unsigned c = unsigned((j * kWaves + w) * 64 + lane);
-    const unsigned u = c / NCH;
-    o.k[j] = u * D + (((c % NCH) ^ unsigned(k_swz<D>(int(u)))) << 4);
-    o.v[j] = (c >> 3) * kTile + (((c & 7u) ^ ((c >> 3) & 7u)) << 4);
-  }
-  o.su = (w & 1) * 64 + lane;
+  o.su = (w & 3) * 32 + lane;
   return o;
 }
 
-// Issue the asynchronous copies of ring tile t (K, transposed V, both scale rows) into buffer b.
+// Asynchronous global -> LDS copy of 16 bytes per lane (4 for copy4): global address base + voff
+// (base uniform), LDS destination lds + 16 * lane (4 * lane).  Written as inline assembly so that
+// the compiler does not track these copies: it would otherwise wait for all of them before any
+// LDS access that might overlap, which would cut the copy pipeline to one step.  Completion is
+// tracked with wait_vm; the LDS address goes through m0, as the instruction requires.
+__device__ inline void copy16(const void* base, uint32_t voff, const void* lds) {
+  const uint32_t la = uint32_t(uintptr_t((lds_ptr)lds));
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(la) : "memory");
+}
+__device__ inline void copy4(const void* base, uint32_t voff, const void* lds) {
+  const uint32_t la = uint32_t(uintptr_t((lds_ptr)lds));
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "{m0}"(la) : "memory");
+}
+
+// Asynchronous copies of ring tile t into LDS: K tile and both scale rows into K buffer b
+// (kLoads + 1 copies per lane), or the transposed V tile into V buffer b (kLoads per lane).
 template <int D>
-__device__ inline void issue_tile(const AttnArgs& a, Smem<D>& sm, const CopyOffs<D>& co, int b,
-                                  int64_t t, int h, int w) {
-  constexpr int NCH = D / 16;
+__device__ inline void issue_k(const AttnArgs& a, Smem<D>& sm, const CopyOffs<D>& co, int b,
+                               int64_t t, int h, int w, int lane) {
   const uint8_t* kbase = a.kc + ((int64_t)h * a.tiles + t) * (kTile * D);   // uniform
-  const uint8_t* vbase = a.vc + ((int64_t)h * a.tiles + t) * (D * kTile);   // uniform
 #pragma unroll
-  for (int j = 0; j < (kTile * NCH) / kThreads; ++j) {
-    const int c0 = (j * kWaves + w) * 64;      // first chunk of this wavefront's copy
-    __builtin_amdgcn_global_load_lds(kbase + co.k[j], (lds_ptr)&sm.k[b][c0 * 16], 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vbase + co.v[j], (lds_ptr)&sm.v[b][c0 * 16], 16, 0, 0);
-  }
-  if (w < 4) {   // wavefronts 0,1: K scales; 2,3: V scales (64 slots each)
-    const int slot = min(int(t) * kTile + co.su, a.slots - 1);   // in bounds; padding masked later
-    const float* src = ((w < 2) ? a.k_scale : a.v_scale) + (int64_t)h * a.slots + slot;
-    float* dst = (w < 2) ? &sm.ks[b][(w & 1) * 64] : &sm.vs[b][(w & 1) * 64];
-    __builtin_amdgcn_global_load_lds(src, (lds_ptr)dst, 4, 0, 0);
+  for (int j = 0; j < CopyOffs<D>::kLoads; ++j)
+    copy16(kbase, uint32_t(((j * kWaves + w) * 64 + lane) * 16), &sm.k[b][(j * kWaves + w) * 1024]);
+  if (lane < 32) {
+    // slot index clamped in bounds; padding slots are masked by the tile's validity
+    const int slot = min(int(t) * kTile + co.su, a.slots - 1);
+    const float* srow = ((w < 4) ? a.k_scale : a.v_scale) + (int64_t)h * a.slots;   // uniform
+    float* dst = (w < 4) ? &sm.ks[b][(w & 3) * 32] : &sm.vs[b][(w & 3) * 32];
+    copy4(srow, uint32_t(slot) * 4u, dst);
   }
 }
 
-// Per-slot factors of the tile in buffer b, and zeroed K and V bytes for invalid slots (so that
-// whatever they hold -- NaN codes included -- never reaches a product).  Wavefronts 0 and 1 take
-// one slot per lane; the zeroing (tiles with invalid slots only) is shared by all and followed
-// by a barrier.  With vmax = f * 2^e (f in [0.5, 1)) the largest valid V scale of the tile, the
-// probabilities enter the PV product as P * v_scale * 2^-e <= P, and the product's B-operand
-// scale multiplies back by 2^e (one exponent per tile: the scale of the FP8 matrix product
-// applies per 32-element block of its contraction, and a block gathers 16-slot pieces of two
-// lane groups).
+template <int D>
+__device__ inline void issue_v(const AttnArgs& a, Smem<D>& sm, int b, int64_t t, int h, int w,
+                               int lane) {
+  const uint8_t* vbase = a.vc + ((int64_t)h * a.tiles + t) * (D * kTile);   // uniform
+#pragma unroll
+  for (int j = 0; j < CopyOffs<D>::kLoads; ++j)
+    copy16(vbase, uint32_t(((j * kWaves + w) * 64 + lane) * 16), &sm.v[b][(j * kWaves + w) * 1024]);
+}
+
+// Wait until at most n of this thread's vector-memory operations are outstanding (they complete
+// in issue order).  n is one of the per-step copy counts (0 .. 2*kLoads + 1).
+__device__ inline void wait_vm(int n) {
+  switch (n) {   // s_waitcnt immediate: vmcnt in bits 3:0, expcnt and lgkmcnt left at their maximum
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+  }
+}
+
+// Work-group barrier for LDS traffic only: this thread's LDS reads and writes are complete, and
+// the compiler keeps memory accesses on their side of it.  Unlike __syncthreads it does not wait
+// for the asynchronous tile copies in flight (their completion is tracked with wait_vm).
+__device__ inline void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Per-slot factors of the tile in K buffer b, and zeroed K bytes for its invalid slots (so that
+// whatever they hold -- NaN codes included -- never reaches a product).  Wavefronts 0 and 1
+// take one slot per lane; the zeroing is shared by all.  With vmax = f * 2^e (f in [0.5, 1)) the
+// largest valid V scale of the tile, the probabilities enter the PV product as
+// P * v_scale * 2^-e <= P, and the product's B-operand scale multiplies back by 2^e (one
+// exponent per tile: the scale of the FP8 matrix product applies per 32-element block of its
+// contraction, and a block gathers 16-slot pieces of two lane groups).
 template <int D>
 __device__ inline void prep_tile(Smem<D>& sm, int b, const TileValid& tvd, float c0, int tid) {
   constexpr int NCH = D / 16;
@@ -221,55 +241,55 @@ __device__ inline void prep_tile(Smem<D>& sm, int b, const TileValid& tvd, float
   }
   if (tvd.count() < kTile) {
     uint8_t* kw = sm.k[b];
-    for (int c = tid; c < kTile * NCH; c += kThreads)   // whole 16-byte chunks of K rows
-      if (!tvd.has(c / NCH)) *reinterpret_cast<uint4*>(kw + c * 16) = make_uint4(0, 0, 0, 0);
-    uint8_t* vw = sm.v[b];
-    for (int c = tid; c < D * 8; c += kThreads) {        // 16-byte chunks of V rows
-      const int u0 = ((c & 7) ^ ((c >> 3) & 7)) * 16;    // first slot of the chunk
-      uint4 x = *reinterpret_cast<uint4*>(vw + c * 16);
-      uint32_t xw[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-      for (int kk = 0; kk < 16; ++kk)
-        if (!tvd.has(u0 + kk)) xw[kk >> 2] &= ~(0xFFu << (8 * (kk & 3)));
-      *reinterpret_cast<uint4*>(vw + c * 16) = make_uint4(xw[0], xw[1], xw[2], xw[3]);
+    for (int c = tid; c < kTile * NCH; c += kThreads) {   // 16-byte units of the K tile
+      const int li = c & 15, bb = c / (16 * (D / 32)) / 2;
+      if (!tvd.has(32 * (li >> 2) + 4 * bb + (li & 3))) *reinterpret_cast<uint4*>(kw + c * 16) = make_uint4(0, 0, 0, 0);
     }
-    __syncthreads();
   }
 }
 
-// Per-lane LDS byte offsets (within one buffer) of the two 16-byte halves of a lane's A
-// operand for score block 0 (K) and channel block 0 (V).  Block bb / db adds bb*4*D bytes
-// (K: rows k_row(bb, li) = k_row(0, li) + 4bb, whose swizzle does not depend on bb) and
-// db*16*128 bytes (V rows 16db + li, swizzled by li % 8).
+// Zeroed V bytes of the invalid slots of the tile in V buffer b (tiles with invalid slots only).
+template <int D>
+__device__ inline void zero_invalid_v(Smem<D>& sm, int b, const TileValid& tvd, int tid) {
+  uint8_t* vw = sm.v[b];
+  for (int c = tid; c < D * 8; c += kThreads) {        // 16-byte units of the V tile
+    const int u0 = 32 * ((c >> 4) & 3) + 16 * ((c >> 6) & 1);   // first slot of the unit
+    uint4 x = *reinterpret_cast<uint4*>(vw + c * 16);
+    uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk)
+      if (!tvd.has(u0 + kk)) xw[kk >> 2] &= ~(0xFFu << (8 * (kk & 3)));
+    *reinterpret_cast<uint4*>(vw + c * 16) = make_uint4(xw[0], xw[1], xw[2], xw[3]);
+  }
+}
+
+// Per-lane LDS byte offsets (within one buffer) of a lane's A operands: half r of score block bb
+// is K unit (bb*2 + r)*(D/32)*16 + lane, half r of channel block db is V unit (db*2 + r)*64 +
+// lane: every operand read is one contiguous 1 KB wavefront read.
 struct LaneOffs {
-  int k0, k1, v0, v1;
+  int k, v;
 };
 
 template <int D>
 __device__ inline LaneOffs lane_offsets(int lane) {
-  const int g = lane >> 4, li = lane & 15;
-  const int u = k_row(0, li);
-  const int sw = k_swz<D>(u);
   LaneOffs o;
-  o.k0 = u * D + (((2 * g) ^ sw) << 4);
-  o.k1 = u * D + (((2 * g + 1) ^ sw) << 4);
-  o.v0 = li * kTile + (((2 * g) ^ (li & 7)) << 4);
-  o.v1 = li * kTile + (((2 * g + 1) ^ (li & 7)) << 4);
+  o.k = (D == 128 ? lane : (lane & 31)) * 16;   // head_dim 64: lanes 32..63 carry zeros
+  o.v = lane * 16;
   return o;
 }
 
 // A operand of score block bb (16 K rows) / of channel block db (16 transposed V rows).
 template <int D>
 __device__ inline v8i k_operand(const uint8_t* kt, const LaneOffs& o, int bb, int g) {
-  if (D != 128 && g >= 2) return v8i{0, 0, 0, 0, 0, 0, 0, 0};   // head_dim 64: upper half zero
-  const uint4 x0 = *reinterpret_cast<const uint4*>(kt + o.k0 + bb * 4 * D);
-  const uint4 x1 = *reinterpret_cast<const uint4*>(kt + o.k1 + bb * 4 * D);
+  const uint4 x0 = *reinterpret_cast<const uint4*>(kt + o.k + (bb * 2) * (D / 32) * 256);
+  const uint4 x1 = *reinterpret_cast<const uint4*>(kt + o.k + (bb * 2 + 1) * (D / 32) * 256);
+  if (D != 128 && g >= 2) return v8i{0, 0, 0, 0, 0, 0, 0, 0};
   return v8i{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
 }
 
 __device__ inline v8i v_operand(const uint8_t* vt, const LaneOffs& o, int db) {
-  const uint4 x0 = *reinterpret_cast<const uint4*>(vt + o.v0 + db * 16 * kTile);
-  const uint4 x1 = *reinterpret_cast<const uint4*>(vt + o.v1 + db * 16 * kTile);
+  const uint4 x0 = *reinterpret_cast<const uint4*>(vt + o.v + (db * 2) * 1024);
+  const uint4 x1 = *reinterpret_cast<const uint4*>(vt + o.v + (db * 2 + 1) * 1024);
   return v8i{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
 }
 
@@ -412,7 +432,17 @@ __device__ __forceinline__ void pipeline_step(const Smem<D>& sm, int bk, int bp,
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
   constexpr int NDB = D / 16;
-  __shared__ __align__(16) Smem<D> sm;
+  __shared__ __align__(16) uint8_t s_k[kBufs][kTile * D];
+  __shared__ __align__(16) uint8_t s_v[kBufs][D * kTile];
+  __shared__ __align__(16) float s_ks[kBufs][kTile];
+  __shared__ __align__(16) float s_vs[kBufs][kTile];
+  __shared__ __align__(16) float s_ck[kBufs][kTile];
+  __shared__ __align__(16) float s_nb[kBufs][kTile];
+  __shared__ __align__(16) float s_iv[kBufs][kTile];
+  __shared__ __align__(16) int s_eg[kBufs][4];
+  __shared__ __align__(16) int s_uni[kBufs][2];
+  __shared__ float s_red[kWaves];
+  Smem<D> sm{s_k, s_v, s_ks, s_vs, s_ck, s_nb, s_iv, s_eg, s_uni, s_red};
 
   const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);   // wavefront (uniform)
 
@@ -441,8 +471,14 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
     const int nseg = owner((int64_t)row * a.tv + a.tv - 1) - owner((int64_t)row * a.tv) + 1;
     auto phys = [&](int k) -> int64_t { return k < a.n1 ? a.first1 + k : a.first2 + (k - a.n1); };
 
-    // first tile's copies go out before the query preparation
-    issue_tile<D>(a, sm, co, 0, phys(k0), head, w);
+    // Copy schedule (j = tile index within the segment; step j forms tile j's probabilities,
+    // runs the PV product of tile j-1 and the QK product of tile j+1):
+    //   K tile j (+ scales) -> K buffer j % 3, issued in step j-3, needed from step j-1 on;
+    //   V tile j            -> V buffer j % 3, issued in step j-1, needed in step j+1.
+    // Each copy has two steps to land; a step waits only for the copies issued two steps back.
+    issue_k<D>(a, sm, co, 0, phys(k0), head, w, lane);
+    if (nt > 1) issue_k<D>(a, sm, co, 1, phys(k0 + 1), head, w, lane);
+    const int nk = CopyOffs<D>::kLoads + 1, nv = CopyOffs<D>::kLoads;
 
     // ---- query scale of the head, then this wavefront's quantised queries
     float qa = 0.0f;
@@ -450,12 +486,12 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
       qa = __builtin_fmaxf(qa, a.q_partial[(int64_t)head * a.n_qgroups + j]);
     for (int off = 32; off > 0; off >>= 1) qa = __builtin_fmaxf(qa, __shfl_xor(qa, off, 64));
     if (lane == 0) sm.red[w] = qa;
-    // the PV of the first step reads "tile k-1" from the last buffer: zeros
+    // the PV of the first step reads "tile -1" from the last V buffer: zeros
     {
       uint4* vz = reinterpret_cast<uint4*>(sm.v[kBufs - 1]);
       for (int c = tid; c < D * kTile / 16; c += kThreads) vz[c] = make_uint4(0, 0, 0, 0);
     }
-    __syncthreads();
+    lds_sync();
     qa = sm.red[0];
 #pragma unroll
     for (int j = 1; j < kWaves; ++j) qa = __builtin_fmaxf(qa, sm.red[j]);
@@ -505,28 +541,54 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
     pb = pa;
     v4f sc[8];
 
-    // ---- prologue: tile k0 resident and prepared, its raw scores in sa
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (nt > 1) issue_tile<D>(a, sm, co, 1, phys(k0 + 1), head, w);
-    prep_tile(sm, 0, tile_valid(phys(k0), a.ring_head, a.filled, a.slots), c0, tid);
-    __syncthreads();
+    // ---- prologue: K tile 0 resident and prepared, its raw scores in sc
+    wait_vm(nt > 1 ? nk : 0);
+    lds_sync();
+    {
+      const TileValid tvd = tile_valid(phys(k0), a.ring_head, a.filled, a.slots);
+      prep_tile(sm, 0, tvd, c0, tid);
+    }
+    lds_sync();
 #pragma unroll
     for (int bb = 0; bb < 8; ++bb)
       sc[bb] = mfma_fp8(k_operand<D>(sm.k[0], lo, bb, g), qop, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 127);
+    // copies of step -1: K tile 2, V tile 0
+    int n_prev = 0;
+    if (nt > 2) { issue_k<D>(a, sm, co, 2, phys(k0 + 2), head, w, lane); n_prev += nk; }
+    issue_v<D>(a, sm, 0, phys(k0), head, w, lane);
+    n_prev += nv;
 
     // ---- pipeline over the segment's tiles; two steps per trip so that the two probability
     // tiles swap roles without register copies
     auto step = [&](int j, const PTile& pprev, PTile& pcur) {
-      const int bk = j & (kBufs - 1), bn = (j + 1) & (kBufs - 1), bp = (j + kBufs - 1) & (kBufs - 1);
-      __builtin_amdgcn_s_waitcnt(0);   // this thread's copies of tile k+1 have landed
-      __syncthreads();                 // everyone's have; buffer of tile k+2 is free
-      if (j + 2 < nt) issue_tile<D>(a, sm, co, (j + 2) & (kBufs - 1), phys(k0 + j + 2), head, w);
-      if (j + 1 < nt) prep_tile(sm, bn, tile_valid(phys(k0 + j + 1), a.ring_head, a.filled, a.slots), c0, tid);
+      const int bk = j % kBufs, bn = (j + 1) % kBufs, bp = (j + kBufs - 1) % kBufs;
+      wait_vm(n_prev);     // this thread's copies issued two steps back have landed:
+      lds_sync();     // K tile j+1 and V tile j-1 are resident, buffers of j+3 / j+1 free
+      n_prev = 0;
+      if (j + 3 < nt) { issue_k<D>(a, sm, co, (j + 3) % kBufs, phys(k0 + j + 3), head, w, lane); n_prev += nk; }
+      if (j + 1 < nt) { issue_v<D>(a, sm, bn, phys(k0 + j + 1), head, w, lane); n_prev += nv; }
+      bool fix = false;    // LDS bytes changed below: barrier before the products read them
+      if (j >= 1) {
+        const TileValid tvp = tile_valid(phys(k0 + j - 1), a.ring_head, a.filled, a.slots);
+        if (tvp.count() < kTile) { zero_invalid_v(sm, bp, tvp, tid); fix = true; }
+      }
+      if (j + 1 < nt) {
+        const TileValid tvn = tile_valid(phys(k0 + j + 1), a.ring_head, a.filled, a.slots);
+        prep_tile(sm, bn, tvn, c0, tid);
+        fix = fix || tvn.count() < kTile;
+      }
+      if (fix) lds_sync();
       pipeline_step<D>(sm, bk, bp, bn, g, lo, qop, sc, pprev, pcur, st);
     };
-    auto final_pv = [&](int b, const PTile& pt) {
-      const uint8_t* vt = sm.v[b];
+    auto final_pv = [&](int jl, const PTile& pt) {   // PV of the last tile jl
+      wait_vm(0);
+      lds_sync();
+      const TileValid tvl = tile_valid(phys(k0 + jl), a.ring_head, a.filled, a.slots);
+      if (tvl.count() < kTile) {
+        zero_invalid_v(sm, jl % kBufs, tvl, tid);
+        lds_sync();
+      }
+      const uint8_t* vt = sm.v[jl % kBufs];
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const v8i vo = v_operand(vt, lo, db);
@@ -537,12 +599,12 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
     for (int j = 0;;) {
       step(j, pa, pb);
       if (++j == nt) {
-        final_pv((j - 1) & (kBufs - 1), pb);
+        final_pv(j - 1, pb);
         break;
       }
       step(j, pb, pa);
       if (++j == nt) {
-        final_pv((j - 1) & (kBufs - 1), pa);
+        final_pv(j - 1, pa);
         break;
       }
     }
@@ -577,7 +639,7 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
           a.lse[(int64_t)head * a.nq + i] = lt > 0.0f ? (st.m + __log2f(lt)) * kLn2 : -INFINITY;
       }
     }
-    __syncthreads();   // LDS buffers are reused by the next segment
+    lds_sync();   // LDS buffers are reused by the next segment
     ub += nt;
   }
 }

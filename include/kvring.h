@@ -60,16 +60,20 @@ enum { KV_RING_OP_WRITE = 1, KV_RING_OP_DELTA_ROTATE = 2, KV_RING_OP_ATTENTION =
 
 /*
  * One ring (one layer, one GPU's share of heads).  All four buffers are device memory of the
- * caller, 16-byte aligned.  With T = ceil(slots / 128) tiles:
- *   k        K codes, T*128*head_dim bytes per head, [heads][T*128][head_dim]: slot s of head h
- *            at byte (h*T*128 + s)*head_dim;
- *   v        V codes, the same size, each 128-slot tile stored transposed (channel-major):
- *            [heads][T][head_dim][128]; channel d of slot s of head h is at byte
- *            ((h*T + s/128)*head_dim + d)*128 + s % 128;
+ * caller, 16-byte aligned.  With T = ceil(slots / 128) tiles of 128 slots, the code buffers hold
+ * per head T tiles of 128*head_dim bytes each, every tile a sequence of 16-byte units in the
+ * order the attention's matrix-core products consume them:
+ *   k        K codes.  Unit ((bb*2 + r)*(head_dim/32) + g)*16 + li of tile t holds channels
+ *            32g + 16r .. +15 (in order) of slot 128t + 32*(li/4) + 4*bb + li%4
+ *            (bb 0..7, r 0..1, g 0..head_dim/32-1, li 0..15);
+ *   v        V codes, each tile transposed.  Unit ((db*2 + r)*4 + g)*16 + li of tile t holds
+ *            channel 16*db + li of slots 128t + 32g + 16r .. +15 (in order)
+ *            (db 0..head_dim/16-1, r 0..1, g 0..3, li 0..15);
  *   k_scale  float32 [heads][slots], the dequantisation scale of the write that filled a slot;
  *   v_scale  float32 [heads][slots].
+ * Byte b of unit n of tile t of head h is at byte ((h*T + t)*128*head_dim + 16n + b).
  * Limits: 1 <= heads <= 65535, 1 <= slots <= 1048576, head_dim in {64, 128}.
- * Bytes of the last tile past `slots` are padding and never read as data.
+ * Bytes of the last tile for slots past `slots` are padding and never read as data.
  */
 typedef struct kv_ring_desc {
   uint8_t *k;
@@ -83,6 +87,12 @@ typedef struct kv_ring_desc {
 
 /* Bytes of one of the two code buffers (k or v): heads * ceil(slots/128) * 128 * head_dim. */
 int64_t kv_ring_codes_bytes(int32_t heads, int32_t slots, int32_t head_dim);
+
+/* Byte offset, within one head's K codes (kv_ring_k_offset) or V codes (kv_ring_v_offset), of
+ * channel `channel` of slot `slot`, per the layout above.  Host only; -1 for a negative slot, a
+ * channel outside 0..head_dim-1 or an unsupported head_dim. */
+int64_t kv_ring_k_offset(int64_t slot, int32_t channel, int32_t head_dim);
+int64_t kv_ring_v_offset(int64_t slot, int32_t channel, int32_t head_dim);
 
 /*
  * Fill a host float32 table [n_pos][head_dim/2][2] with cos and sin of p * theta_i for

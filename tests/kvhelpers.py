@@ -11,12 +11,38 @@ import numpy as np
 TILE = 128
 
 
+def k_unit_index(u: np.ndarray, q: np.ndarray, head_dim: int) -> np.ndarray:
+    """16-byte unit (within a tile) holding channels 16q .. 16q+15 of tile slot u (kvring.h)."""
+    li = 4 * (u >> 5) + (u & 3)
+    bb = (u >> 2) & 7
+    g, r = q >> 1, q & 1
+    return ((bb * 2 + r) * (head_dim // 32) + g) * 16 + li
+
+
+def v_unit_index(d: np.ndarray, u16: np.ndarray) -> np.ndarray:
+    """16-byte unit (within a tile) holding tile slots 16*u16 .. +15 of channel d (kvring.h)."""
+    g, r = u16 >> 1, u16 & 1
+    return ((d // 16 * 2 + r) * 4 + g) * 16 + d % 16
+
+
+def code_byte_maps(head_dim: int):
+    """Byte offsets within a tile: kmap[u, c] of K channel c of tile slot u, vmap[u, c] of V."""
+    D = head_dim
+    u = np.arange(TILE)[:, None]
+    c = np.arange(D)[None, :]
+    kmap = k_unit_index(u, c // 16, D) * 16 + c % 16
+    vmap = v_unit_index(c, u // 16) * 16 + u % 16
+    return kmap, vmap
+
+
 def logical_codes(k_buf: np.ndarray, v_buf: np.ndarray, heads: int, slots: int, head_dim: int):
     """Library code buffers (flat uint8) -> K, V codes [heads, slots, head_dim]."""
     tiles = (slots + TILE - 1) // TILE
-    k = k_buf.reshape(heads, tiles * TILE, head_dim)[:, :slots, :]
-    v4 = v_buf.reshape(heads, tiles, head_dim, TILE)
-    v = v4.transpose(0, 1, 3, 2).reshape(heads, tiles * TILE, head_dim)[:, :slots, :]
+    kmap, vmap = code_byte_maps(head_dim)
+    kt = k_buf.reshape(heads, tiles, TILE * head_dim)
+    vt = v_buf.reshape(heads, tiles, TILE * head_dim)
+    k = kt[:, :, kmap].reshape(heads, tiles * TILE, head_dim)[:, :slots, :]
+    v = vt[:, :, vmap].reshape(heads, tiles * TILE, head_dim)[:, :slots, :]
     return np.ascontiguousarray(k), np.ascontiguousarray(v)
 
 
@@ -33,11 +59,14 @@ def poison_free_slots_gpu(ring, valid: np.ndarray):
     H, S, D = ring.heads, ring.slots, ring.head_dim
     tiles = (S + TILE - 1) // TILE
     free = np.setdiff1d(np.arange(tiles * TILE), valid)
-    kb = ring.k.view(H, tiles * TILE, D)
-    kb[:, torch.from_numpy(free).to(kb.device), :] = 0x7F
-    vb = ring.v.view(H, tiles, D, TILE)
-    for s in free.tolist():
-        vb[:, s // TILE, :, s % TILE] = 0xFF
+    kmap, vmap = code_byte_maps(D)
+    tile_bytes = TILE * D
+    kidx = ((free // TILE) * tile_bytes)[:, None] + kmap[free % TILE]
+    vidx = ((free // TILE) * tile_bytes)[:, None] + vmap[free % TILE]
+    kb = ring.k.view(H, tiles * tile_bytes)
+    vb = ring.v.view(H, tiles * tile_bytes)
+    kb[:, torch.from_numpy(kidx.reshape(-1)).to(kb.device)] = 0x7F
+    vb[:, torch.from_numpy(vidx.reshape(-1)).to(vb.device)] = 0xFF
     fs = free[free < S]
     nan = torch.tensor(float("nan"), device=ring.k_scale.device)
     ring.k_scale[:, torch.from_numpy(fs).to(kb.device)] = nan

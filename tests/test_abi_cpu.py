@@ -46,6 +46,24 @@ def test_rope_table_matches_oracle_bit_for_bit(kv):
         assert ours.tobytes() == ref.tobytes()
 
 
+def test_code_offsets_follow_the_documented_layout(kv):
+    """The library's layout functions against the numpy reading of the kvring.h formulas, and
+    each tile's offsets are a permutation of the tile's bytes."""
+    from kvhelpers import code_byte_maps
+    for d in (64, 128):
+        kmap, vmap = code_byte_maps(d)
+        for slot in (0, 1, 31, 32, 77, 127, 128, 300, 5787):
+            base = (slot // 128) * 128 * d
+            for c in range(0, d, 5):
+                assert kv.k_offset(slot, c, d) == base + kmap[slot % 128, c]
+                assert kv.v_offset(slot, c, d) == base + vmap[slot % 128, c]
+        ks = sorted(kv.k_offset(u, c, d) for u in range(128) for c in range(d))
+        vs = sorted(kv.v_offset(u, c, d) for u in range(128) for c in range(d))
+        assert ks == list(range(128 * d)) and vs == list(range(128 * d))
+    assert kv.k_offset(-1, 0, 128) == -1 and kv.k_offset(0, 128, 128) == -1
+    assert kv.v_offset(0, 0, 96) == -1 and kv.v_offset(0, -1, 64) == -1
+
+
 def test_sizes(kv):
     assert kv.codes_bytes(24, 5788, 128) == 24 * 46 * 128 * 128
     assert kv.codes_bytes(1, 64, 64) == 128 * 64
