@@ -155,13 +155,16 @@ __device__ inline CopyOffs<D> copy_offsets(int w, int lane) {
 // the compiler does not track these copies: it would otherwise wait for all of them before any
 // LDS access that might overlap, which would cut the copy pipeline to one step.  Completion is
 // tracked with wait_vm; the LDS address goes through m0, as the instruction requires.
+// The compiler inserts no hazard wait states around inline assembly, so the leading s_nop 4
+// provides them: 5 wait states cover an SGPR operand written just before by a vector
+// instruction (v_readlane restoring a spilled base address) and the m0 write.
 __device__ inline void copy16(const void* base, uint32_t voff, const void* lds) {
   const uint32_t la = uint32_t(uintptr_t((lds_ptr)lds));
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(la) : "memory");
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(la) : "memory");
 }
 __device__ inline void copy4(const void* base, uint32_t voff, const void* lds) {
   const uint32_t la = uint32_t(uintptr_t((lds_ptr)lds));
-  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "{m0}"(la) : "memory");
+  asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "{m0}"(la) : "memory");
 }
 
 // Asynchronous copies of ring tile t into LDS: K tile and both scale rows into K buffer b

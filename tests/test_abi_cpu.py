@@ -140,3 +140,27 @@ def test_product_path_has_no_oracle_import():
             if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
+
+
+def test_lds_copies_carry_hazard_wait_states(tmp_path):
+    """The attention kernel's asynchronous global->LDS copies are inline assembly, around which
+    the compiler inserts no hazard wait states: a base-address SGPR written by a vector
+    instruction right before (a spilled SGPR restored with v_readlane) needs 5 wait states
+    before the copy reads it.  Every copy in the generated gfx950 code must carry them."""
+    import shutil
+    import subprocess
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    src = os.path.join(ROOT, "fp8_ring_kv_write_amd", "csrc", "ring_attention.hip")
+    out = tmp_path / "ra.s"
+    subprocess.run([hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off",
+                    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                    "-mllvm", "-amdgpu-mfma-vgpr-form", "-S", "--cuda-device-only", src,
+                    "-o", str(out)], check=True, capture_output=True)
+    lines = [l.strip() for l in out.read_text().splitlines()]
+    copies = [i for i, l in enumerate(lines) if l.startswith("global_load_lds")]
+    assert copies, "no LDS copies found"
+    for i in copies:
+        prev = [l for l in lines[max(0, i - 3):i] if l and not l.startswith(";")]
+        assert prev and prev[-1] == "s_nop 4", lines[i - 3:i + 1]
