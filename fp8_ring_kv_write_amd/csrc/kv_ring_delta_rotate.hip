@@ -6,8 +6,10 @@
 // Keys are dequantised (decode * slot scale, float32), rotated by the delta table (float32,
 // every operation rounded), and requantised with one new per-head scale over all valid
 // slots.  Two passes over the K codes (the second mostly from L2 / infinity cache), no
-// atomics: pass 1 writes per-(head, chunk) absmax partials, pass 2 reduces them and rewrites
-// codes and scales.  V is untouched.
+// atomics: pass 1 writes per-(head, tile) absmax partials, pass 2 reduces them and rewrites
+// codes and scales.  A work-group takes one 128-slot tile of one head, each thread 4 (head_dim
+// 128) or 2 (64) 16-byte units of 16 channels with all of its loads in flight at once.  V is
+// untouched.
 
 #include "kvring_common.hpp"
 #include "kvring_internal.hpp"
@@ -41,76 +43,101 @@ __device__ inline void dequant_rotate(const uint32_t (&codes)[CPT / 4], float sc
   }
 }
 
-template <int CPT>
-__device__ inline void load_codes(const uint8_t* p, uint32_t (&w)[CPT / 4]) {
-  if constexpr (CPT == 16) {
-    uint4 v = *reinterpret_cast<const uint4*>(p);
-    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-  } else {
-    uint2 v = *reinterpret_cast<const uint2*>(p);
-    w[0] = v.x; w[1] = v.y;
+// Unit p (16 bytes) of a K tile -> tile slot u and channel chunk q (channels 16q .. 16q+15),
+// per the tile layout (k_code_offset).
+template <int D>
+__device__ inline void unit_slot(int p, int& u, int& q) {
+  constexpr int G = D / 32;
+  const int li = p & 15, rest = p >> 4, g = rest % G, rb = rest / G;
+  u = 32 * (li >> 2) + 4 * (rb >> 1) + (li & 3);
+  q = 2 * g + (rb & 1);
+}
+
+// Units handled by one thread: a work-group of kThreads takes one 128-slot tile of one head.
+template <int D>
+constexpr int kUnitsPerThread = (kTile * D / 16) / kThreads;
+
+// Loads of a thread's units: codes (16 bytes each) and the scale of each unit's slot, all
+// issued before any is used.
+template <int D>
+struct Units {
+  uint32_t w[kUnitsPerThread<D>][4];
+  float scale[kUnitsPerThread<D>];
+  int q[kUnitsPerThread<D>], slot[kUnitsPerThread<D>];
+  bool ok[kUnitsPerThread<D>];
+};
+
+template <int D>
+__device__ inline void load_units(const uint8_t* tile, const float* srow, int t, const RotGeom& g,
+                                  Units<D>& x) {
+#pragma unroll
+  for (int j = 0; j < kUnitsPerThread<D>; ++j) {
+    const int p = j * kThreads + int(threadIdx.x);
+    int u;
+    unit_slot<D>(p, u, x.q[j]);
+    x.slot[j] = t * kTile + u;
+    x.ok[j] = slot_valid(x.slot[j], g.head, g.filled, g.slots);
+    uint4 v = make_uint4(0, 0, 0, 0);
+    float sc = 0.0f;
+    if (x.ok[j]) {
+      v = *reinterpret_cast<const uint4*>(tile + p * 16);
+      sc = srow[x.slot[j]];
+    }
+    x.w[j][0] = v.x; x.w[j][1] = v.y; x.w[j][2] = v.z; x.w[j][3] = v.w;
+    x.scale[j] = sc;
   }
 }
 
-// grid = (chunks of 32 slots over the whole ring, heads)
+// grid = (tiles, heads): max |rotated key| over the valid slots of one tile of one head.
 template <int D>
 __global__ __launch_bounds__(kThreads) void rotate_absmax_partials(
     const uint8_t* __restrict__ kc, const float* __restrict__ k_scale, RotGeom g, DeltaTable tab,
     float* __restrict__ partial) {
-  constexpr int CPT = D / 8;
   __shared__ float red[4];
-  const int chunk = blockIdx.x, h = blockIdx.y;
-  const int slot = chunk * kChunk + (threadIdx.x >> 3), cg = threadIdx.x & 7;
+  const int t = blockIdx.x, h = blockIdx.y;
+  Units<D> x;
+  load_units<D>(kc + ((int64_t)h * g.tiles + t) * kTile * D, k_scale + (int64_t)h * g.slots, t, g, x);
   float m = 0.0f;
-  if (slot_valid(slot, g.head, g.filled, g.slots)) {
-    uint32_t w[CPT / 4];
-    load_codes<CPT>(kc + (int64_t)h * g.tiles * kTile * D + k_code_offset(slot, (cg * CPT) & ~15, D) +
-                        ((cg * CPT) & 15), w);
-    float x[CPT];
-    dequant_rotate<CPT>(w, k_scale[(int64_t)h * g.slots + slot], tab, cg * (CPT / 2), x);
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) m = __builtin_fmaxf(m, __builtin_fabsf(x[j]));
+  for (int j = 0; j < kUnitsPerThread<D>; ++j) {
+    if (!x.ok[j]) continue;
+    float v[16];
+    dequant_rotate<16>(x.w[j], x.scale[j], tab, 8 * x.q[j], v);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[e]));
   }
   m = block_max_256(m, red);
-  if (threadIdx.x == 0) partial[(int64_t)h * g.nchunks + chunk] = m;
+  if (threadIdx.x == 0) partial[(int64_t)h * g.tiles + t] = m;
 }
 
+// grid = (tiles, heads): requantise one tile of one head with the head's new scale.
 template <int D>
 __global__ __launch_bounds__(kThreads) void rotate_requantize(
     uint8_t* __restrict__ kc, float* __restrict__ k_scale, RotGeom g, DeltaTable tab,
     const float* __restrict__ partial) {
-  constexpr int CPT = D / 8;
   __shared__ float red[4];
-  const int chunk = blockIdx.x, h = blockIdx.y;
+  const int t = blockIdx.x, h = blockIdx.y;
+  uint8_t* tile = kc + ((int64_t)h * g.tiles + t) * kTile * D;
+  float* srow = k_scale + (int64_t)h * g.slots;
+  Units<D> x;
+  load_units<D>(tile, srow, t, g, x);
   float a = 0.0f;
-  for (int j = threadIdx.x; j < g.nchunks; j += kThreads)
-    a = __builtin_fmaxf(a, partial[(int64_t)h * g.nchunks + j]);
-  a = block_max_256(a, red);
+  for (int j = threadIdx.x; j < g.tiles; j += kThreads) a = __builtin_fmaxf(a, partial[(int64_t)h * g.tiles + j]);
+  a = block_max_256(a, red);   // also orders every thread's scale reads before the writes below
   float scale, inv;
   scale_from_absmax(a, scale, inv);
-
-  const int slot = chunk * kChunk + (threadIdx.x >> 3), cg = threadIdx.x & 7;
-  if (!slot_valid(slot, g.head, g.filled, g.slots)) return;
-  uint8_t* p = kc + (int64_t)h * g.tiles * kTile * D + k_code_offset(slot, (cg * CPT) & ~15, D) +
-               ((cg * CPT) & 15);
-  uint32_t w[CPT / 4];
-  load_codes<CPT>(p, w);
-  float* sp = k_scale + (int64_t)h * g.slots + slot;
-  float x[CPT];
-  dequant_rotate<CPT>(w, *sp, tab, cg * (CPT / 2), x);
 #pragma unroll
-  for (int j = 0; j < CPT / 4; ++j)
-    w[j] = e4m3x4(x[4 * j] * inv, x[4 * j + 1] * inv, x[4 * j + 2] * inv, x[4 * j + 3] * inv);
-  // every thread of the slot has read its scale before any of them may overwrite it: the
-  // 8 threads of a slot are consecutive lanes of one wavefront and execute in lock step, but
-  // make the ordering explicit anyway
-  __builtin_amdgcn_wave_barrier();
-  if constexpr (CPT == 16) {
-    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
-  } else {
-    *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+  for (int j = 0; j < kUnitsPerThread<D>; ++j) {
+    if (!x.ok[j]) continue;
+    float v[16];
+    dequant_rotate<16>(x.w[j], x.scale[j], tab, 8 * x.q[j], v);
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = e4m3x4(v[4 * e] * inv, v[4 * e + 1] * inv, v[4 * e + 2] * inv, v[4 * e + 3] * inv);
+    const int p = j * kThreads + int(threadIdx.x);
+    *reinterpret_cast<uint4*>(tile + p * 16) = make_uint4(o[0], o[1], o[2], o[3]);
+    if (x.q[j] == 0) srow[x.slot[j]] = scale;
   }
-  if (cg == 0) *sp = scale;
 }
 
 }  // namespace
@@ -129,7 +156,7 @@ hipError_t launch_delta_rotate(const kv_ring_desc& r, int32_t ring_head, int32_t
   g.heads = r.heads;
   g.nchunks = (r.slots + kChunk - 1) / kChunk;
   g.tiles = tile_count(r.slots);
-  dim3 grid(g.nchunks, r.heads);
+  dim3 grid(g.tiles, r.heads);
   if (r.head_dim == 128)
     hipLaunchKernelGGL(rotate_absmax_partials<128>, grid, dim3(kThreads), 0, stream, r.k,
                        r.k_scale, g, tab, ws);
