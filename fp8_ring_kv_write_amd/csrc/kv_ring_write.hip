@@ -115,6 +115,24 @@ __global__ __launch_bounds__(kThreads) void write_quantize(
   const int h = blockIdx.y;
   const int chunk = blockIdx.x < g.n_chunks_a ? g.chunk_a0 + blockIdx.x : blockIdx.x - g.n_chunks_a;
 
+  // this thread's inputs first (they do not depend on the scales), so that their latency
+  // overlaps the reduction of the partials
+  const int t = threadIdx.x >> 3, cg = threadIdx.x & 7;
+  const int slot = chunk * kChunk + t;
+  int i = slot - g.start;
+  i = i < 0 ? i + g.slots : i;
+  const bool mine = slot < g.slots && i < g.n;
+  float xk[CPT], xv[CPT];
+  float4 tab[CPT / 4];
+  if (mine) {
+    const int64_t src = ((int64_t)i * g.heads + h) * D + cg * CPT;
+    load_bf16<CPT>(k_new + src, xk);
+    load_bf16<CPT>(v_new + src, xv);
+    const float4* t4 = reinterpret_cast<const float4*>(rope + ((g.pos0 + i) * (D / 2) + cg * (CPT / 2)) * 2);
+#pragma unroll
+    for (int j = 0; j < CPT / 4; ++j) tab[j] = t4[j];
+  }
+
   // the write's per-head absmax of K' and V from the pass-1 partials
   float ak = 0.0f, av = 0.0f;
   for (int j = threadIdx.x; j < g.n_partial_groups; j += kThreads) {
@@ -127,16 +145,19 @@ __global__ __launch_bounds__(kThreads) void write_quantize(
   scale_from_absmax(ak, sk, ik);
   scale_from_absmax(av, sv, iv);
 
-  const int t = threadIdx.x >> 3, cg = threadIdx.x & 7;
-  const int slot = chunk * kChunk + t;
-  int i = slot - g.start;
-  i = i < 0 ? i + g.slots : i;
-  const bool mine = slot < g.slots && i < g.n;
   if (mine) {
-    const int64_t src = ((int64_t)i * g.heads + h) * D + cg * CPT;
-    float x[CPT];
-    load_bf16<CPT>(k_new + src, x);
-    rope_pairs<CPT>(x, rope + ((g.pos0 + i) * (D / 2) + cg * (CPT / 2)) * 2);
+    float (&x)[CPT] = xk;
+#pragma unroll
+    for (int j = 0; j < CPT / 4; ++j) {   // RoPE: pairs 2j, 2j+1 of this thread's channels
+      const float cs[2][2] = {{tab[j].x, tab[j].y}, {tab[j].z, tab[j].w}};
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int p = 2 * j + e;
+        const float xe = x[2 * p], xo = x[2 * p + 1];
+        x[2 * p] = xe * cs[e][0] - xo * cs[e][1];
+        x[2 * p + 1] = xe * cs[e][1] + xo * cs[e][0];
+      }
+    }
     uint32_t w[CPT / 4];
 #pragma unroll
     for (int j = 0; j < CPT / 4; ++j)
@@ -149,10 +170,9 @@ __global__ __launch_bounds__(kThreads) void write_quantize(
     } else {
       *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
     }
-    load_bf16<CPT>(v_new + src, x);
 #pragma unroll
     for (int j = 0; j < CPT / 4; ++j)
-      w[j] = e4m3x4(x[4 * j] * iv, x[4 * j + 1] * iv, x[4 * j + 2] * iv, x[4 * j + 3] * iv);
+      w[j] = e4m3x4(xv[4 * j] * iv, xv[4 * j + 1] * iv, xv[4 * j + 2] * iv, xv[4 * j + 3] * iv);
     uint32_t* vl = reinterpret_cast<uint32_t*>(&vlds[t][cg * CPT]);
 #pragma unroll
     for (int j = 0; j < CPT / 4; ++j) vl[j] = w[j];
