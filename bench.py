@@ -44,7 +44,7 @@ ATT_KERNEL = "attn_stream<128>"
 # (FETCH_SIZE, WRITE_SIZE) over this workload, each divided by the factor the same counter
 # reads for a torch copy of --calibrate-copy bytes.  Valid only for the kernel sources whose
 # hash is recorded; reported as null otherwise.
-ATT_TRAFFIC = {"sources": "1727db2eb11a918e", "bytes": 167_220_000,
+ATT_TRAFFIC = {"sources": "61b23e069a89d8ab", "bytes": 167_220_000,
                "read_bytes": 141_660_000, "write_bytes": 25_560_000}
 WRITE_BYTES = 2 * N * H * D * 2 + 2 * N * H * D + 2 * N * H * 4
 ROTATE_BYTES = 2 * (H * S * D + H * S * 4)
@@ -266,13 +266,21 @@ def main() -> int:
     return 0
 
 
-def kernel_sources_hash() -> str:
-    """blake2b of the sources the main attention kernel is compiled from."""
+def kernel_sources_hash(read=None) -> str:
+    """blake2b of the code (comments, blank lines and trailing blanks dropped) of the sources
+    the main attention kernel is compiled from.  `read(name)` returns a source's text."""
     import hashlib
+    import re
+    if read is None:
+        def read(name):
+            with open(os.path.join(ROOT, "fp8_ring_kv_write_amd", "csrc", name)) as fh:
+                return fh.read()
     h = hashlib.blake2b(digest_size=8)
     for f in ("ring_attention.hip", "kvring_common.hpp", "kvring_internal.hpp"):
-        with open(os.path.join(ROOT, "fp8_ring_kv_write_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        for line in read(f).splitlines():
+            line = re.sub(r"//.*$", "", line).rstrip()
+            if line:
+                h.update(line.encode() + b"\n")
     return h.hexdigest()
 
 

@@ -16,8 +16,10 @@
 //      this multi-XCD part write back and invalidate L2.
 //
 // Per tile: K tile and transposed V tile are copied straight from HBM into LDS with
-// global_load_lds (16 bytes per lane, XOR-swizzled 16-byte chunks, double-buffered so the next
-// tile's copy overlaps this tile's math).  Each wavefront owns 16 queries:
+// global_load_lds (16 bytes per lane; the ring stores each tile in the order the products read
+// it, so copies and operand reads are linear 1 KB wavefront accesses free of bank conflicts;
+// three buffers per operand, each copy issued two pipeline steps before it is needed).  Each
+// wavefront owns 16 queries:
 //   S^T = K Q^T           8 MFMA 16x16x128 FP8 (fp32 accumulate)
 //   online softmax        log2 domain, lazily rescaled (the running max may lag the true max
 //                         by up to 2^4, so P <= 16)
