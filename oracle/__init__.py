@@ -38,3 +38,4 @@ from .kvcache import (  # noqa: F401
     ring_attention,
     SCALE_FLOOR,
 )
+from .window import window_advance, read_time_ring, read_time_attention  # noqa: F401
