@@ -17,6 +17,10 @@ Also reported (one JSON line on stdout; progress on stderr):
   delta_rotate kv_ring_delta_rotate of one full ring (36.67 MB algorithmic: K codes and
               scales read and written);
   chunk       240 (write + attention) calls over 60 rings, 4 passes, as one chunk;
+  read_time_baseline  the design the ring replaces, with the same kernels: per call the linear
+              bfloat16 window is copied forward by the new tokens (kv_window_advance), rotated
+              and quantised whole (kv_ring_write of all 5,788 tokens), then attended; its
+              cache-maintenance time per call against the ring's write;
   cpu_baseline the CPU oracle on the same step (full call), on the host's cores.
 """
 
@@ -61,6 +65,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-chunk", action="store_true", help="skip the 240-call chunk measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-read-time", action="store_true", help="skip the read-time baseline")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="also run one plain device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
@@ -184,6 +189,58 @@ def main() -> int:
     rot_gbps = ROTATE_BYTES / (rot_us * 1e-6) / 1e9
     log(f"delta rotate {rot_us:.1f} us ({rot_gbps:.0f} GB/s)")
 
+    # ---------------------------------------------------------------- read-time baseline
+    # The design the ring replaces: a linear bfloat16 window copied forward by the new tokens,
+    # then rotated and quantised whole (one write of S tokens), then the same attention.
+    read_time = None
+    if not args.no_read_time:
+        win = [[to_dev(normal_bf16(tensor_seed("read_time", 0, t), (S, H, D))) for t in (1, 2)],
+               [torch.empty((S, H, D), dtype=torch.bfloat16, device=dev) for _ in range(2)]]
+        rt_ring = kv.Ring(H, S, D, dev)
+        ws_rt = torch.empty(kv.workspace_bytes(kv.OP_WRITE, H, S, D, S), dtype=torch.uint8, device=dev)
+        w_pos0 = pos0 + N - S          # the window ends with the new tokens
+
+        def rt_maintain(i):
+            src, dst = win[i % 2], win[(i + 1) % 2]
+            kv.kv_window_advance(src[0], dst[0], k_new, stream=stream)
+            kv.kv_window_advance(src[1], dst[1], v_new, stream=stream)
+            kv.kv_ring_write(rt_ring, dst[0], dst[1], 0, w_pos0, tab, workspace=ws_rt, stream=stream)
+
+        def rt_call(i):
+            rt_maintain(i)
+            kv.ring_attention(rt_ring, 0, S, q, pos0, tab, scale, out=out, lse=lse, workspace=ws_a,
+                              stream=stream)
+
+        for i in range(5):
+            rt_call(i)
+        # whole calls back to back, timed like the steps above
+        e0.record(stream)
+        for i in range(reps):
+            rt_call(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rt_call_us = 1000.0 * e0.elapsed_time(e1) / reps
+        # the maintenance part alone (copies + whole-window write), timed like the write above
+        mev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i, (mb, ma) in enumerate(mev):
+            mb.record(stream)
+            rt_maintain(i)
+            ma.record(stream)
+        torch.cuda.synchronize()
+        rt_maint_us = 1000.0 * sum(b.elapsed_time(a) for b, a in mev) / reps
+        wt_call_us = gpu_ms * 1000.0      # the timed steps: write + attention, back to back
+        read_time = {
+            "call_us": round(rt_call_us, 2), "maintenance_us": round(rt_maint_us, 2),
+            "write_time_call_us": round(wt_call_us, 2), "write_time_maintenance_us": round(write_us, 2),
+            "maintenance_speedup": round(rt_maint_us / write_us, 2),
+            "call_speedup": round(rt_call_us / wt_call_us, 3),
+            "chunk_maintenance_ms": {"read_time": round(240 * rt_maint_us / 1000, 2),
+                                     "write_time": round(240 * write_us / 1000, 2)},
+        }
+        log(f"read-time call {rt_call_us:.1f} us (maintenance {rt_maint_us:.1f} us) vs write-time "
+            f"{wt_call_us:.1f} us (maintenance {write_us:.1f} us)")
+        del win, rt_ring, ws_rt
+
     # ---------------------------------------------------------------- a 240-call chunk over 60 rings
     chunk = None
     if not args.no_chunk:
@@ -257,6 +314,7 @@ def main() -> int:
         "delta_rotate": {"us": round(rot_us, 2), "GBps": round(rot_gbps, 1),
                          "frac_hbm_peak": round(rot_gbps / HBM_PEAK_GBPS, 4), "bytes": ROTATE_BYTES},
         "chunk": chunk,
+        "read_time_baseline": read_time,
         "roofline": {"bound": "mfma", "achieved": round(att_tflops, 1), "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(att_tflops / FP8_PEAK_TFLOPS, 4),
                      "traffic": attention_traffic(), "kernel": ATT_KERNEL, "flop_per_launch": ATT_FLOP},

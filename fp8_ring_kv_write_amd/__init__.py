@@ -23,6 +23,7 @@ from ._lib import (  # noqa: F401
     kv_ring_delta_rotate,
     ring_attention,
     fp8_encode,
+    kv_window_advance,
     set_attention_events,
     status_string,
     lib,

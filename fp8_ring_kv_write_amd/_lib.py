@@ -55,6 +55,7 @@ def _load() -> ctypes.CDLL:
         "kv_ring_fp8_encode": (ctypes.c_int, [vp, vp, i64, vp]),
         "kv_ring_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "kv_ring_set_attention_events": (ctypes.c_int, [vp, vp]),
+        "kv_window_advance": (ctypes.c_int, [vp, vp, vp, i32, i32, i64, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -193,6 +194,23 @@ def fp8_encode(x, out=None, stream=None):
     _check("kv_ring_fp8_encode", lib.kv_ring_fp8_encode(_ptr(x), _ptr(out), int(x.numel()),
                                                         _stream(stream, x.device)))
     return out
+
+
+def kv_window_advance(src, dst, fresh, stream=None) -> None:
+    """Read-time baseline copy: dst = src[n:] followed by fresh, for contiguous device tensors of
+    rows ([window, ...] and [n, ...] with the same row shape and dtype); dst must not overlap
+    src or fresh."""
+    window, n = int(dst.shape[0]), int(fresh.shape[0])
+    if tuple(src.shape) != tuple(dst.shape) or tuple(fresh.shape[1:]) != tuple(dst.shape[1:]):
+        raise ValueError("src, dst and fresh must share the row shape; src and dst the window")
+    if src.dtype != dst.dtype or fresh.dtype != dst.dtype:
+        raise ValueError("src, dst and fresh must share the dtype")
+    if not (src.is_contiguous() and dst.is_contiguous() and fresh.is_contiguous()):
+        raise ValueError("contiguous tensors only")
+    row_bytes = dst[0].numel() * dst.element_size() if window > 0 else 0
+    _check("kv_window_advance", lib.kv_window_advance(
+        _ptr(src) if n < window else None, _ptr(dst), _ptr(fresh) if n > 0 else None, window, n,
+        row_bytes, _stream(stream, dst.device)))
 
 
 def set_attention_events(before=None, after=None) -> None:

@@ -15,7 +15,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvring.so")
-SOURCES = ["kvring_abi.hip", "kv_ring_write.hip", "kv_ring_delta_rotate.hip", "ring_attention.hip"]
+SOURCES = ["kvring_abi.hip", "kv_ring_write.hip", "kv_ring_delta_rotate.hip", "ring_attention.hip",
+           "kv_window.hip"]
 ARCH = os.environ.get("KVRING_ARCH", "gfx950")
 
 

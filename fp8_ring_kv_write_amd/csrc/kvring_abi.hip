@@ -11,6 +11,12 @@
 #include "kvring_common.hpp"
 #include "kvring_internal.hpp"
 
+namespace kvring {
+// kv_window.hip
+hipError_t launch_window_advance(const void* src, void* dst, const void* fresh, int32_t window,
+                                 int32_t n, int64_t row_bytes, hipStream_t stream);
+}  // namespace kvring
+
 namespace {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -158,6 +164,23 @@ int kv_ring_fp8_encode(const float* x, uint8_t* out, int64_t n, void* stream) {
   if (!x || !out) return KV_RING_ERR_NULL;
   if (!aligned(x, 16) || !aligned(out, 16)) return KV_RING_ERR_ALIGN;
   return status_of(kvring::launch_fp8_encode(x, out, n, static_cast<hipStream_t>(stream)));
+}
+
+int kv_window_advance(const void* src, void* dst, const void* fresh, int32_t window, int32_t n,
+                      int64_t row_bytes, void* stream) {
+  if (window < 1 || n < 0 || n > window) return KV_RING_ERR_RANGE;
+  if (row_bytes < 16 || row_bytes % 16 != 0 || row_bytes > (int64_t(1) << 30)) return KV_RING_ERR_SHAPE;
+  if (!dst || (n < window && !src) || (n > 0 && !fresh)) return KV_RING_ERR_NULL;
+  if (!aligned(dst, 16) || (src && !aligned(src, 16)) || (fresh && !aligned(fresh, 16)))
+    return KV_RING_ERR_ALIGN;
+  const uintptr_t d0 = reinterpret_cast<uintptr_t>(dst), d1 = d0 + uintptr_t(window) * uintptr_t(row_bytes);
+  auto overlaps = [&](const void* p, int64_t rows) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(p), a1 = a0 + uintptr_t(rows) * uintptr_t(row_bytes);
+    return rows > 0 && a0 < d1 && d0 < a1;
+  };
+  if (overlaps(src, window - n) || overlaps(fresh, n)) return KV_RING_ERR_RANGE;
+  return status_of(kvring::launch_window_advance(src, dst, fresh, window, n, row_bytes,
+                                                 static_cast<hipStream_t>(stream)));
 }
 
 int kv_ring_set_attention_events(void* before, void* after) {

@@ -163,6 +163,29 @@ int ring_attention(const kv_ring_desc *ring, int32_t ring_head, int32_t filled, 
 int kv_ring_fp8_encode(const float *x, uint8_t *out, int64_t n, void *stream);
 
 /*
+ * The read-time design that the ring replaces, kept as a baseline to measure against
+ * (abstract: whole-cache work repeated in every attention call before it was moved to write
+ * time; cpdf.ai blog, "Como rodar 57B...": the ring advances the window without copies).  That
+ * design keeps the last `window` tokens as a linear bfloat16 cache and, in every call, copies it
+ * forward by the n new tokens, then rotates and quantises the whole window again; with this
+ * library the second part is kv_ring_write of all `window` tokens into a ring of `window`
+ * slots at start_slot 0 (one per-head scale over the window), followed by ring_attention with
+ * ring_head 0 and filled = window.
+ *
+ * kv_window_advance is the copy: dst rows 0 .. window-n-1 = src rows n .. window-1, then
+ * dst rows window-n .. window-1 = fresh rows 0 .. n-1.
+ *   src, dst, fresh  device memory, 16-byte aligned, rows of row_bytes bytes (for a cache of
+ *                    [tokens][heads][head_dim] bfloat16, row_bytes = heads*head_dim*2);
+ *                    src may be NULL when n == window, fresh when n == 0;
+ *   0 <= n <= window, 1 <= window; 16 <= row_bytes <= 2^30, a multiple of 16.
+ * dst must not overlap the rows read from src or fresh (callers alternate two buffers).
+ * Errors: KV_RING_ERR_RANGE (window, n, or overlapping buffers), KV_RING_ERR_SHAPE (row_bytes),
+ * KV_RING_ERR_NULL, KV_RING_ERR_ALIGN.
+ */
+int kv_window_advance(const void *src, void *dst, const void *fresh, int32_t window, int32_t n,
+                      int64_t row_bytes, void *stream);
+
+/*
  * Profiling aid.  When both handles are non-NULL, each later ring_attention call records
  * `before` (a hipEvent_t) on its stream immediately before launching its main attention kernel
  * and `after` immediately after it, so the caller can time that kernel alone with

@@ -130,6 +130,19 @@ def test_argument_errors_are_reported_before_any_launch(kv):
     assert L.kv_ring_fp8_encode(F + 4, F, 5, None) == -2
     assert L.kv_ring_fp8_encode(F, F, 0, None) == 0
     assert L.kv_ring_rope_table(None, 10, 64, 10000.0) == -1
+    # window copy of the read-time baseline (src, dst, fresh: 10 rows of 64 bytes each)
+    S0, D0, N0 = F, F + (1 << 16), F + (2 << 16)
+    assert L.kv_window_advance(S0, D0, N0, 0, 0, 64, None) == -4
+    assert L.kv_window_advance(S0, D0, N0, 10, 11, 64, None) == -4
+    assert L.kv_window_advance(S0, D0, N0, 10, -1, 64, None) == -4
+    assert L.kv_window_advance(S0, D0, N0, 10, 3, 8, None) == -3
+    assert L.kv_window_advance(S0, D0, N0, 10, 3, 72, None) == -3
+    assert L.kv_window_advance(S0, None, N0, 10, 3, 64, None) == -1
+    assert L.kv_window_advance(None, D0, N0, 10, 3, 64, None) == -1
+    assert L.kv_window_advance(S0, D0, None, 10, 3, 64, None) == -1
+    assert L.kv_window_advance(S0, D0 + 8, N0, 10, 3, 64, None) == -2
+    assert L.kv_window_advance(S0, S0 + 64, N0, 10, 3, 64, None) == -4    # dst overlaps src
+    assert L.kv_window_advance(S0, D0, D0 + 320, 10, 3, 64, None) == -4   # fresh inside dst
 
 
 def test_product_path_has_no_oracle_import():

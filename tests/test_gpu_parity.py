@@ -296,3 +296,47 @@ def test_attention_is_deterministic(kv, torch):
     o2, l2 = kv.ring_attention(p.g, p.head, p.filled, q, sched[-1].pos0, p.tab_dev, 0.09)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+# ------------------------------------------------------------------ read-time baseline
+
+@pytest.mark.parametrize("w,n,row", [(5788, 757, (24, 128)), (300, 0, (2, 64)), (300, 300, (2, 64)),
+                                     (97, 1, (8,)), (97, 96, (3, 40))])
+def test_window_advance_bit_exact(kv, torch, w, n, row):
+    rng = np.random.default_rng(w + n)
+    win = rng.integers(0, 1 << 16, size=(w, *row), dtype=np.uint16)
+    fresh = rng.integers(0, 1 << 16, size=(n, *row), dtype=np.uint16)
+    src, fr = to_dev_bf16(win), to_dev_bf16(fresh)
+    dst = torch.full_like(src, float("nan"))
+    kv.kv_window_advance(src, dst, fr)
+    torch.cuda.synchronize()
+    got = dst.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, oracle.window_advance(win, fresh))
+    if n < w:   # the copy never writes over what it reads
+        with pytest.raises(kv.KvRingError):
+            kv.kv_window_advance(src, src, fr)
+
+
+def test_read_time_call_full_size(kv, torch):
+    """The read-time design on one layer: a 5,788-token bfloat16 window (positions 6,212 ..
+    11,999 after the advance) moves forward by 757 tokens, the whole window is rotated and
+    quantised again (one write of 5,788 tokens into a ring of 5,788 slots at slot 0), then 757
+    queries at the newest positions attend over it."""
+    w, n, h, d, p_new = 5788, 757, 24, 128, 6212
+    old_k = normal_bf16(tensor_seed("read_time", 0, 1), (w, h, d))
+    old_v = normal_bf16(tensor_seed("read_time", 0, 2), (w, h, d))
+    new_k = normal_bf16(tensor_seed("read_time", 1, 1), (n, h, d))
+    new_v = normal_bf16(tensor_seed("read_time", 1, 2), (n, h, d))
+    q = normal_bf16(tensor_seed("read_time", 1, 0), (n, h, d))
+    wk, wv = oracle.window_advance(old_k, new_k), oracle.window_advance(old_v, new_v)
+    dk, dv = torch.empty((w, h, d), dtype=torch.bfloat16, device="cuda"), torch.empty(
+        (w, h, d), dtype=torch.bfloat16, device="cuda")
+    kv.kv_window_advance(to_dev_bf16(old_k), dk, to_dev_bf16(new_k))
+    kv.kv_window_advance(to_dev_bf16(old_v), dv, to_dev_bf16(new_v))
+    p = Pair(kv, torch, h, w, d)
+    kv.kv_ring_write(p.g, dk, dv, 0, p_new, p.tab_dev)
+    p.o = oracle.read_time_ring(wk, wv, p_new, p.tab)
+    p.head, p.filled = 0, w
+    p.assert_same("read-time window")
+    out, lse, ro, rl = p.attend(q, p_new + w - n, 1 / math.sqrt(d))
+    check_attention(out, lse, ro, rl, label="read-time call")
