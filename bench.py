@@ -261,25 +261,38 @@ def main() -> int:
                 inputs.append(tuple(torch.randn((N, H, D), generator=gen, device=dev).to(torch.bfloat16)
                                     for _ in range(3)))
 
-        def run_chunk():
+        def run_chunk(st=None):
             for p in range(passes):
                 for l in range(layers):
                     kk, vv, qq = inputs[p * layers + l]
-                    kv.kv_ring_write(rings[l], kk, vv, start, pos0, tab, workspace=ws_w, stream=stream)
+                    kv.kv_ring_write(rings[l], kk, vv, start, pos0, tab, workspace=ws_w, stream=st)
                     kv.ring_attention(rings[l], head, filled, qq, pos0, tab, scale, out=out, lse=lse,
-                                      workspace=ws_a, stream=stream)
+                                      workspace=ws_a, stream=st)
 
-        run_chunk()
+        run_chunk(stream)
         torch.cuda.synchronize()
         reps_c = 5
         t0 = time.perf_counter()
         for _ in range(reps_c):
-            run_chunk()
+            run_chunk(stream)
         torch.cuda.synchronize()
         chunk_ms = (time.perf_counter() - t0) * 1000.0 / reps_c
-        chunk = {"calls": passes * layers, "layers": layers, "passes": passes, "ms": round(chunk_ms, 3)}
-        log(f"chunk of 240 calls: {chunk_ms:.2f} ms")
-        del inputs, rings
+        # the same 480 library calls captured once in a HIP graph and replayed
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run_chunk()                   # the capture stream is torch's current stream here
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps_c):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1000.0 / reps_c
+        chunk = {"calls": passes * layers, "layers": layers, "passes": passes, "ms": round(chunk_ms, 3),
+                 "graph_ms": round(graph_ms, 3)}
+        log(f"chunk of 240 calls: {chunk_ms:.2f} ms eager, {graph_ms:.2f} ms as one graph")
+        del inputs, rings, graph
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None

@@ -340,3 +340,69 @@ def test_read_time_call_full_size(kv, torch):
     p.assert_same("read-time window")
     out, lse, ro, rl = p.attend(q, p_new + w - n, 1 / math.sqrt(d))
     check_attention(out, lse, ro, rl, label="read-time call")
+
+
+# ------------------------------------------------------------------ graph capture
+
+def test_layer_calls_replay_from_a_captured_graph(kv, torch):
+    """Write + attention on two rings captured once in a HIP graph (no call allocates, memsets or
+    synchronises), replayed three times with eager work and synchronisation in between: every
+    replay leaves exactly the rings, outputs and LSE that the same calls leave when run eagerly."""
+    h, s, d, n = 4, 700, 128, 100
+    tab_dev, _ = tables(kv, torch, d)
+    rings = [kv.Ring(h, s, d), kv.Ring(h, s, d)]
+    for r in rings:
+        for c in range(6):
+            kv.kv_ring_write(r, to_dev_bf16(normal_bf16(tensor_seed("graph", c, 1), (n, h, d))),
+                             to_dev_bf16(normal_bf16(tensor_seed("graph", c, 2), (n, h, d))),
+                             (c * n) % s, c * n, tab_dev)
+    head, filled = (6 * n) % s, 6 * n
+    k_new = [to_dev_bf16(normal_bf16(tensor_seed("graph", 10 + i, 1), (n, h, d))) for i in range(2)]
+    v_new = [to_dev_bf16(normal_bf16(tensor_seed("graph", 10 + i, 2), (n, h, d))) for i in range(2)]
+    q = [to_dev_bf16(normal_bf16(tensor_seed("graph", 10 + i, 0), (n, h, d))) for i in range(2)]
+    ws_w = torch.empty(kv.workspace_bytes(kv.OP_WRITE, h, s, d, n), dtype=torch.uint8, device="cuda")
+    ws_a = torch.empty(kv.workspace_bytes(kv.OP_ATTENTION, h, s, d, n), dtype=torch.uint8, device="cuda")
+    outs = [torch.empty_like(q[0]) for _ in range(2)]
+    lses = [torch.empty((h, n), dtype=torch.float32, device="cuda") for _ in range(2)]
+    start, pos0 = (head - n) % s, 5 * n
+    snap = [(r.k.clone(), r.v.clone(), r.k_scale.clone(), r.v_scale.clone()) for r in rings]
+
+    def calls():
+        for i, r in enumerate(rings):
+            kv.kv_ring_write(r, k_new[i], v_new[i], start, pos0, tab_dev, workspace=ws_w)
+            kv.ring_attention(r, head, filled, q[i], pos0, tab_dev, 0.09, out=outs[i], lse=lses[i],
+                              workspace=ws_a)
+
+    def restore():
+        for r, (k, v, ks, vs) in zip(rings, snap):
+            r.k.copy_(k), r.v.copy_(v), r.k_scale.copy_(ks), r.v_scale.copy_(vs)
+
+    def state():
+        return [t.clone() for r in rings for t in (r.k, r.v, r.k_scale, r.v_scale)] + \
+               [t.clone() for t in outs + lses]
+
+    calls()
+    torch.cuda.synchronize()
+    eager = state()
+    restore()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):     # warm the side stream before capture
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        restore()
+        for t in outs + lses:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = state()
+        for a, b in zip(got, eager):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep} differs"
+        _ = (q[0].float() * 2).sum().item()   # eager work between replays
