@@ -4,9 +4,10 @@
 One step = one layer call of the path, the unit the Runway Characters pages count 240 of per
 chunk (abstract of arXiv 2611.05642): kv_ring_write of 757 new tokens (RoPE + per-head FP8)
 into a full 5,788-slot ring, then ring_attention of 757 queries over all 5,788 slots, with 24
-heads x head_dim 128 as one GPU's share.  Inputs are seeded synthetic N(0,1) bfloat16 tensors
-already resident in device memory.  `value` is steps per second, i.e. ring_attention calls per
-second including their write.
+heads x head_dim 128 as one GPU's share, issued as one kv_ring_write_attend call (the same
+work and results as the two calls; the two-call step is timed and reported beside it).  Inputs
+are seeded synthetic N(0,1) bfloat16 tensors already resident in device memory.  `value` is
+steps per second, i.e. ring_attention calls per second including their write.
 
 Also reported (one JSON line on stdout; progress on stderr):
   attention   the main attention kernel alone, timed with HIP events recorded on its launch
@@ -119,7 +120,13 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
+    ws_f = torch.empty(kv.workspace_bytes(kv.OP_WRITE_ATTEND, H, S, D, N), dtype=torch.uint8, device=dev)
+
     def step():
+        kv.kv_ring_write_attend(ring, k_new, v_new, start, pos0, head, filled, q, pos0, tab, scale,
+                                out=out, lse=lse, workspace=ws_f, stream=stream)
+
+    def step_separate():
         kv.kv_ring_write(ring, k_new, v_new, start, pos0, tab, workspace=ws_w, stream=stream)
         kv.ring_attention(ring, head, filled, q, pos0, tab, scale, out=out, lse=lse, workspace=ws_a,
                           stream=stream)
@@ -141,6 +148,16 @@ def main() -> int:
     gpu_ms = e0.elapsed_time(e1) / args.steps
     ms_per_step = wall * 1000.0 / args.steps
     log(f"step: {ms_per_step * 1000:.1f} us wall, {gpu_ms * 1000:.1f} us GPU")
+    # the same step as two calls (kv_ring_write, then ring_attention)
+    for _ in range(5):
+        step_separate()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step_separate()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    sep_ms = e0.elapsed_time(e1) / args.steps
+    log(f"step as two calls: {sep_ms * 1000:.1f} us GPU")
 
     # ---------------------------------------------------------------- attention kernel alone
     reps = max(50, args.steps // 2)
@@ -265,9 +282,8 @@ def main() -> int:
             for p in range(passes):
                 for l in range(layers):
                     kk, vv, qq = inputs[p * layers + l]
-                    kv.kv_ring_write(rings[l], kk, vv, start, pos0, tab, workspace=ws_w, stream=st)
-                    kv.ring_attention(rings[l], head, filled, qq, pos0, tab, scale, out=out, lse=lse,
-                                      workspace=ws_a, stream=st)
+                    kv.kv_ring_write_attend(rings[l], kk, vv, start, pos0, head, filled, qq, pos0, tab,
+                                            scale, out=out, lse=lse, workspace=ws_f, stream=st)
 
         run_chunk(stream)
         torch.cuda.synchronize()
@@ -319,6 +335,7 @@ def main() -> int:
             "heads": H, "slots": S, "head_dim": D, "new_tokens": N, "queries": N,
         },
         "gpu_ms_per_step": round(gpu_ms, 5),
+        "two_call_gpu_ms_per_step": round(sep_ms, 5),
         "attention": {"kernel_us": round(att_us, 2), "call_us": round(call_us, 2),
                       "tflops": round(att_tflops, 1), "frac_fp8_peak": round(att_tflops / FP8_PEAK_TFLOPS, 4),
                       "calls_per_s": round(1e6 / call_us, 1)},

@@ -12,6 +12,7 @@ from ._lib import (  # noqa: F401
     OP_WRITE,
     OP_DELTA_ROTATE,
     OP_ATTENTION,
+    OP_WRITE_ATTEND,
     TILE,
     library_path,
     codes_bytes,
@@ -22,6 +23,7 @@ from ._lib import (  # noqa: F401
     kv_ring_write,
     kv_ring_delta_rotate,
     ring_attention,
+    kv_ring_write_attend,
     fp8_encode,
     kv_window_advance,
     set_attention_events,

@@ -10,7 +10,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(HERE, "libkvring.so")
 
-OP_WRITE, OP_DELTA_ROTATE, OP_ATTENTION = 1, 2, 3
+OP_WRITE, OP_DELTA_ROTATE, OP_ATTENTION, OP_WRITE_ATTEND = 1, 2, 3, 4
 TILE = 128
 
 
@@ -56,6 +56,8 @@ def _load() -> ctypes.CDLL:
         "kv_ring_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "kv_ring_set_attention_events": (ctypes.c_int, [vp, vp]),
         "kv_window_advance": (ctypes.c_int, [vp, vp, vp, i32, i32, i64, vp]),
+        "kv_ring_write_attend": (ctypes.c_int, [dp, vp, vp, i32, i32, i64, i32, i32, vp, i32, i64, vp,
+                                                i64, f32, vp, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -183,6 +185,26 @@ def ring_attention(ring: Ring, ring_head: int, filled: int, q, q_pos0: int, rope
     _check("ring_attention", lib.ring_attention(
         ring.desc, ring_head, filled, _ptr(q), nq, q_pos0, _ptr(rope), int(rope.shape[0]),
         float(softmax_scale), _ptr(out), _ptr(lse), _ptr(ws), wsb, _stream(stream, ring.device)))
+    return out, lse
+
+
+def kv_ring_write_attend(ring: Ring, k_new, v_new, start_slot: int, pos0: int, ring_head: int,
+                         filled: int, q, q_pos0: int, rope, softmax_scale: float, out=None, lse=None,
+                         workspace=None, stream=None):
+    """kv_ring_write then ring_attention in one call (ring_head, filled: the ring after the
+    write).  Returns (out, lse) like ring_attention."""
+    import torch
+    n, nq = int(k_new.shape[0]), int(q.shape[0])
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((ring.heads, nq), dtype=torch.float32, device=q.device)
+    need = workspace_bytes(OP_WRITE_ATTEND, ring.heads, ring.slots, ring.head_dim, max(n, nq, 1))
+    ws, wsb = _ws(workspace, need, ring.device)
+    _check("kv_ring_write_attend", lib.kv_ring_write_attend(
+        ring.desc, _ptr(k_new), _ptr(v_new), n, start_slot, pos0, ring_head, filled, _ptr(q), nq,
+        q_pos0, _ptr(rope), int(rope.shape[0]), float(softmax_scale), _ptr(out), _ptr(lse), _ptr(ws),
+        wsb, _stream(stream, ring.device)))
     return out, lse
 
 

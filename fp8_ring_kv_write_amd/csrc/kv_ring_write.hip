@@ -66,32 +66,40 @@ __device__ inline float absmax(const float (&x)[CPT]) {
   return m;
 }
 
-// Pass 1.  grid = (ceil(n/32), heads, tensors); tensor 0 is rotated (K or Q), tensor 1 (V) is
-// not.  partial layout [tensor][heads][ngroups].
-// `zero`/`nzero`: int counters that work-group (0, 0, 0) clears for a kernel launched after this
-// one on the same stream (the attention's row counters); NULL/0 when unused.
+// Pass 1: per (tensor, head, 32-token group) max |x|, rotated tensors (K, Q) after RoPE at their
+// positions.  One launch can serve up to three tensors (K and V of a write, and the queries of
+// the attention that follows it): grid = (max groups, heads, jobs); job z writes its partials
+// [heads][groups of job z] at its own base pointer.
+struct AbsmaxJob {
+  const uint16_t* x;   // bfloat16 [n][heads][D]
+  float* partial;      // [heads][groups]
+  int64_t pos0;        // position of token 0 (rotated jobs)
+  int32_t n, groups, rotate;
+};
+struct AbsmaxJobs {
+  AbsmaxJob job[3];
+};
+
 template <int D>
-__global__ __launch_bounds__(kThreads) void rope_absmax_partials(
-    const uint16_t* __restrict__ x0, const uint16_t* __restrict__ x1, int32_t n, int32_t heads,
-    int64_t pos0, const float* __restrict__ rope, float* __restrict__ partial, int* zero,
-    int32_t nzero) {
+__global__ __launch_bounds__(kThreads) void rope_absmax_partials(AbsmaxJobs jobs, int32_t heads,
+                                                                 const float* __restrict__ rope) {
   constexpr int CPT = D / 8;
   __shared__ float red[4];
-  const int grp = blockIdx.x, h = blockIdx.y, tensor = blockIdx.z;
-  if (grp == 0 && h == 0 && tensor == 0)
-    for (int j = threadIdx.x; j < nzero; j += kThreads) zero[j] = 0;
+  const AbsmaxJob& jb = jobs.job[blockIdx.z];
+  const int grp = blockIdx.x, h = blockIdx.y;
+  if (grp >= jb.groups) return;   // uniform per work-group: this job has fewer tokens
   const int i = grp * kChunk + (threadIdx.x >> 3);
   const int cg = threadIdx.x & 7;
   float m = 0.0f;
-  if (i < n) {
-    const uint16_t* src = (tensor == 0 ? x0 : x1) + ((int64_t)i * heads + h) * D + cg * CPT;
+  if (i < jb.n) {
+    const uint16_t* src = jb.x + ((int64_t)i * heads + h) * D + cg * CPT;
     float x[CPT];
     load_bf16<CPT>(src, x);
-    if (tensor == 0) rope_pairs<CPT>(x, rope + ((pos0 + i) * (D / 2) + cg * (CPT / 2)) * 2);
+    if (jb.rotate) rope_pairs<CPT>(x, rope + ((jb.pos0 + i) * (D / 2) + cg * (CPT / 2)) * 2);
     m = absmax<CPT>(x);
   }
   m = block_max_256(m, red);
-  if (threadIdx.x == 0) partial[((int64_t)tensor * heads + h) * gridDim.x + grp] = m;
+  if (threadIdx.x == 0) jb.partial[(int64_t)h * jb.groups + grp] = m;
 }
 
 struct WriteGeom {
@@ -217,20 +225,38 @@ int64_t write_workspace_floats(int32_t heads, int32_t n) {
   return 2LL * heads * ((n + kChunk - 1) / kChunk);
 }
 
-hipError_t launch_write(const kv_ring_desc& r, const uint16_t* k_new, const uint16_t* v_new,
-                        int32_t n, int32_t start_slot, int64_t pos0, const float* rope,
-                        float* ws, hipStream_t stream) {
-  const int ngroups = (n + kChunk - 1) / kChunk;
-  dim3 g1(ngroups, r.heads, 2);
-  if (r.head_dim == 128)
-    hipLaunchKernelGGL(rope_absmax_partials<128>, g1, dim3(kThreads), 0, stream, k_new, v_new, n,
-                       r.heads, pos0, rope, ws, nullptr, 0);
-  else
-    hipLaunchKernelGGL(rope_absmax_partials<64>, g1, dim3(kThreads), 0, stream, k_new, v_new, n,
-                       r.heads, pos0, rope, ws, nullptr, 0);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+namespace {
 
+hipError_t launch_absmax(const AbsmaxJobs& jobs, int njobs, int32_t heads, int32_t head_dim,
+                         const float* rope, hipStream_t stream) {
+  int gx = 1;
+  for (int j = 0; j < njobs; ++j) gx = jobs.job[j].groups > gx ? jobs.job[j].groups : gx;
+  dim3 g1(gx, heads, njobs);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(rope_absmax_partials<128>, g1, dim3(kThreads), 0, stream, jobs, heads, rope);
+  else
+    hipLaunchKernelGGL(rope_absmax_partials<64>, g1, dim3(kThreads), 0, stream, jobs, heads, rope);
+  return hipGetLastError();
+}
+
+AbsmaxJob absmax_job(const uint16_t* x, int32_t n, bool rotate, int64_t pos0, float* partial) {
+  AbsmaxJob j;
+  j.x = x;
+  j.partial = partial;
+  j.pos0 = pos0;
+  j.n = n;
+  j.groups = (n + kChunk - 1) / kChunk;
+  j.rotate = rotate ? 1 : 0;
+  return j;
+}
+
+}  // namespace
+
+// Write pass 2 (pass 1's K and V partials are in ws).
+hipError_t launch_write_quantize(const kv_ring_desc& r, const uint16_t* k_new, const uint16_t* v_new,
+                                 int32_t n, int32_t start_slot, int64_t pos0, const float* rope,
+                                 float* ws, hipStream_t stream) {
+  const int ngroups = (n + kChunk - 1) / kChunk;
   WriteGeom g;
   g.n = n;
   g.start = start_slot;
@@ -260,19 +286,43 @@ hipError_t launch_write(const kv_ring_desc& r, const uint16_t* k_new, const uint
   return hipGetLastError();
 }
 
-// Q partials for the attention prologue reuse pass 1 (tensor 0 only).
+hipError_t launch_write(const kv_ring_desc& r, const uint16_t* k_new, const uint16_t* v_new,
+                        int32_t n, int32_t start_slot, int64_t pos0, const float* rope,
+                        float* ws, hipStream_t stream) {
+  const int ngroups = (n + kChunk - 1) / kChunk;
+  AbsmaxJobs jobs;
+  jobs.job[0] = absmax_job(k_new, n, true, pos0, ws);
+  jobs.job[1] = absmax_job(v_new, n, false, 0, ws + (int64_t)r.heads * ngroups);
+  jobs.job[2] = jobs.job[1];
+  hipError_t e = launch_absmax(jobs, 2, r.heads, r.head_dim, rope, stream);
+  if (e != hipSuccess) return e;
+  return launch_write_quantize(r, k_new, v_new, n, start_slot, pos0, rope, ws, stream);
+}
+
+// Queries' partials for the attention: [heads][ceil(nq/32)] at `partial`.
 hipError_t launch_q_absmax(const uint16_t* q, int32_t nq, int32_t heads, int32_t head_dim,
-                           int64_t q_pos0, const float* rope, float* partial, int* zero,
-                           int32_t nzero, hipStream_t stream) {
-  const int ngroups = (nq + kChunk - 1) / kChunk;
-  dim3 g1(ngroups, heads, 1);
-  if (head_dim == 128)
-    hipLaunchKernelGGL(rope_absmax_partials<128>, g1, dim3(kThreads), 0, stream, q, q, nq, heads,
-                       q_pos0, rope, partial, zero, nzero);
-  else
-    hipLaunchKernelGGL(rope_absmax_partials<64>, g1, dim3(kThreads), 0, stream, q, q, nq, heads,
-                       q_pos0, rope, partial, zero, nzero);
-  return hipGetLastError();
+                           int64_t q_pos0, const float* rope, float* partial, hipStream_t stream) {
+  AbsmaxJobs jobs;
+  jobs.job[0] = absmax_job(q, nq, true, q_pos0, partial);
+  jobs.job[1] = jobs.job[2] = jobs.job[0];
+  return launch_absmax(jobs, 1, heads, head_dim, rope, stream);
+}
+
+// Write followed by attention: K, V and Q partials in one launch, then the write's second pass;
+// the attention (launched by the caller) finds its query partials at q_partial.
+hipError_t launch_write_and_q_absmax(const kv_ring_desc& r, const uint16_t* k_new,
+                                     const uint16_t* v_new, int32_t n, int32_t start_slot,
+                                     int64_t pos0, const uint16_t* q, int32_t nq, int64_t q_pos0,
+                                     const float* rope, float* ws, float* q_partial,
+                                     hipStream_t stream) {
+  const int ngroups = (n + kChunk - 1) / kChunk;
+  AbsmaxJobs jobs;
+  jobs.job[0] = absmax_job(k_new, n, true, pos0, ws);
+  jobs.job[1] = absmax_job(v_new, n, false, 0, ws + (int64_t)r.heads * ngroups);
+  jobs.job[2] = absmax_job(q, nq, true, q_pos0, q_partial);
+  hipError_t e = launch_absmax(jobs, 3, r.heads, r.head_dim, rope, stream);
+  if (e != hipSuccess) return e;
+  return launch_write_quantize(r, k_new, v_new, n, start_slot, pos0, rope, ws, stream);
 }
 
 }  // namespace kvring

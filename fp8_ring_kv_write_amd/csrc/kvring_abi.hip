@@ -41,6 +41,12 @@ int check_workspace(void* ws, size_t have, size_t need) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? KV_RING_OK : KV_RING_ERR_LAUNCH; }
 
+// Floats of the fused call's workspace taken by its write part (the attention part follows,
+// 16-byte aligned); m = max(new tokens, queries).
+int64_t write_attend_split(int32_t heads, int32_t m) {
+  return (kvring::write_workspace_floats(heads, m) + 3) / 4 * 4;
+}
+
 double rope_theta(int32_t i, int32_t head_dim, double base) {
   return std::pow(base, -(2.0 * i) / (double)head_dim);
 }
@@ -92,6 +98,10 @@ size_t kv_ring_workspace_bytes(int32_t op, int32_t heads, int32_t slots, int32_t
       if (n < 0) return 0;
       if (n == 0) return 16;
       return sizeof(float) * (size_t)kvring::attention_workspace_floats(heads, slots, head_dim, n);
+    case KV_RING_OP_WRITE_ATTEND:   // n = max(new tokens, queries)
+      if (n < 1) return 0;
+      return sizeof(float) * (size_t)(write_attend_split(heads, n) +
+                                      kvring::attention_workspace_floats(heads, slots, head_dim, n));
     default:
       return 0;
   }
@@ -154,8 +164,49 @@ int ring_attention(const kv_ring_desc* ring, int32_t ring_head, int32_t filled, 
   if (st) return st;
   return status_of(kvring::launch_attention(*ring, ring_head, filled, static_cast<const uint16_t*>(q), nq,
                                             q_pos0, rope_table, softmax_scale, static_cast<uint16_t*>(out),
-                                            lse, static_cast<float*>(workspace),
+                                            lse, static_cast<float*>(workspace), false,
                                             static_cast<hipStream_t>(stream)));
+}
+
+int kv_ring_write_attend(const kv_ring_desc* ring, const void* k_new, const void* v_new, int32_t n,
+                         int32_t start_slot, int64_t pos0, int32_t ring_head, int32_t filled,
+                         const void* q, int32_t nq, int64_t q_pos0, const float* rope_table,
+                         int64_t rope_n_pos, float softmax_scale, void* out, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_ring(ring);
+  if (st) return st;
+  // the write's checks
+  if (!k_new || !v_new || !rope_table) return KV_RING_ERR_NULL;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(rope_table, 16)) return KV_RING_ERR_ALIGN;
+  if (n < 1 || n > ring->slots || start_slot < 0 || start_slot >= ring->slots) return KV_RING_ERR_RANGE;
+  if (pos0 < 0 || rope_n_pos < 1 || pos0 > rope_n_pos - n) return KV_RING_ERR_POSITION;
+  // the attention's checks
+  if (nq < 0 || ring_head < 0 || ring_head >= ring->slots || filled < 0 || filled > ring->slots)
+    return KV_RING_ERR_RANGE;
+  if (nq > 0) {
+    if (!q || !out || !lse) return KV_RING_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(out, 8) || !aligned(lse, 4)) return KV_RING_ERR_ALIGN;
+    if (q_pos0 < 0 || q_pos0 > rope_n_pos - nq) return KV_RING_ERR_POSITION;
+    if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0f)) return KV_RING_ERR_RANGE;
+  }
+  const int32_t m = n > nq ? n : nq;
+  st = check_workspace(workspace, workspace_bytes,
+                       kv_ring_workspace_bytes(KV_RING_OP_WRITE_ATTEND, ring->heads, ring->slots, ring->head_dim, m));
+  if (st) return st;
+  float* ws = static_cast<float*>(workspace);
+  float* ws_att = ws + write_attend_split(ring->heads, m);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const auto* kn = static_cast<const uint16_t*>(k_new);
+  const auto* vn = static_cast<const uint16_t*>(v_new);
+  if (nq == 0)
+    return status_of(kvring::launch_write(*ring, kn, vn, n, start_slot, pos0, rope_table, ws, s));
+  hipError_t e = kvring::launch_write_and_q_absmax(*ring, kn, vn, n, start_slot, pos0,
+                                                   static_cast<const uint16_t*>(q), nq, q_pos0,
+                                                   rope_table, ws, ws_att, s);
+  if (e != hipSuccess) return KV_RING_ERR_LAUNCH;
+  return status_of(kvring::launch_attention(*ring, ring_head, filled, static_cast<const uint16_t*>(q), nq,
+                                            q_pos0, rope_table, softmax_scale, static_cast<uint16_t*>(out),
+                                            lse, ws_att, true, s));
 }
 
 int kv_ring_fp8_encode(const float* x, uint8_t* out, int64_t n, void* stream) {

@@ -27,10 +27,21 @@ struct DeltaTable {  // cos/sin of delta * theta_i for i < head_dim/2, float32
 hipError_t launch_delta_rotate(const kv_ring_desc& r, int32_t ring_head, int32_t filled,
                                const DeltaTable& tab, float* ws, hipStream_t stream);
 
+// The attention's workspace starts with the queries' absmax partials ([heads][ceil(nq/32)]);
+// with q_partials_ready an earlier launch on the stream has written them and the attention
+// does not compute them again.
 hipError_t launch_attention(const kv_ring_desc& r, int32_t ring_head, int32_t filled,
                             const uint16_t* q, int32_t nq, int64_t q_pos0, const float* rope,
                             float softmax_scale, uint16_t* out, float* lse, float* ws,
-                            hipStream_t stream);
+                            bool q_partials_ready, hipStream_t stream);
+
+// Write pass 1 for K, V and the queries in one launch, then write pass 2; the queries'
+// partials go to q_partial (the start of the attention's workspace).
+hipError_t launch_write_and_q_absmax(const kv_ring_desc& r, const uint16_t* k_new,
+                                     const uint16_t* v_new, int32_t n, int32_t start_slot,
+                                     int64_t pos0, const uint16_t* q, int32_t nq, int64_t q_pos0,
+                                     const float* rope, float* ws, float* q_partial,
+                                     hipStream_t stream);
 
 void set_attention_events(void* before, void* after);
 

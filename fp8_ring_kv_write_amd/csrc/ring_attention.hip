@@ -40,8 +40,7 @@
 namespace kvring {
 
 hipError_t launch_q_absmax(const uint16_t* q, int32_t nq, int32_t heads, int32_t head_dim,
-                           int64_t q_pos0, const float* rope, float* partial, int* zero,
-                           int32_t nzero, hipStream_t stream);
+                           int64_t q_pos0, const float* rope, float* partial, hipStream_t stream);
 
 namespace {
 
@@ -778,7 +777,7 @@ int64_t attention_workspace_floats(int32_t heads, int32_t slots, int32_t head_di
 hipError_t launch_attention(const kv_ring_desc& r, int32_t ring_head, int32_t filled,
                             const uint16_t* q, int32_t nq, int64_t q_pos0, const float* rope,
                             float softmax_scale, uint16_t* out, float* lse, float* ws,
-                            hipStream_t stream) {
+                            bool q_partials_ready, hipStream_t stream) {
   const Plan p = make_plan(r.heads, r.slots, nq, ring_head, filled, device_cus());
   AttnArgs a;
   a.kc = r.k;
@@ -812,8 +811,11 @@ hipError_t launch_attention(const kv_ring_desc& r, int32_t ring_head, int32_t fi
   a.part_o = ws + qparts;
   a.part_ml = a.part_o + (int64_t)p.rows * 8 * kRowQ * r.head_dim;
 
-  hipError_t e = launch_q_absmax(q, nq, r.heads, r.head_dim, q_pos0, rope, ws, nullptr, 0, stream);
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (!q_partials_ready) {   // else an earlier launch on this stream left them at ws
+    e = launch_q_absmax(q, nq, r.heads, r.head_dim, q_pos0, rope, ws, stream);
+    if (e != hipSuccess) return e;
+  }
   if (g_ev_before && g_ev_after) {
     e = hipEventRecord(g_ev_before, stream);
     if (e != hipSuccess) return e;

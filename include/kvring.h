@@ -56,7 +56,12 @@ enum {
   KV_RING_ERR_LAUNCH = -7      /* a kernel launch failed (HIP error)                   */
 };
 
-enum { KV_RING_OP_WRITE = 1, KV_RING_OP_DELTA_ROTATE = 2, KV_RING_OP_ATTENTION = 3 };
+enum {
+  KV_RING_OP_WRITE = 1,
+  KV_RING_OP_DELTA_ROTATE = 2,
+  KV_RING_OP_ATTENTION = 3,
+  KV_RING_OP_WRITE_ATTEND = 4
+};
 
 /*
  * One ring (one layer, one GPU's share of heads).  All four buffers are device memory of the
@@ -104,7 +109,8 @@ int64_t kv_ring_v_offset(int64_t slot, int32_t channel, int32_t head_dim);
 int kv_ring_rope_table(float *host_out, int64_t n_pos, int32_t head_dim, double base);
 
 /* Workspace bytes for `op` (KV_RING_OP_*) with n = new tokens (write), unused (delta
- * rotate) or nq = queries (attention).  Returns 0 for an unknown op or invalid shape. */
+ * rotate), nq = queries (attention) or the larger of the two (write + attention).  Returns 0
+ * for an unknown op or invalid shape. */
 size_t kv_ring_workspace_bytes(int32_t op, int32_t heads, int32_t slots, int32_t head_dim,
                                int32_t n);
 
@@ -154,6 +160,24 @@ int ring_attention(const kv_ring_desc *ring, int32_t ring_head, int32_t filled, 
                    int32_t nq, int64_t q_pos0, const float *rope_table, int64_t rope_n_pos,
                    float softmax_scale, void *out, float *lse, void *workspace,
                    size_t workspace_bytes, void *stream);
+
+/*
+ * One layer call of the method (abstract: in each of the 240 calls per chunk the new tokens
+ * enter the cache and the new queries attend over it): exactly kv_ring_write(ring, k_new,
+ * v_new, n, start_slot, pos0, ...) followed on the same stream by ring_attention(ring,
+ * ring_head, filled, q, nq, q_pos0, ...), with ring_head and filled the ring's state after the
+ * write.  Same results bit for bit; one launch fewer, because the queries' per-head absmax runs
+ * in the same launch as the write's K and V absmax.
+ *   workspace  kv_ring_workspace_bytes(KV_RING_OP_WRITE_ATTEND, heads, slots, head_dim,
+ *              max(n, nq)) bytes, 16-byte aligned.
+ * nq == 0 makes it the write alone (q, out, lse unused).
+ * Errors: those of the two calls (all checked before anything is enqueued).
+ */
+int kv_ring_write_attend(const kv_ring_desc *ring, const void *k_new, const void *v_new, int32_t n,
+                         int32_t start_slot, int64_t pos0, int32_t ring_head, int32_t filled,
+                         const void *q, int32_t nq, int64_t q_pos0, const float *rope_table,
+                         int64_t rope_n_pos, float softmax_scale, void *out, float *lse,
+                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * The E4M3 encoder the kernels use, exposed so it can be checked exhaustively: out[i] =

@@ -68,7 +68,7 @@ def test_sizes(kv):
     assert kv.codes_bytes(24, 5788, 128) == 24 * 46 * 128 * 128
     assert kv.codes_bytes(1, 64, 64) == 128 * 64
     assert kv.codes_bytes(0, 64, 64) == 0 and kv.codes_bytes(1, 64, 96) == 0
-    for op in (kv.OP_WRITE, kv.OP_DELTA_ROTATE, kv.OP_ATTENTION):
+    for op in (kv.OP_WRITE, kv.OP_DELTA_ROTATE, kv.OP_ATTENTION, kv.OP_WRITE_ATTEND):
         assert kv.workspace_bytes(op, 24, 5788, 128, 757) > 0
         assert kv.workspace_bytes(op, 24, 5788, 128, 757) % 4 == 0
     assert kv.workspace_bytes(99, 24, 5788, 128, 757) == 0
@@ -130,6 +130,27 @@ def test_argument_errors_are_reported_before_any_launch(kv):
     assert L.kv_ring_fp8_encode(F + 4, F, 5, None) == -2
     assert L.kv_ring_fp8_encode(F, F, 0, None) == 0
     assert L.kv_ring_rope_table(None, 10, 64, 10000.0) == -1
+    # write + attention in one call: the checks of both
+    wf = kv.workspace_bytes(kv.OP_WRITE_ATTEND, 2, 64, 64, 16)
+    assert wf >= ws + wa - 16
+    def wa_call(*, desc=good, k=F, n=16, start=0, pos0=0, head=16, filled=16, q=F, nq=16, qpos=0,
+                ntab=128, scale=0.125, out=F, lse=F, wsp=F, wsb=wf):
+        return L.kv_ring_write_attend(d(desc), k, F, n, start, pos0, head, filled, q, nq, qpos, F, ntab,
+                                      scale, out, lse, wsp, wsb, None)
+    assert wa_call(k=None) == -1
+    assert wa_call(k=F + 2) == -2
+    assert wa_call(n=0) == -4
+    assert wa_call(start=64) == -4
+    assert wa_call(pos0=120) == -5
+    assert wa_call(head=64) == -4
+    assert wa_call(filled=65) == -4
+    assert wa_call(nq=-1) == -4
+    assert wa_call(q=None) == -1
+    assert wa_call(out=F + 2) == -2
+    assert wa_call(qpos=113) == -5
+    assert wa_call(scale=0.0) == -4
+    assert wa_call(wsb=wf - 4) == -6
+    assert wa_call(desc=_Desc(F, F, F, F, 2, 64, 96)) == -3
     # window copy of the read-time baseline (src, dst, fresh: 10 rows of 64 bytes each)
     S0, D0, N0 = F, F + (1 << 16), F + (2 << 16)
     assert L.kv_window_advance(S0, D0, N0, 0, 0, 64, None) == -4

@@ -406,3 +406,43 @@ def test_layer_calls_replay_from_a_captured_graph(kv, torch):
         for a, b in zip(got, eager):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep} differs"
         _ = (q[0].float() * 2).sum().item()   # eager work between replays
+
+
+# ------------------------------------------------------------------ fused layer call
+
+@pytest.mark.parametrize("heads,slots,d,n,nq,writes", [
+    (24, 5788, 128, 757, 757, 8),    # the steady-state layer call (the last write wraps)
+    (3, 700, 128, 16, 129, 5),       # more queries than new tokens
+    (2, 300, 64, 100, 1, 4),
+    (2, 300, 128, 77, 0, 2),         # no queries: the write alone
+])
+def test_write_attend_equals_write_then_attention(kv, torch, heads, slots, d, n, nq, writes):
+    """kv_ring_write_attend leaves the same ring bytes, outputs and LSE, bit for bit, as
+    kv_ring_write followed by ring_attention."""
+    tab_dev, _ = tables(kv, torch, d)
+    rings = [kv.Ring(heads, slots, d), kv.Ring(heads, slots, d)]
+    filled = 0
+    for c in range(writes - 1):
+        kk = to_dev_bf16(normal_bf16(tensor_seed("fused", c, 1), (n, heads, d)))
+        vv = to_dev_bf16(normal_bf16(tensor_seed("fused", c, 2), (n, heads, d)))
+        for r in rings:
+            kv.kv_ring_write(r, kk, vv, (c * n) % slots, c * n, tab_dev)
+        filled = min(filled + n, slots)
+    c = writes - 1
+    start, pos0 = (c * n) % slots, c * n
+    head, filled = oracle.advance(start, n, filled, slots)
+    kk = to_dev_bf16(normal_bf16(tensor_seed("fused", c, 1), (n, heads, d)))
+    vv = to_dev_bf16(normal_bf16(tensor_seed("fused", c, 2), (n, heads, d)))
+    q = to_dev_bf16(normal_bf16(tensor_seed("fused", c, 0), (nq, heads, d)))
+    q_pos0 = pos0 + n - nq if nq <= pos0 + n else 0
+    kv.kv_ring_write(rings[0], kk, vv, start, pos0, tab_dev)
+    o1, l1 = kv.ring_attention(rings[0], head, filled, q, q_pos0, tab_dev, 1 / math.sqrt(d))
+    o2, l2 = kv.kv_ring_write_attend(rings[1], kk, vv, start, pos0, head, filled, q, q_pos0, tab_dev,
+                                     1 / math.sqrt(d))
+    torch.cuda.synchronize()
+    for a, b in ((rings[0].k, rings[1].k), (rings[0].v, rings[1].v),
+                 (rings[0].k_scale, rings[1].k_scale), (rings[0].v_scale, rings[1].v_scale)):
+        assert torch.equal(a, b)
+    if nq:
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+        assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
