@@ -160,7 +160,7 @@ def main() -> int:
     log(f"step as two calls: {sep_ms * 1000:.1f} us GPU")
 
     # ---------------------------------------------------------------- attention kernel alone
-    reps = max(50, args.steps // 2)
+    reps = max(50, args.steps // 2) // 2 * 2
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     calls = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for b, a in evs:        # torch creates the HIP event on its first record(); the library then
@@ -183,26 +183,27 @@ def main() -> int:
     log(f"attention kernel {att_us:.1f} us ({att_tflops:.0f} TFLOP/s), whole call {call_us:.1f} us")
 
     # ---------------------------------------------------------------- write alone
-    wev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    # back to back between two events, like the steps: the throughput of repeated writes
     for _ in range(5):
         kv.kv_ring_write(ring, k_new, v_new, start, pos0, tab, workspace=ws_w, stream=stream)
-    for b, a in wev:
-        b.record(stream)
+    e0.record(stream)
+    for _ in range(reps):
         kv.kv_ring_write(ring, k_new, v_new, start, pos0, tab, workspace=ws_w, stream=stream)
-        a.record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
-    write_us = 1000.0 * sum(b.elapsed_time(a) for b, a in wev) / reps
+    write_us = 1000.0 * e0.elapsed_time(e1) / reps
     write_gbps = WRITE_BYTES / (write_us * 1e-6) / 1e9
     log(f"write {write_us:.1f} us ({write_gbps:.0f} GB/s)")
 
     # ---------------------------------------------------------------- delta rotation of one ring
-    rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for i, (b, a) in enumerate(rev):
-        b.record(stream)
+    for i in range(4):
         kv.kv_ring_delta_rotate(ring, head, filled, -4000 if i % 2 == 0 else 4000, workspace=ws_r, stream=stream)
-        a.record(stream)
+    e0.record(stream)
+    for i in range(reps):   # +-4000 alternate, so positions stay within range
+        kv.kv_ring_delta_rotate(ring, head, filled, -4000 if i % 2 == 0 else 4000, workspace=ws_r, stream=stream)
+    e1.record(stream)
     torch.cuda.synchronize()
-    rot_us = 1000.0 * sum(b.elapsed_time(a) for b, a in rev) / reps
+    rot_us = 1000.0 * e0.elapsed_time(e1) / reps
     rot_gbps = ROTATE_BYTES / (rot_us * 1e-6) / 1e9
     log(f"delta rotate {rot_us:.1f} us ({rot_gbps:.0f} GB/s)")
 
@@ -238,13 +239,12 @@ def main() -> int:
         torch.cuda.synchronize()
         rt_call_us = 1000.0 * e0.elapsed_time(e1) / reps
         # the maintenance part alone (copies + whole-window write), timed like the write above
-        mev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for i, (mb, ma) in enumerate(mev):
-            mb.record(stream)
+        e0.record(stream)
+        for i in range(reps):
             rt_maintain(i)
-            ma.record(stream)
+        e1.record(stream)
         torch.cuda.synchronize()
-        rt_maint_us = 1000.0 * sum(b.elapsed_time(a) for b, a in mev) / reps
+        rt_maint_us = 1000.0 * e0.elapsed_time(e1) / reps
         wt_call_us = gpu_ms * 1000.0      # the timed steps: write + attention, back to back
         read_time = {
             "call_us": round(rt_call_us, 2), "maintenance_us": round(rt_maint_us, 2),

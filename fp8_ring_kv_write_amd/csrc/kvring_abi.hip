@@ -135,10 +135,18 @@ int kv_ring_delta_rotate(const kv_ring_desc* ring, int32_t ring_head, int32_t fi
   st = check_workspace(workspace, workspace_bytes,
                        kv_ring_workspace_bytes(KV_RING_OP_DELTA_ROTATE, ring->heads, ring->slots, ring->head_dim, 0));
   if (st) return st;
+  // theta_i depends only on (head_dim, base): kept per thread between calls
+  thread_local int32_t theta_dim = 0;
+  thread_local double theta_base = 0.0, theta[64];
+  if (theta_dim != ring->head_dim || theta_base != rope_base) {
+    for (int32_t i = 0; i < ring->head_dim / 2; ++i) theta[i] = rope_theta(i, ring->head_dim, rope_base);
+    theta_dim = ring->head_dim;
+    theta_base = rope_base;
+  }
   kvring::DeltaTable tab;
   std::memset(&tab, 0, sizeof(tab));
   for (int32_t i = 0; i < ring->head_dim / 2; ++i) {
-    const double ang = (double)delta * rope_theta(i, ring->head_dim, rope_base);
+    const double ang = (double)delta * theta[i];
     tab.cs[i][0] = (float)std::cos(ang);
     tab.cs[i][1] = (float)std::sin(ang);
   }
