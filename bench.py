@@ -18,6 +18,10 @@ Also reported (one JSON line on stdout; progress on stderr):
   delta_rotate kv_ring_delta_rotate of one full ring (36.67 MB algorithmic: K codes and
               scales read and written);
   chunk       240 (write + attention) calls over 60 rings, 4 passes, as one chunk;
+  cold_cache  write, delta rotation and step timed one call at a time after a 512 MB buffer is
+              rewritten (the infinity cache no longer holds the ring, as between two calls of
+              one layer in a 60-layer model);
+  write_sweep kv_ring_write time and GB/s over the token count (32 .. 5,788);
   read_time_baseline  the design the ring replaces, with the same kernels: per call the linear
               bfloat16 window is copied forward by the new tokens (kv_window_advance), rotated
               and quantised whole (kv_ring_write of all 5,788 tokens), then attended; its
@@ -67,6 +71,8 @@ def main() -> int:
     ap.add_argument("--no-chunk", action="store_true", help="skip the 240-call chunk measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-read-time", action="store_true", help="skip the read-time baseline")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timings")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the write-size sweep")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="also run one plain device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
@@ -83,6 +89,7 @@ def main() -> int:
     from workloads import normal_bf16, tensor_seed, steady_ring_schedule
 
     dev = torch.device("cuda:0")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -126,6 +133,24 @@ def main() -> int:
         kv.kv_ring_write_attend(ring, k_new, v_new, start, pos0, head, filled, q, pos0, tab, scale,
                                 out=out, lse=lse, workspace=ws_f, stream=stream)
 
+    def graph_us(fn, n_calls):
+        """GPU time per call of fn(i) for i < n_calls, captured once in a HIP graph and replayed
+        (no host work between the calls: the time the GPU needs, not the time Python needs to
+        issue them)."""
+        fn(0)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n_calls):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return 1000.0 * e0.elapsed_time(e1) / n_calls
+
     def step_separate():
         kv.kv_ring_write(ring, k_new, v_new, start, pos0, tab, workspace=ws_w, stream=stream)
         kv.ring_attention(ring, head, filled, q, pos0, tab, scale, out=out, lse=lse, workspace=ws_a,
@@ -136,7 +161,6 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     log(f"timing {args.steps} steps")
     t0 = time.perf_counter()
     e0.record(stream)
@@ -192,8 +216,9 @@ def main() -> int:
     e1.record(stream)
     torch.cuda.synchronize()
     write_us = 1000.0 * e0.elapsed_time(e1) / reps
-    write_gbps = WRITE_BYTES / (write_us * 1e-6) / 1e9
-    log(f"write {write_us:.1f} us ({write_gbps:.0f} GB/s)")
+    write_gpu_us = graph_us(lambda i: kv.kv_ring_write(ring, k_new, v_new, start, pos0, tab, workspace=ws_w), 50)
+    write_gbps = WRITE_BYTES / (write_gpu_us * 1e-6) / 1e9
+    log(f"write {write_gpu_us:.1f} us GPU ({write_gbps:.0f} GB/s), {write_us:.1f} us per call issued from Python")
 
     # ---------------------------------------------------------------- delta rotation of one ring
     for i in range(4):
@@ -204,8 +229,62 @@ def main() -> int:
     e1.record(stream)
     torch.cuda.synchronize()
     rot_us = 1000.0 * e0.elapsed_time(e1) / reps
-    rot_gbps = ROTATE_BYTES / (rot_us * 1e-6) / 1e9
-    log(f"delta rotate {rot_us:.1f} us ({rot_gbps:.0f} GB/s)")
+    rot_gpu_us = graph_us(lambda i: kv.kv_ring_delta_rotate(ring, head, filled, -4000 if i % 2 == 0 else 4000,
+                                                            workspace=ws_r), 50)
+    rot_gbps = ROTATE_BYTES / (rot_gpu_us * 1e-6) / 1e9
+    log(f"delta rotate {rot_gpu_us:.1f} us GPU ({rot_gbps:.0f} GB/s), {rot_us:.1f} us per call issued from Python")
+
+    # ---------------------------------------------------------------- cold caches
+    # Between two calls on the same layer a model runs every other layer, whose rings (60 x 36 MB)
+    # push this one out of the 256 MB infinity cache.  Here a 512 MB buffer is rewritten before
+    # each timed call to the same effect; each call is then timed alone with events around it.
+    cold = None
+    if not args.no_cold:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cold_reps = 20
+
+        def timed_cold(fn):
+            tot = 0.0
+            for i in range(cold_reps):
+                flush.fill_(i & 0xFF)
+                b, a = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                b.record(stream)
+                fn(i)
+                a.record(stream)
+                torch.cuda.synchronize()
+                tot += b.elapsed_time(a)
+            return 1000.0 * tot / cold_reps
+
+        c_write = timed_cold(lambda i: kv.kv_ring_write(ring, k_new, v_new, start, pos0, tab, workspace=ws_w,
+                                                        stream=stream))
+        c_rot = timed_cold(lambda i: kv.kv_ring_delta_rotate(ring, head, filled, -4000 if i % 2 == 0 else 4000,
+                                                             workspace=ws_r, stream=stream))
+        c_step = timed_cold(lambda i: step())
+        cold = {"write_us": round(c_write, 2), "write_GBps": round(WRITE_BYTES / (c_write * 1e-6) / 1e9, 1),
+                "delta_rotate_us": round(c_rot, 2),
+                "delta_rotate_GBps": round(ROTATE_BYTES / (c_rot * 1e-6) / 1e9, 1),
+                "step_us": round(c_step, 2), "calls": cold_reps}
+        log(f"cold caches: write {c_write:.1f} us, delta rotate {c_rot:.1f} us, step {c_step:.1f} us")
+        del flush
+
+    # ---------------------------------------------------------------- write sizes
+    # the write is latency-bound at 757 tokens: its time over the token count
+    sweep = None
+    if not args.no_sweep:
+        sweep = []
+        for n_tok in (32, 128, 757, 1514, 2894, 5788):
+            kk = to_dev(normal_bf16(tensor_seed("sweep", n_tok, 1), (n_tok, H, D)))
+            vv = to_dev(normal_bf16(tensor_seed("sweep", n_tok, 2), (n_tok, H, D)))
+            wsn = torch.empty(kv.workspace_bytes(kv.OP_WRITE, H, S, D, n_tok), dtype=torch.uint8, device=dev)
+            us = graph_us(lambda i: kv.kv_ring_write(ring, kk, vv, 0, 0, tab, workspace=wsn), 20)
+            nbytes = n_tok * H * D * (2 * 2 + 2) + 2 * n_tok * H * 4
+            sweep.append({"tokens": n_tok, "us": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)})
+        log("write sweep: " + ", ".join(f"{w['tokens']}: {w['us']:.1f} us ({w['GBps']:.0f} GB/s)" for w in sweep))
+        # the ring was overwritten: restore the steady state the later measurements expect
+        for c, w in enumerate(sched):
+            kv.kv_ring_write(ring, to_dev(normal_bf16(tensor_seed("single_call", c, 1), (N, H, D))),
+                             to_dev(normal_bf16(tensor_seed("single_call", c, 2), (N, H, D))),
+                             w.start_slot, w.pos0, tab)
 
     # ---------------------------------------------------------------- read-time baseline
     # The design the ring replaces: a linear bfloat16 window copied forward by the new tokens,
@@ -220,9 +299,9 @@ def main() -> int:
 
         def rt_maintain(i):
             src, dst = win[i % 2], win[(i + 1) % 2]
-            kv.kv_window_advance(src[0], dst[0], k_new, stream=stream)
-            kv.kv_window_advance(src[1], dst[1], v_new, stream=stream)
-            kv.kv_ring_write(rt_ring, dst[0], dst[1], 0, w_pos0, tab, workspace=ws_rt, stream=stream)
+            kv.kv_window_advance(src[0], dst[0], k_new)        # on torch's current stream
+            kv.kv_window_advance(src[1], dst[1], v_new)
+            kv.kv_ring_write(rt_ring, dst[0], dst[1], 0, w_pos0, tab, workspace=ws_rt)
 
         def rt_call(i):
             rt_maintain(i)
@@ -239,23 +318,18 @@ def main() -> int:
         torch.cuda.synchronize()
         rt_call_us = 1000.0 * e0.elapsed_time(e1) / reps
         # the maintenance part alone (copies + whole-window write), timed like the write above
-        e0.record(stream)
-        for i in range(reps):
-            rt_maintain(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        rt_maint_us = 1000.0 * e0.elapsed_time(e1) / reps
+        rt_maint_us = graph_us(rt_maintain, 20)
         wt_call_us = gpu_ms * 1000.0      # the timed steps: write + attention, back to back
         read_time = {
             "call_us": round(rt_call_us, 2), "maintenance_us": round(rt_maint_us, 2),
-            "write_time_call_us": round(wt_call_us, 2), "write_time_maintenance_us": round(write_us, 2),
-            "maintenance_speedup": round(rt_maint_us / write_us, 2),
+            "write_time_call_us": round(wt_call_us, 2), "write_time_maintenance_us": round(write_gpu_us, 2),
+            "maintenance_speedup": round(rt_maint_us / write_gpu_us, 2),
             "call_speedup": round(rt_call_us / wt_call_us, 3),
             "chunk_maintenance_ms": {"read_time": round(240 * rt_maint_us / 1000, 2),
-                                     "write_time": round(240 * write_us / 1000, 2)},
+                                     "write_time": round(240 * write_gpu_us / 1000, 2)},
         }
         log(f"read-time call {rt_call_us:.1f} us (maintenance {rt_maint_us:.1f} us) vs write-time "
-            f"{wt_call_us:.1f} us (maintenance {write_us:.1f} us)")
+            f"{wt_call_us:.1f} us (maintenance {write_gpu_us:.1f} us)")
         del win, rt_ring, ws_rt
 
     # ---------------------------------------------------------------- a 240-call chunk over 60 rings
@@ -339,11 +413,15 @@ def main() -> int:
         "attention": {"kernel_us": round(att_us, 2), "call_us": round(call_us, 2),
                       "tflops": round(att_tflops, 1), "frac_fp8_peak": round(att_tflops / FP8_PEAK_TFLOPS, 4),
                       "calls_per_s": round(1e6 / call_us, 1)},
-        "write": {"us": round(write_us, 2), "GBps": round(write_gbps, 1),
-                  "frac_hbm_peak": round(write_gbps / HBM_PEAK_GBPS, 4), "bytes": WRITE_BYTES},
-        "delta_rotate": {"us": round(rot_us, 2), "GBps": round(rot_gbps, 1),
-                         "frac_hbm_peak": round(rot_gbps / HBM_PEAK_GBPS, 4), "bytes": ROTATE_BYTES},
+        "write": {"us": round(write_gpu_us, 2), "GBps": round(write_gbps, 1),
+                  "frac_hbm_peak": round(write_gbps / HBM_PEAK_GBPS, 4), "bytes": WRITE_BYTES,
+                  "issued_us": round(write_us, 2)},
+        "delta_rotate": {"us": round(rot_gpu_us, 2), "GBps": round(rot_gbps, 1),
+                         "frac_hbm_peak": round(rot_gbps / HBM_PEAK_GBPS, 4), "bytes": ROTATE_BYTES,
+                         "issued_us": round(rot_us, 2)},
         "chunk": chunk,
+        "cold_cache": cold,
+        "write_sweep": sweep,
         "read_time_baseline": read_time,
         "roofline": {"bound": "mfma", "achieved": round(att_tflops, 1), "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(att_tflops / FP8_PEAK_TFLOPS, 4),

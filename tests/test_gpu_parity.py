@@ -446,3 +446,26 @@ def test_write_attend_equals_write_then_attention(kv, torch, heads, slots, d, n,
     if nq:
         assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
         assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+
+
+# ------------------------------------------------------------------ more shapes
+
+def test_single_slot_ring(kv, torch):
+    """A ring of one slot: every write replaces it, the attention has one valid key."""
+    p = Pair(kv, torch, 2, 1, 128)
+    for c in range(3):
+        p.write(normal_bf16(tensor_seed("one_slot", c, 1), (1, 2, 128)),
+                normal_bf16(tensor_seed("one_slot", c, 2), (1, 2, 128)), 0, c)
+        p.assert_same(f"write {c}")
+    assert (p.head, p.filled) == (0, 1)
+    q = normal_bf16(tensor_seed("one_slot", 9, 0), (3, 2, 128))
+    check_attention(*p.attend(q, 0, 1 / math.sqrt(128)), label="one slot")
+
+
+def test_attention_head_dim_64_full_size(kv, torch):
+    """The steady-state call with head_dim 64: 757 queries over a full 5,788-slot ring, 24 heads."""
+    p = Pair(kv, torch, 24, 5788, 64)
+    sched = _fill_steady(p, "d64_full", 757, 8)
+    p.assert_same("steady ring d64")
+    q = normal_bf16(tensor_seed("d64_full", 99, 0), (757, 24, 64))
+    check_attention(*p.attend(q, sched[-1].pos0, 1 / math.sqrt(64)), label="d64 single call")
