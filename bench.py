@@ -53,8 +53,8 @@ ATT_KERNEL = "attn_stream<128>"
 # (FETCH_SIZE, WRITE_SIZE) over this workload, each divided by the factor the same counter
 # reads for a torch copy of --calibrate-copy bytes.  Valid only for the kernel sources whose
 # hash is recorded; reported as null otherwise.
-ATT_TRAFFIC = {"sources": "61b23e069a89d8ab", "bytes": 167_220_000,
-               "read_bytes": 141_660_000, "write_bytes": 25_560_000}
+ATT_TRAFFIC = {"sources": "151528635ddef32a", "bytes": 166_830_000,
+               "read_bytes": 141_270_000, "write_bytes": 25_560_000}
 WRITE_BYTES = 2 * N * H * D * 2 + 2 * N * H * D + 2 * N * H * 4
 ROTATE_BYTES = 2 * (H * S * D + H * S * 4)
 
@@ -72,6 +72,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-read-time", action="store_true", help="skip the read-time baseline")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timings")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time repeated calls as issued from Python only (no graph replays; for profilers)")
     ap.add_argument("--no-sweep", action="store_true", help="skip the write-size sweep")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="also run one plain device copy of BYTES bytes (counter calibration)")
@@ -136,7 +138,16 @@ def main() -> int:
     def graph_us(fn, n_calls):
         """GPU time per call of fn(i) for i < n_calls, captured once in a HIP graph and replayed
         (no host work between the calls: the time the GPU needs, not the time Python needs to
-        issue them)."""
+        issue them).  With --no-graph: the calls issued back to back instead."""
+        if args.no_graph:
+            for i in range(n_calls):
+                fn(i)
+            e0.record(stream)
+            for i in range(n_calls):
+                fn(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return 1000.0 * e0.elapsed_time(e1) / n_calls
         fn(0)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
@@ -368,21 +379,24 @@ def main() -> int:
         torch.cuda.synchronize()
         chunk_ms = (time.perf_counter() - t0) * 1000.0 / reps_c
         # the same 480 library calls captured once in a HIP graph and replayed
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            run_chunk()                   # the capture stream is torch's current stream here
-        torch.cuda.synchronize()
-        graph.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(reps_c):
+        graph_ms = None
+        if not args.no_graph:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                run_chunk()               # the capture stream is torch's current stream here
+            torch.cuda.synchronize()
             graph.replay()
-        torch.cuda.synchronize()
-        graph_ms = (time.perf_counter() - t0) * 1000.0 / reps_c
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(reps_c):
+                graph.replay()
+            torch.cuda.synchronize()
+            graph_ms = round((time.perf_counter() - t0) * 1000.0 / reps_c, 3)
+            del graph
         chunk = {"calls": passes * layers, "layers": layers, "passes": passes, "ms": round(chunk_ms, 3),
-                 "graph_ms": round(graph_ms, 3)}
-        log(f"chunk of 240 calls: {chunk_ms:.2f} ms eager, {graph_ms:.2f} ms as one graph")
-        del inputs, rings, graph
+                 "graph_ms": graph_ms}
+        log(f"chunk of 240 calls: {chunk_ms:.2f} ms eager, {graph_ms} ms as one graph")
+        del inputs, rings
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
