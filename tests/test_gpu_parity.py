@@ -469,3 +469,12 @@ def test_attention_head_dim_64_full_size(kv, torch):
     p.assert_same("steady ring d64")
     q = normal_bf16(tensor_seed("d64_full", 99, 0), (757, 24, 64))
     check_attention(*p.attend(q, sched[-1].pos0, 1 / math.sqrt(64)), label="d64 single call")
+
+
+def test_attention_more_rows_than_work_groups(kv, torch):
+    """1,500 queries x 24 heads = 288 rows of 128 queries, more rows than the 256 work-groups of
+    the persistent grid, over a partly filled ring that wraps."""
+    p = Pair(kv, torch, 24, 700, 128)
+    sched = _fill_steady(p, "many_rows", 150, 6)     # 900 tokens: wraps, ring full
+    q = normal_bf16(tensor_seed("many_rows", 9, 0), (1500, 24, 128))
+    check_attention(*p.attend(q, 0, 1 / math.sqrt(128)), label="288 rows")
