@@ -13,6 +13,8 @@
 // Arithmetic is float32 with every product and sum rounded separately (the translation
 // unit is compiled with -ffp-contract=off) so the codes match the CPU oracle bit for bit.
 
+#include <cstring>
+
 #include "kvring_common.hpp"
 #include "kvring_internal.hpp"
 
@@ -110,18 +112,46 @@ struct WriteGeom {
   int64_t pos0;
 };
 
-// Pass 2.  grid = (chunks touched by the write, heads).
+struct WriteArgs {
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const float* partial;   // pass-1 partials [2][heads][groups]
+  uint8_t* kc;
+  uint8_t* vc;
+  float* k_scale;
+  float* v_scale;
+  WriteGeom g;
+  int32_t blocks;         // work-groups of the write (chunks touched); 0: no write
+};
+
+// The attention's queries, quantised once per call: rotated at their positions and encoded with
+// the head's scale, stored in the order the attention's QK product takes them as its B operand
+// (per 128-query row: wavefront w, lane 16g + li -> query 16w + li, channels 32g .. 32g+31).
+struct QuantQArgs {
+  const uint16_t* q;      // bfloat16 [nq][heads][D]
+  const float* partial;   // [heads][groups]: the queries' absmax partials from pass 1
+  uint8_t* codes;         // [heads * qtiles][8][64][32]
+  float* scale;           // [heads]
+  int64_t pos0;
+  int32_t nq, groups, qtiles;
+  int32_t blocks;         // 2 * qtiles (a work-group takes 64 queries of a row); 0: none
+};
+
+// Pass 2 of the write: one aligned 32-slot chunk of the ring x one head.
 template <int D>
-__global__ __launch_bounds__(kThreads) void write_quantize(
-    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
-    const float* __restrict__ rope, const float* __restrict__ partial, WriteGeom g,
-    uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, float* __restrict__ k_scale,
-    float* __restrict__ v_scale) {
+__device__ inline void write_chunk(const WriteArgs& wa, const float* __restrict__ rope, int blk, int h) {
   constexpr int CPT = D / 8;
   __shared__ float red[2][4];
   __shared__ __align__(16) uint8_t vlds[kChunk][D];
-  const int h = blockIdx.y;
-  const int chunk = blockIdx.x < g.n_chunks_a ? g.chunk_a0 + blockIdx.x : blockIdx.x - g.n_chunks_a;
+  const WriteGeom& g = wa.g;
+  const uint16_t* __restrict__ k_new = wa.k_new;
+  const uint16_t* __restrict__ v_new = wa.v_new;
+  const float* __restrict__ partial = wa.partial;
+  uint8_t* __restrict__ kc = wa.kc;
+  uint8_t* __restrict__ vc = wa.vc;
+  float* __restrict__ k_scale = wa.k_scale;
+  float* __restrict__ v_scale = wa.v_scale;
+  const int chunk = blk < g.n_chunks_a ? g.chunk_a0 + blk : blk - g.n_chunks_a;
 
   // this thread's inputs first (they do not depend on the scales), so that their latency
   // overlaps the reduction of the partials
@@ -219,6 +249,66 @@ __global__ __launch_bounds__(kThreads) void write_quantize(
   }
 }
 
+// Query quantisation: half a row (64 queries) of one head.  Thread -> (wavefront w of the
+// attention's row, lane): the 32 bytes that lane holds as its QK operand.
+template <int D>
+__device__ inline void quantize_q_half(const QuantQArgs& qa_, const float* __restrict__ rope, int blk,
+                                       int h, int heads) {
+  __shared__ float red[4];
+  const int qt = blk >> 1, w = 4 * (blk & 1) + (int(threadIdx.x) >> 6);
+  const int lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
+  const int i = qt * 128 + w * 16 + li;
+  const bool live = i < qa_.nq && (D == 128 || g < 2);
+  uint4 raw[4];
+  float4 tab[8];
+  if (live) {   // inputs first: their latency overlaps the reduction below
+    const uint4* src = reinterpret_cast<const uint4*>(qa_.q + ((int64_t)i * heads + h) * D + 32 * g);
+    const float4* t4 = reinterpret_cast<const float4*>(rope + ((qa_.pos0 + i) * (D / 2) + 16 * g) * 2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) raw[j] = src[j];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tab[j] = t4[j];
+  }
+  float a = 0.0f;
+  for (int j = threadIdx.x; j < qa_.groups; j += kThreads) a = __builtin_fmaxf(a, qa_.partial[(int64_t)h * qa_.groups + j]);
+  a = block_max_256(a, red);
+  float scale, inv;
+  scale_from_absmax(a, scale, inv);
+  if (blk == 0 && threadIdx.x == 0) qa_.scale[h] = scale;
+  uint32_t wd[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (live) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {   // 8 channels (4 pairs) per step
+      const uint32_t bw[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+      const float4 t0 = tab[2 * j], t1 = tab[2 * j + 1];
+      const float cs[4][2] = {{t0.x, t0.y}, {t0.z, t0.w}, {t1.x, t1.y}, {t1.z, t1.w}};
+      float y[8];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float xe = __uint_as_float(bw[p] << 16), xo = __uint_as_float(bw[p] & 0xFFFF0000u);
+        y[2 * p] = (xe * cs[p][0] - xo * cs[p][1]) * inv;
+        y[2 * p + 1] = (xe * cs[p][1] + xo * cs[p][0]) * inv;
+      }
+      wd[2 * j] = e4m3x4(y[0], y[1], y[2], y[3]);
+      wd[2 * j + 1] = e4m3x4(y[4], y[5], y[6], y[7]);
+    }
+  }
+  uint4* dst = reinterpret_cast<uint4*>(qa_.codes + ((((int64_t)h * qa_.qtiles + qt) * 8 + w) * 64 + lane) * 32);
+  dst[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+  dst[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
+}
+
+// Pass 2: grid = (write blocks + query blocks, heads); each work-group does one or the other.
+template <int D>
+__global__ __launch_bounds__(kThreads) void quantize_pass(WriteArgs wa, QuantQArgs qa_,
+                                                          const float* __restrict__ rope, int32_t heads) {
+  const int h = blockIdx.y;
+  if ((int)blockIdx.x < wa.blocks)
+    write_chunk<D>(wa, rope, blockIdx.x, h);
+  else
+    quantize_q_half<D>(qa_, rope, blockIdx.x - wa.blocks, h, heads);
+}
+
 }  // namespace
 
 int64_t write_workspace_floats(int32_t heads, int32_t n) {
@@ -252,19 +342,26 @@ AbsmaxJob absmax_job(const uint16_t* x, int32_t n, bool rotate, int64_t pos0, fl
 
 }  // namespace
 
-// Write pass 2 (pass 1's K and V partials are in ws).
-hipError_t launch_write_quantize(const kv_ring_desc& r, const uint16_t* k_new, const uint16_t* v_new,
-                                 int32_t n, int32_t start_slot, int64_t pos0, const float* rope,
-                                 float* ws, hipStream_t stream) {
-  const int ngroups = (n + kChunk - 1) / kChunk;
-  WriteGeom g;
+namespace {
+
+WriteArgs write_args(const kv_ring_desc& r, const uint16_t* k_new, const uint16_t* v_new, int32_t n,
+                     int32_t start_slot, int64_t pos0, float* ws) {
+  WriteArgs wa;
+  wa.k_new = k_new;
+  wa.v_new = v_new;
+  wa.partial = ws;
+  wa.kc = r.k;
+  wa.vc = r.v;
+  wa.k_scale = r.k_scale;
+  wa.v_scale = r.v_scale;
+  WriteGeom& g = wa.g;
   g.n = n;
   g.start = start_slot;
   g.slots = r.slots;
   g.heads = r.heads;
   g.tiles = tile_count(r.slots);
   g.pos0 = pos0;
-  g.n_partial_groups = ngroups;
+  g.n_partial_groups = (n + kChunk - 1) / kChunk;
   const int end_a = start_slot + n < r.slots ? start_slot + n : r.slots;
   g.chunk_a0 = start_slot / kChunk;
   g.n_chunks_a = (end_a - 1) / kChunk - g.chunk_a0 + 1;
@@ -276,15 +373,48 @@ hipError_t launch_write_quantize(const kv_ring_desc& r, const uint16_t* k_new, c
     // handled once, by the first run's work-group
     if ((end_b - 1) / kChunk == g.chunk_a0) n_chunks_b -= 1;
   }
-  dim3 g2(g.n_chunks_a + n_chunks_b, r.heads);
-  if (r.head_dim == 128)
-    hipLaunchKernelGGL(write_quantize<128>, g2, dim3(kThreads), 0, stream, k_new, v_new, rope, ws,
-                       g, r.k, r.v, r.k_scale, r.v_scale);
+  wa.blocks = g.n_chunks_a + n_chunks_b;
+  return wa;
+}
+
+QuantQArgs quant_q_args(const uint16_t* q, int32_t nq, int64_t q_pos0, const float* q_partial,
+                        uint8_t* codes, float* scale) {
+  QuantQArgs qa_;
+  qa_.q = q;
+  qa_.partial = q_partial;
+  qa_.codes = codes;
+  qa_.scale = scale;
+  qa_.pos0 = q_pos0;
+  qa_.nq = nq;
+  qa_.groups = (nq + kChunk - 1) / kChunk;
+  qa_.qtiles = (nq + 127) / 128;
+  qa_.blocks = 2 * qa_.qtiles;
+  return qa_;
+}
+
+hipError_t launch_quantize_pass(const WriteArgs& wa, const QuantQArgs& qa_, const float* rope,
+                                int32_t heads, int32_t head_dim, hipStream_t stream) {
+  dim3 g2(wa.blocks + qa_.blocks, heads);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(quantize_pass<128>, g2, dim3(kThreads), 0, stream, wa, qa_, rope, heads);
   else
-    hipLaunchKernelGGL(write_quantize<64>, g2, dim3(kThreads), 0, stream, k_new, v_new, rope, ws,
-                       g, r.k, r.v, r.k_scale, r.v_scale);
+    hipLaunchKernelGGL(quantize_pass<64>, g2, dim3(kThreads), 0, stream, wa, qa_, rope, heads);
   return hipGetLastError();
 }
+
+WriteArgs no_write() {
+  WriteArgs wa;
+  std::memset(&wa, 0, sizeof(wa));
+  return wa;
+}
+
+QuantQArgs no_queries() {
+  QuantQArgs qa_;
+  std::memset(&qa_, 0, sizeof(qa_));
+  return qa_;
+}
+
+}  // namespace
 
 hipError_t launch_write(const kv_ring_desc& r, const uint16_t* k_new, const uint16_t* v_new,
                         int32_t n, int32_t start_slot, int64_t pos0, const float* rope,
@@ -296,25 +426,27 @@ hipError_t launch_write(const kv_ring_desc& r, const uint16_t* k_new, const uint
   jobs.job[2] = jobs.job[1];
   hipError_t e = launch_absmax(jobs, 2, r.heads, r.head_dim, rope, stream);
   if (e != hipSuccess) return e;
-  return launch_write_quantize(r, k_new, v_new, n, start_slot, pos0, rope, ws, stream);
+  return launch_quantize_pass(write_args(r, k_new, v_new, n, start_slot, pos0, ws), no_queries(), rope,
+                              r.heads, r.head_dim, stream);
 }
 
-// Queries' partials for the attention: [heads][ceil(nq/32)] at `partial`.
-hipError_t launch_q_absmax(const uint16_t* q, int32_t nq, int32_t heads, int32_t head_dim,
-                           int64_t q_pos0, const float* rope, float* partial, hipStream_t stream) {
+hipError_t launch_q_prep(const uint16_t* q, int32_t nq, int32_t heads, int32_t head_dim,
+                         int64_t q_pos0, const float* rope, float* q_partial, uint8_t* codes,
+                         float* scale, hipStream_t stream) {
   AbsmaxJobs jobs;
-  jobs.job[0] = absmax_job(q, nq, true, q_pos0, partial);
+  jobs.job[0] = absmax_job(q, nq, true, q_pos0, q_partial);
   jobs.job[1] = jobs.job[2] = jobs.job[0];
-  return launch_absmax(jobs, 1, heads, head_dim, rope, stream);
+  hipError_t e = launch_absmax(jobs, 1, heads, head_dim, rope, stream);
+  if (e != hipSuccess) return e;
+  return launch_quantize_pass(no_write(), quant_q_args(q, nq, q_pos0, q_partial, codes, scale), rope,
+                              heads, head_dim, stream);
 }
 
-// Write followed by attention: K, V and Q partials in one launch, then the write's second pass;
-// the attention (launched by the caller) finds its query partials at q_partial.
-hipError_t launch_write_and_q_absmax(const kv_ring_desc& r, const uint16_t* k_new,
-                                     const uint16_t* v_new, int32_t n, int32_t start_slot,
-                                     int64_t pos0, const uint16_t* q, int32_t nq, int64_t q_pos0,
-                                     const float* rope, float* ws, float* q_partial,
-                                     hipStream_t stream) {
+hipError_t launch_write_and_q_prep(const kv_ring_desc& r, const uint16_t* k_new,
+                                   const uint16_t* v_new, int32_t n, int32_t start_slot,
+                                   int64_t pos0, const uint16_t* q, int32_t nq, int64_t q_pos0,
+                                   const float* rope, float* ws, float* q_partial, uint8_t* codes,
+                                   float* scale, hipStream_t stream) {
   const int ngroups = (n + kChunk - 1) / kChunk;
   AbsmaxJobs jobs;
   jobs.job[0] = absmax_job(k_new, n, true, pos0, ws);
@@ -322,7 +454,9 @@ hipError_t launch_write_and_q_absmax(const kv_ring_desc& r, const uint16_t* k_ne
   jobs.job[2] = absmax_job(q, nq, true, q_pos0, q_partial);
   hipError_t e = launch_absmax(jobs, 3, r.heads, r.head_dim, rope, stream);
   if (e != hipSuccess) return e;
-  return launch_write_quantize(r, k_new, v_new, n, start_slot, pos0, rope, ws, stream);
+  return launch_quantize_pass(write_args(r, k_new, v_new, n, start_slot, pos0, ws),
+                              quant_q_args(q, nq, q_pos0, q_partial, codes, scale), rope, r.heads,
+                              r.head_dim, stream);
 }
 
 }  // namespace kvring

@@ -208,9 +208,11 @@ int kv_ring_write_attend(const kv_ring_desc* ring, const void* k_new, const void
   const auto* vn = static_cast<const uint16_t*>(v_new);
   if (nq == 0)
     return status_of(kvring::launch_write(*ring, kn, vn, n, start_slot, pos0, rope_table, ws, s));
-  hipError_t e = kvring::launch_write_and_q_absmax(*ring, kn, vn, n, start_slot, pos0,
-                                                   static_cast<const uint16_t*>(q), nq, q_pos0,
-                                                   rope_table, ws, ws_att, s);
+  const kvring::AttnWorkspace aw =
+      kvring::attention_workspace(ws_att, ring->heads, ring->slots, ring->head_dim, nq);
+  hipError_t e = kvring::launch_write_and_q_prep(*ring, kn, vn, n, start_slot, pos0,
+                                                 static_cast<const uint16_t*>(q), nq, q_pos0,
+                                                 rope_table, ws, aw.q_partial, aw.q_codes, aw.q_scale, s);
   if (e != hipSuccess) return KV_RING_ERR_LAUNCH;
   return status_of(kvring::launch_attention(*ring, ring_head, filled, static_cast<const uint16_t*>(q), nq,
                                             q_pos0, rope_table, softmax_scale, static_cast<uint16_t*>(out),

@@ -14,7 +14,6 @@ namespace kvring {
 int64_t write_workspace_floats(int32_t heads, int32_t n);
 int64_t rotate_workspace_floats(int32_t heads, int32_t slots);
 int64_t attention_workspace_floats(int32_t heads, int32_t slots, int32_t head_dim, int32_t nq);
-int attention_splits(int32_t heads, int32_t slots, int32_t nq);
 
 hipError_t launch_write(const kv_ring_desc& r, const uint16_t* k_new, const uint16_t* v_new,
                         int32_t n, int32_t start_slot, int64_t pos0, const float* rope,
@@ -27,21 +26,37 @@ struct DeltaTable {  // cos/sin of delta * theta_i for i < head_dim/2, float32
 hipError_t launch_delta_rotate(const kv_ring_desc& r, int32_t ring_head, int32_t filled,
                                const DeltaTable& tab, float* ws, hipStream_t stream);
 
-// The attention's workspace starts with the queries' absmax partials ([heads][ceil(nq/32)]);
-// with q_partials_ready an earlier launch on the stream has written them and the attention
-// does not compute them again.
+// The attention's workspace: the queries' absmax partials, the split rows' partial results, and
+// the queries quantised for the QK product with their per-head scales.
+struct AttnWorkspace {
+  float* q_partial;   // [heads][ceil(nq/32)]
+  float* part_o;      // [rows][8][128][head_dim]
+  float* part_ml;     // [rows][8][128][2]
+  uint8_t* q_codes;   // [heads * ceil(nq/128)][8][64][32]
+  float* q_scale;     // [heads]
+};
+AttnWorkspace attention_workspace(float* ws, int32_t heads, int32_t slots, int32_t head_dim,
+                                  int32_t nq);
+
+// With q_ready an earlier launch on the stream has written the quantised queries (and scales)
+// into the workspace; otherwise the attention prepares them first (two launches).
 hipError_t launch_attention(const kv_ring_desc& r, int32_t ring_head, int32_t filled,
                             const uint16_t* q, int32_t nq, int64_t q_pos0, const float* rope,
                             float softmax_scale, uint16_t* out, float* lse, float* ws,
-                            bool q_partials_ready, hipStream_t stream);
+                            bool q_ready, hipStream_t stream);
 
-// Write pass 1 for K, V and the queries in one launch, then write pass 2; the queries'
-// partials go to q_partial (the start of the attention's workspace).
-hipError_t launch_write_and_q_absmax(const kv_ring_desc& r, const uint16_t* k_new,
-                                     const uint16_t* v_new, int32_t n, int32_t start_slot,
-                                     int64_t pos0, const uint16_t* q, int32_t nq, int64_t q_pos0,
-                                     const float* rope, float* ws, float* q_partial,
-                                     hipStream_t stream);
+// Query preparation: absmax partials, then rotation and quantisation (two launches).
+hipError_t launch_q_prep(const uint16_t* q, int32_t nq, int32_t heads, int32_t head_dim,
+                         int64_t q_pos0, const float* rope, float* q_partial, uint8_t* codes,
+                         float* scale, hipStream_t stream);
+
+// Write followed by the query preparation, sharing both launches: pass 1 for K, V and the
+// queries, then pass 2 (the write's quantisation and the queries').
+hipError_t launch_write_and_q_prep(const kv_ring_desc& r, const uint16_t* k_new,
+                                   const uint16_t* v_new, int32_t n, int32_t start_slot,
+                                   int64_t pos0, const uint16_t* q, int32_t nq, int64_t q_pos0,
+                                   const float* rope, float* ws, float* q_partial, uint8_t* codes,
+                                   float* scale, hipStream_t stream);
 
 void set_attention_events(void* before, void* after);
 

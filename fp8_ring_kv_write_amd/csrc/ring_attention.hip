@@ -39,9 +39,6 @@
 
 namespace kvring {
 
-hipError_t launch_q_absmax(const uint16_t* q, int32_t nq, int32_t heads, int32_t head_dim,
-                           int64_t q_pos0, const float* rope, float* partial, hipStream_t stream);
-
 namespace {
 
 constexpr int kWaves = 8;               // 2 wavefronts per SIMD
@@ -58,17 +55,15 @@ struct AttnArgs {
   const uint8_t* vc;
   const float* k_scale;
   const float* v_scale;
-  const uint16_t* q;
-  const float* rope;
-  const float* q_partial;  // [heads][n_qgroups]
+  const uint8_t* q_codes;  // quantised queries: per row [8 wavefronts][64 lanes][32 bytes]
+  const float* q_scale;    // [heads]
   uint16_t* out;
   float* lse;
   float* part_o;           // [rows][max_seg][kRowQ][D]
   float* part_ml;          // [rows][max_seg][kRowQ][2]
   int64_t tiles;           // ring tiles per head
-  int64_t q_pos0;
   int64_t units;           // rows * tv
-  int32_t heads, slots, ring_head, filled, nq, n_qgroups;
+  int32_t heads, slots, ring_head, filled, nq;
   int32_t qtiles, rows, tv, grid, max_seg;
   int32_t first1, n1, first2;  // valid tiles: logical k < n1 -> first1 + k, else first2 + k - n1
   float score_scale;           // softmax_scale * log2(e)
@@ -87,7 +82,8 @@ struct Smem {
   float (&iv)[kBufs][kTile];   // per slot: 1 / v_scale (valid) or 0
   int (&eg)[kBufs][4];         // exponent of the largest valid v_scale per 32 slots (-128: none)
   int (&uni)[kBufs][2];        // per 64 slots: all valid, one K scale and one V scale (1) or not
-  float (&red)[kWaves];
+  uint8_t (&q)[kRowQ * 128];   // the row's quantised queries (QK operands, 32 bytes per lane)
+  float (&qs)[4];              // the head's query scale
 };
 
 __device__ inline v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c, int scale_b) {
@@ -196,7 +192,7 @@ __device__ inline void issue_v(const AttnArgs& a, Smem<D>& sm, int b, int64_t t,
 }
 
 // Wait until at most n of this thread's vector-memory operations are outstanding (they complete
-// in issue order).  n is one of the per-step copy counts (0 .. 2*kLoads + 1).
+// in issue order).  n is one of the per-step copy counts (0 .. 2*kLoads + 2).
 __device__ inline void wait_vm(int n) {
   switch (n) {   // s_waitcnt immediate: vmcnt in bits 3:0, expcnt and lgkmcnt left at their maximum
     case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
@@ -204,7 +200,9 @@ __device__ inline void wait_vm(int n) {
     case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
     case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
     case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F77); break;
   }
 }
 
@@ -445,8 +443,9 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
   __shared__ __align__(16) float s_iv[kBufs][kTile];
   __shared__ __align__(16) int s_eg[kBufs][4];
   __shared__ __align__(16) int s_uni[kBufs][2];
-  __shared__ float s_red[kWaves];
-  Smem<D> sm{s_k, s_v, s_ks, s_vs, s_ck, s_nb, s_iv, s_eg, s_uni, s_red};
+  __shared__ __align__(16) uint8_t s_q[kRowQ * 128];
+  __shared__ __align__(16) float s_qs[4];
+  Smem<D> sm{s_k, s_v, s_ks, s_vs, s_ck, s_nb, s_iv, s_eg, s_uni, s_q, s_qs};
 
   const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);   // wavefront (uniform)
 
@@ -465,7 +464,6 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
   const LaneOffs lo = lane_offsets<D>(lane);
 
   while (ub < ue) {
-    const bool g_live = (D == 128) || (g < 2);
     const int row = int(ub / a.tv);
     const int k0 = int(ub % a.tv);
     const int k1 = int(min<int64_t>(a.tv, k0 + (ue - ub)));
@@ -480,57 +478,32 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
     //   K tile j (+ scales) -> K buffer j % 3, issued in step j-3, needed from step j-1 on;
     //   V tile j            -> V buffer j % 3, issued in step j-1, needed in step j+1.
     // Each copy has two steps to land; a step waits only for the copies issued two steps back.
+    // The row's quantised queries (16 KB, 32 bytes per lane) and the head's query scale are
+    // copied first, then K tiles 0 and 1, so that one memory round trip covers all of them.
+    {
+      const uint8_t* qbase = a.q_codes + (int64_t)row * (kRowQ * 128);   // uniform
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        copy16(qbase, uint32_t(((j * kWaves + w) * 64 + lane) * 16), &sm.q[(j * kWaves + w) * 1024]);
+      if (w == 0 && lane == 0) copy4(a.q_scale, uint32_t(head) * 4u, &sm.qs[0]);
+    }
     issue_k<D>(a, sm, co, 0, phys(k0), head, w, lane);
     if (nt > 1) issue_k<D>(a, sm, co, 1, phys(k0 + 1), head, w, lane);
     const int nk = CopyOffs<D>::kLoads + 1, nv = CopyOffs<D>::kLoads;
 
-    // ---- query scale of the head, then this wavefront's quantised queries
-    float qa = 0.0f;
-    for (int j = tid; j < a.n_qgroups; j += kThreads)
-      qa = __builtin_fmaxf(qa, a.q_partial[(int64_t)head * a.n_qgroups + j]);
-    for (int off = 32; off > 0; off >>= 1) qa = __builtin_fmaxf(qa, __shfl_xor(qa, off, 64));
-    if (lane == 0) sm.red[w] = qa;
     // the PV of the first step reads "tile -1" from the last V buffer: zeros
     {
       uint4* vz = reinterpret_cast<uint4*>(sm.v[kBufs - 1]);
       for (int c = tid; c < D * kTile / 16; c += kThreads) vz[c] = make_uint4(0, 0, 0, 0);
     }
+    wait_vm(nt > 1 ? 2 * nk : nk);   // this thread's query copies have landed (K tiles may not)
     lds_sync();
-    qa = sm.red[0];
-#pragma unroll
-    for (int j = 1; j < kWaves; ++j) qa = __builtin_fmaxf(qa, sm.red[j]);
-    float q_scale, q_inv;
-    scale_from_absmax(qa, q_scale, q_inv);
-    const float c0 = a.score_scale * q_scale;
-
+    const float c0 = a.score_scale * sm.qs[0];
     v8i qop;
     {
-      const int i = qt * kRowQ + w * 16 + li;
-      uint32_t wd[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (i < a.nq && g_live) {
-        const uint16_t* src = a.q + ((int64_t)i * a.heads + head) * D + 32 * g;
-        const float* tab = a.rope + ((a.q_pos0 + i) * (D / 2) + 16 * g) * 2;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {   // 8 channels (4 pairs) per step
-          const uint4 bq = reinterpret_cast<const uint4*>(src)[j];
-          const float4 t0 = reinterpret_cast<const float4*>(tab)[2 * j];
-          const float4 t1 = reinterpret_cast<const float4*>(tab)[2 * j + 1];
-          const uint32_t bw[4] = {bq.x, bq.y, bq.z, bq.w};
-          const float cs[4][2] = {{t0.x, t0.y}, {t0.z, t0.w}, {t1.x, t1.y}, {t1.z, t1.w}};
-          float y[8];
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const float xe = __uint_as_float(bw[p] << 16), xo = __uint_as_float(bw[p] & 0xFFFF0000u);
-            const float cc = cs[p][0], ss = cs[p][1];
-            y[2 * p] = (xe * cc - xo * ss) * q_inv;
-            y[2 * p + 1] = (xe * ss + xo * cc) * q_inv;
-          }
-          wd[2 * j] = e4m3x4(y[0], y[1], y[2], y[3]);
-          wd[2 * j + 1] = e4m3x4(y[4], y[5], y[6], y[7]);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) qop[j] = int(wd[j]);
+      const uint4 x0 = *reinterpret_cast<const uint4*>(&sm.q[(w * 64 + lane) * 32]);
+      const uint4 x1 = *reinterpret_cast<const uint4*>(&sm.q[(w * 64 + lane) * 32 + 16]);
+      qop = v8i{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
     }
 
     RowState<D> st;
@@ -760,42 +733,69 @@ void set_attention_events(void* before, void* after) {
   g_ev_after = static_cast<hipEvent_t>(after);
 }
 
-int attention_splits(int32_t heads, int32_t slots, int32_t nq) {
-  return make_plan(heads, slots, nq, 0, slots, kMaxGrid).max_seg;
+namespace {
+
+// Workspace layout (floats, each part 16-byte aligned): query absmax partials | split rows'
+// partial outputs | their (m, l) | quantised queries | query scales.  Sized for the largest plan
+// any (ring_head, filled) and any grid <= 256 can produce (<= 8 segments per row).
+struct WsLayout {
+  int64_t q_partial, part_o, part_ml, q_codes, q_scale, total;
+};
+
+WsLayout ws_layout(int32_t heads, int32_t slots, int32_t head_dim, int32_t nq) {
+  auto up4 = [](int64_t x) { return (x + 3) / 4 * 4; };
+  const Plan p = make_plan(heads, slots, nq, 0, slots, kMaxGrid);
+  WsLayout l;
+  l.q_partial = 0;
+  l.part_o = l.q_partial + up4((int64_t)heads * ((nq + 31) / 32));
+  l.part_ml = l.part_o + (int64_t)p.rows * 8 * kRowQ * head_dim;
+  l.q_codes = l.part_ml + (int64_t)p.rows * 8 * kRowQ * 2;
+  l.q_scale = l.q_codes + (int64_t)p.rows * (kRowQ * 128) / 4;
+  l.total = l.q_scale + up4(heads);
+  return l;
 }
 
-// Workspace: q partials | partial O | partial (m, l), each 16-byte aligned.  Sized for the
-// largest plan any (ring_head, filled) and any grid <= 256 can produce (<= 8 segments per row).
+}  // namespace
+
 int64_t attention_workspace_floats(int32_t heads, int32_t slots, int32_t head_dim, int32_t nq) {
-  const int64_t qparts = ((int64_t)heads * ((nq + 31) / 32) + 3) / 4 * 4;
-  const Plan p = make_plan(heads, slots, nq, 0, slots, kMaxGrid);
-  const int64_t po = (int64_t)p.rows * 8 * kRowQ * head_dim;
-  const int64_t pml = (int64_t)p.rows * 8 * kRowQ * 2;
-  return qparts + po + pml;
+  return ws_layout(heads, slots, head_dim, nq).total;
+}
+
+AttnWorkspace attention_workspace(float* ws, int32_t heads, int32_t slots, int32_t head_dim,
+                                  int32_t nq) {
+  const WsLayout l = ws_layout(heads, slots, head_dim, nq);
+  AttnWorkspace w;
+  w.q_partial = ws + l.q_partial;
+  w.part_o = ws + l.part_o;
+  w.part_ml = ws + l.part_ml;
+  w.q_codes = reinterpret_cast<uint8_t*>(ws + l.q_codes);
+  w.q_scale = ws + l.q_scale;
+  return w;
 }
 
 hipError_t launch_attention(const kv_ring_desc& r, int32_t ring_head, int32_t filled,
                             const uint16_t* q, int32_t nq, int64_t q_pos0, const float* rope,
                             float softmax_scale, uint16_t* out, float* lse, float* ws,
-                            bool q_partials_ready, hipStream_t stream) {
+                            bool q_ready, hipStream_t stream) {
   const Plan p = make_plan(r.heads, r.slots, nq, ring_head, filled, device_cus());
+  const AttnWorkspace aw = attention_workspace(ws, r.heads, r.slots, r.head_dim, nq);
   AttnArgs a;
   a.kc = r.k;
   a.vc = r.v;
   a.k_scale = r.k_scale;
   a.v_scale = r.v_scale;
-  a.q = q;
-  a.rope = rope;
+  a.q_codes = aw.q_codes;
+  a.q_scale = aw.q_scale;
   a.out = out;
   a.lse = lse;
+  a.part_o = aw.part_o;
+  a.part_ml = aw.part_ml;
   a.tiles = tile_count(r.slots);
-  a.q_pos0 = q_pos0;
   a.heads = r.heads;
   a.slots = r.slots;
   a.ring_head = ring_head;
   a.filled = filled;
   a.nq = nq;
-  a.n_qgroups = (nq + 31) / 32;
   a.qtiles = p.qtiles;
   a.rows = p.rows;
   a.tv = p.tv;
@@ -806,14 +806,10 @@ hipError_t launch_attention(const kv_ring_desc& r, int32_t ring_head, int32_t fi
   a.n1 = p.n1;
   a.first2 = p.first2;
   a.score_scale = softmax_scale * kLog2e;
-  const int64_t qparts = ((int64_t)r.heads * a.n_qgroups + 3) / 4 * 4;
-  a.q_partial = ws;
-  a.part_o = ws + qparts;
-  a.part_ml = a.part_o + (int64_t)p.rows * 8 * kRowQ * r.head_dim;
 
   hipError_t e = hipSuccess;
-  if (!q_partials_ready) {   // else an earlier launch on this stream left them at ws
-    e = launch_q_absmax(q, nq, r.heads, r.head_dim, q_pos0, rope, ws, stream);
+  if (!q_ready) {   // else an earlier launch on this stream wrote them
+    e = launch_q_prep(q, nq, r.heads, r.head_dim, q_pos0, rope, aw.q_partial, aw.q_codes, aw.q_scale, stream);
     if (e != hipSuccess) return e;
   }
   if (g_ev_before && g_ev_after) {
