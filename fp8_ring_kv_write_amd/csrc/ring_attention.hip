@@ -7,8 +7,9 @@
 //   1. rope_absmax_partials (shared with the write): per-(head, 32-query group) max |RoPE(q)|;
 //   2. attn_stream: a persistent grid of one 8-wavefront work-group per compute unit.  The work
 //      is the set of units (row, tile), a row being 128 queries of one head and a tile 128 ring
-//      slots; each work-group takes an equal contiguous range of units, so a row may be split
-//      between work-groups.  A row held by one work-group is finished in place; the segments of
+//      slots; each work-group takes a contiguous range of units of equal weight (a tile weighs
+//      one, the start of a row's segment kSegCost more), so a row may be split between
+//      work-groups.  A row held by one work-group is finished in place; the segments of
 //      a split row store unnormalised partial results.  Consecutive work-groups of one XCD get
 //      consecutive units, so the rows of one head share that XCD's L2;
 //   3. attn_combine: log-sum-exp merge of the split rows (skipped when no row is split).  Doing
@@ -46,6 +47,7 @@ constexpr int kThreads = 64 * kWaves;   // 512
 constexpr int kRowQ = 16 * kWaves;      // 128 queries per row, 16 per wavefront
 constexpr int kBufs = 3;                // LDS buffers per operand (see attn_stream's schedule)
 constexpr int kMaxGrid = 256;
+constexpr int kSegCost = 2;             // weight of a segment start in tiles (UnitSplit)
 constexpr float kTau = 4.0f;            // lazy rescale threshold, log2 units
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -63,10 +65,33 @@ struct AttnArgs {
   float* part_ml;          // [rows][max_seg][kRowQ][2]
   int64_t tiles;           // ring tiles per head
   int64_t units;           // rows * tv
+  int64_t cost;            // rows * (tv + seg_cost): the partition's total weight
+  int32_t seg_cost;        // weight of a segment start, in tiles (see UnitSplit)
   int32_t heads, slots, ring_head, filled, nq;
   int32_t qtiles, rows, tv, grid, max_seg;
   int32_t first1, n1, first2;  // valid tiles: logical k < n1 -> first1 + k, else first2 + k - n1
   float score_scale;           // softmax_scale * log2(e)
+};
+
+// Partition of the units (row, tile) among the work-groups, by weight rather than by count: a
+// work-group whose range starts a row pays a second segment start (the end of one row's
+// segment, the quantised queries and first tiles of the next) -- measured at about two tiles of
+// work -- so every row start weighs seg_cost tiles on top of its tv tiles.  Unit u of row r at
+// tile k sits at weight position r * (tv + seg_cost) + seg_cost + k; virtual work-group v takes
+// the units whose position falls in [v * cost / grid, (v + 1) * cost / grid).
+struct UnitSplit {
+  int64_t tv, c, cost;
+  int grid;
+  __host__ __device__ int64_t pos(int64_t u) const { return (u / tv) * (tv + c) + c + u % tv; }
+  // first unit at or after weight position x
+  __host__ __device__ int64_t first_unit(int64_t x) const {
+    const int64_t r = x / (tv + c), o = x % (tv + c);
+    return r * tv + (o > c ? o - c : 0);
+  }
+  __host__ __device__ int64_t begin(int v) const { return first_unit((int64_t)v * cost / grid); }
+  __host__ __device__ int owner(int64_t u) const {   // virtual work-group holding unit u
+    return int(((pos(u) + 1) * grid + cost - 1) / cost) - 1;
+  }
 };
 
 // LDS of a work-group.  Each array is its own LDS object, so that the compiler can tell reads of
@@ -453,11 +478,10 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
   // XCDs round-robin), so that neighbouring units share an L2
   const int wg = blockIdx.x;
   const int v = (a.grid % 8 == 0) ? (wg % 8) * (a.grid / 8) + wg / 8 : wg;
-  auto owner = [&](int64_t u) -> int {   // virtual work-group holding unit u
-    return int(((u + 1) * a.grid + a.units - 1) / a.units) - 1;
-  };
-  int64_t ub = (int64_t)v * a.units / a.grid;
-  const int64_t ue = (int64_t)(v + 1) * a.units / a.grid;
+  const UnitSplit split{a.tv, a.seg_cost, a.cost, a.grid};
+  auto owner = [&](int64_t u) -> int { return split.owner(u); };
+  int64_t ub = split.begin(v);
+  const int64_t ue = split.begin(v + 1);
   const int tid = int(threadIdx.x);
   const int lane = tid & 63, g = lane >> 4, li = lane & 15;
   const CopyOffs<D> co = copy_offsets<D>(w, lane);
@@ -626,7 +650,8 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
   const int row = blockIdx.y;
-  const auto owner = [&](int64_t u) -> int { return int(((u + 1) * a.grid + a.units - 1) / a.units) - 1; };
+  const UnitSplit split{a.tv, a.seg_cost, a.cost, a.grid};
+  const auto owner = [&](int64_t u) -> int { return split.owner(u); };
   const int first = owner((int64_t)row * a.tv);
   const int nseg = owner((int64_t)row * a.tv + a.tv - 1) - first + 1;
   if (nseg <= 1) return;
@@ -661,8 +686,8 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
 }
 
 struct Plan {
-  int qtiles, rows, tv, grid, max_seg, first1, n1, first2;
-  int64_t units;
+  int qtiles, rows, tv, grid, max_seg, first1, n1, first2, seg_cost;
+  int64_t units, cost;
 };
 
 int device_cus() {
@@ -708,16 +733,19 @@ Plan make_plan(int32_t heads, int32_t slots, int32_t nq, int32_t ring_head, int3
     p.tv = 0;
   }
   p.units = (int64_t)p.rows * p.tv;
-  // every work-group takes at least ceil(tv / 7) units, so that at most 8 share a row
+  p.seg_cost = p.tv >= 8 ? kSegCost : 0;
+  const int64_t span = (int64_t)p.tv + p.seg_cost;   // weight of a row
+  p.cost = (int64_t)p.rows * span;
+  // every work-group takes a weight of at least ceil(span / 7), so that at most 8 share a row
   int64_t g = grid_cap < kMaxGrid ? grid_cap : kMaxGrid;
   if (p.tv > 0) {
-    const int64_t min_units = (p.tv + 6) / 7;
-    if (g > p.units / min_units) g = p.units / min_units;
+    const int64_t min_w = (span + 6) / 7;
+    if (g > p.cost / min_w) g = p.cost / min_w;
   }
   p.grid = int(g < 1 ? 1 : g);
-  // a row of tv units spans at most ceil(tv / floor(units / grid)) + 1 work-groups
-  const int64_t per = p.units / p.grid;
-  p.max_seg = p.units > 0 ? int((p.tv + per - 1) / per) + 1 : 1;
+  // a row of weight span is shared by at most ceil(span / floor(cost / grid)) + 1 work-groups
+  const int64_t per = p.cost / p.grid;
+  p.max_seg = p.units > 0 ? int((span + per - 1) / per) + 1 : 1;
   if (p.max_seg > 8) p.max_seg = 8;
   return p;
 }
@@ -800,6 +828,8 @@ hipError_t launch_attention(const kv_ring_desc& r, int32_t ring_head, int32_t fi
   a.rows = p.rows;
   a.tv = p.tv;
   a.units = p.units;
+  a.cost = p.cost;
+  a.seg_cost = p.seg_cost;
   a.grid = p.grid;
   a.max_seg = p.max_seg;
   a.first1 = p.first1;
@@ -819,6 +849,8 @@ hipError_t launch_attention(const kv_ring_desc& r, int32_t ring_head, int32_t fi
   if (p.tv == 0) {
     // empty ring: every row is a single segment with no tiles -> zeros and -inf
     a.units = p.rows;
+    a.cost = p.rows;
+    a.seg_cost = 0;
     a.tv = 1;
     a.n1 = 0;
     a.grid = p.rows < kMaxGrid ? p.rows : kMaxGrid;
@@ -832,8 +864,8 @@ hipError_t launch_attention(const kv_ring_desc& r, int32_t ring_head, int32_t fi
   if (e != hipSuccess) return e;
   bool split = false;   // does any row span more than one work-group?
   for (int row = 0; row < p.rows && !split; ++row) {
-    const auto owner = [&](int64_t u) { return ((u + 1) * a.grid + a.units - 1) / a.units - 1; };
-    split = owner((int64_t)row * a.tv + a.tv - 1) != owner((int64_t)row * a.tv);
+    const UnitSplit us{a.tv, a.seg_cost, a.cost, a.grid};
+    split = us.owner((int64_t)row * a.tv + a.tv - 1) != us.owner((int64_t)row * a.tv);
   }
   if (!split) return e;
   dim3 gc((kRowQ * r.head_dim / 4 + 255) / 256, p.rows);
