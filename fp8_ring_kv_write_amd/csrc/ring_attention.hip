@@ -106,7 +106,7 @@ struct Smem {
   float (&nb)[kBufs][kTile];   // per slot: log2(v_scale) (valid) or -inf
   float (&iv)[kBufs][kTile];   // per slot: 1 / v_scale (valid) or 0
   int (&eg)[kBufs][4];         // exponent of the largest valid v_scale per 32 slots (-128: none)
-  int (&uni)[kBufs][2];        // per 64 slots: all valid, one K scale and one V scale (1) or not
+  int (&uni)[kBufs][4];        // per 32 slots: all valid, one K scale and one V scale (1) or not
   uint8_t (&q)[kRowQ * 128];   // the row's quantised queries (QK operands, 32 bytes per lane)
   float (&qs)[4];              // the head's query scale
 };
@@ -236,35 +236,47 @@ __device__ inline void wait_vm(int n) {
 // for the asynchronous tile copies in flight (their completion is tracked with wait_vm).
 __device__ inline void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Max over the 16 lanes of each row of a wavefront (every lane receives it): data-parallel
+// moves between lanes (DPP), no trip through LDS.
+__device__ inline uint32_t row_max16(uint32_t m) {
+  m = max(m, uint32_t(__builtin_amdgcn_update_dpp(int(m), int(m), 0xB1, 0xF, 0xF, false)));   // lane ^ 1
+  m = max(m, uint32_t(__builtin_amdgcn_update_dpp(int(m), int(m), 0x4E, 0xF, 0xF, false)));   // lane ^ 2
+  m = max(m, uint32_t(__builtin_amdgcn_update_dpp(int(m), int(m), 0x141, 0xF, 0xF, false)));  // 7 - lane (of 8)
+  m = max(m, uint32_t(__builtin_amdgcn_update_dpp(int(m), int(m), 0x140, 0xF, 0xF, false)));  // 15 - lane (of 16)
+  return m;
+}
+
 // Per-slot factors of the tile in K buffer b, and zeroed K bytes for its invalid slots (so that
-// whatever they hold -- NaN codes included -- never reaches a product).  Wavefronts 0 and 1
-// take one slot per lane; the zeroing is shared by all.  With vmax = f * 2^e (f in [0.5, 1)) the
-// largest valid V scale of the tile, the probabilities enter the PV product as
-// P * v_scale * 2^-e <= P, and the product's B-operand scale multiplies back by 2^e (one
-// exponent per tile: the scale of the FP8 matrix product applies per 32-element block of its
-// contraction, and a block gathers 16-slot pieces of two lane groups).
+// whatever they hold -- NaN codes included -- never reaches a product).  Wavefronts 0-3 (one per
+// SIMD) take 32 slots each, one per lane of their first half; the zeroing is shared by all.
+// With vmax = f * 2^e (f in [0.5, 1)) the largest valid V scale of the tile, the probabilities
+// enter the PV product as P * v_scale * 2^-e <= P, and the product's B-operand scale multiplies
+// back by 2^e (one exponent per tile: the scale of the FP8 matrix product applies per 32-element
+// block of its contraction, and a block gathers 16-slot pieces of two lane groups).
 template <int D>
 __device__ inline void prep_tile(Smem<D>& sm, int b, const TileValid& tvd, float c0, int tid) {
   constexpr int NCH = D / 16;
-  if (tid < kTile) {
-    const int u = tid;
+  const int lane = tid & 63;
+  if (tid < 4 * 64 && lane < 32) {
+    const int u = (tid >> 6) * 32 + lane;
     const bool ok = tvd.has(u);
-    const float vsu = sm.vs[b][u];
-    float vmax = ok ? vsu : 0.0f;
-#pragma unroll
-    for (int off = 16; off > 0; off >>= 1) vmax = __builtin_fmaxf(vmax, __shfl_xor(vmax, off, 64));
+    const float ksu = sm.ks[b][u], vsu = sm.vs[b][u];
+    // the group's largest valid V scale (positive floats order as their bit patterns)
+    uint32_t m = row_max16(ok ? __float_as_uint(vsu) : 0u);
+    const auto sw = __builtin_amdgcn_permlane16_swap(m, m, false, false);   // rows 0 <-> 1
+    m = max(sw[0], sw[1]);
     int e = -128;
-    if (vmax > 0.0f) {
-      (void)__builtin_frexpf(vmax, &e);
+    if (m != 0u) {
+      (void)__builtin_frexpf(__uint_as_float(m), &e);
       e = max(-110, min(120, e));
     }
-    sm.ck[b][u] = ok ? c0 * sm.ks[b][u] : 0.0f;
+    sm.ck[b][u] = ok ? c0 * ksu : 0.0f;
     sm.nb[b][u] = ok ? __log2f(vsu) : -INFINITY;
-    sm.iv[b][u] = ok ? 1.0f / vsu : 0.0f;
-    if ((u & 31) == 0) sm.eg[b][u >> 5] = e;
-    const bool same = ok && sm.ks[b][u] == sm.ks[b][0] && vsu == sm.vs[b][0];
-    const bool all_same = __all(same);
-    if ((u & 63) == 0) sm.uni[b][u >> 6] = all_same ? 1 : 0;
+    sm.iv[b][u] = ok ? __builtin_amdgcn_rcpf(vsu) : 0.0f;
+    if (lane == 0) sm.eg[b][u >> 5] = e;
+    const bool same = ok && ksu == sm.ks[b][0] && vsu == sm.vs[b][0];
+    const bool all_same = __all(same);   // over this wavefront's 32 active lanes
+    if (lane == 0) sm.uni[b][u >> 5] = all_same ? 1 : 0;
   }
   if (tvd.count() < kTile) {
     uint8_t* kw = sm.k[b];
@@ -375,9 +387,9 @@ __device__ __forceinline__ void pipeline_step(const Smem<D>& sm, int bk, int bp,
 
   // ---- tile k: scores with their factors, max, rescale decision.  A uniform tile (all slots
   // valid, one K scale, one V scale) keeps its raw scores: t = raw * c + b for every slot.
-  const int2 un = *reinterpret_cast<const int2*>(&sm.uni[bk][0]);
+  const int4 un = *reinterpret_cast<const int4*>(&sm.uni[bk][0]);
   float cf = 1.0f, bf = 0.0f, tmax;
-  if (un.x & un.y) {
+  if (un.x & un.y & un.z & un.w) {
     cf = sm.ck[bk][0];
     bf = sm.nb[bk][0];
     float rmax = sc[0][0];
@@ -467,7 +479,7 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
   __shared__ __align__(16) float s_nb[kBufs][kTile];
   __shared__ __align__(16) float s_iv[kBufs][kTile];
   __shared__ __align__(16) int s_eg[kBufs][4];
-  __shared__ __align__(16) int s_uni[kBufs][2];
+  __shared__ __align__(16) int s_uni[kBufs][4];
   __shared__ __align__(16) uint8_t s_q[kRowQ * 128];
   __shared__ __align__(16) float s_qs[4];
   Smem<D> sm{s_k, s_v, s_ks, s_vs, s_ck, s_nb, s_iv, s_eg, s_uni, s_q, s_qs};
