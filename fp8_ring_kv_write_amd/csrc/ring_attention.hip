@@ -499,14 +499,15 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
   const CopyOffs<D> co = copy_offsets<D>(w, lane);
   const LaneOffs lo = lane_offsets<D>(lane);
 
+  // The first segment may start inside a row; every later one starts the next row at tile 0
+  // (and is then the row's first segment).  The 64-bit divisions happen once per work-group.
+  int row = int(ub / a.tv), k0 = int(ub % a.tv);
+  int seg = k0 > 0 ? v - owner((int64_t)row * a.tv) : 0;   // index of this segment in its row
   while (ub < ue) {
-    const int row = int(ub / a.tv);
-    const int k0 = int(ub % a.tv);
     const int k1 = int(min<int64_t>(a.tv, k0 + (ue - ub)));
     const int nt = k1 - k0;
     const int head = row / a.qtiles, qt = row % a.qtiles;
-    const int seg = v - owner((int64_t)row * a.tv);
-    const int nseg = owner((int64_t)row * a.tv + a.tv - 1) - owner((int64_t)row * a.tv) + 1;
+    const bool row_split = nt < a.tv;   // the row has other segments (in other work-groups)
     auto phys = [&](int k) -> int64_t { return k < a.n1 ? a.first1 + k : a.first2 + (k - a.n1); };
 
     // Copy schedule (j = tile index within the segment; step j forms tile j's probabilities,
@@ -626,7 +627,7 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
     float lt = st.l;
     lt += __shfl_xor(lt, 16, 64);
     lt += __shfl_xor(lt, 32, 64);
-    if (nseg > 1) {
+    if (row_split) {
       const int64_t slot0 = ((int64_t)row * a.max_seg + seg) * kRowQ;
       const int ql = w * 16 + li;
       float* po = a.part_o + (slot0 + ql) * D + 4 * g;
@@ -654,6 +655,9 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
     }
     lds_sync();   // LDS buffers are reused by the next segment
     ub += nt;
+    row += 1;
+    k0 = 0;
+    seg = 0;
   }
 }
 
