@@ -512,9 +512,12 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
 
     // Copy schedule (j = tile index within the segment; step j forms tile j's probabilities,
     // runs the PV product of tile j-1 and the QK product of tile j+1):
-    //   K tile j (+ scales) -> K buffer j % 3, issued in step j-3, needed from step j-1 on;
-    //   V tile j            -> V buffer j % 3, issued in step j-1, needed in step j+1.
-    // Each copy has two steps to land; a step waits only for the copies issued two steps back.
+    //   K tile j (+ scales) -> K buffer j % 3, issued at the end of step j-3, needed from step
+    //                          j-1 on;
+    //   V tile j            -> V buffer j % 3, issued at the end of step j-1, needed in step j+1.
+    // A step waits only for the copies issued two steps back, so each copy has a step to land.
+    // Issued after the step's products rather than before them, the copies queue in the memory
+    // pipeline while the matrix cores finish, instead of holding every wavefront at the start.
     // The row's quantised queries (16 KB, 32 bytes per lane) and the head's query scale are
     // copied first, then K tiles 0 and 1, so that one memory round trip covers all of them.
     {
@@ -579,8 +582,6 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
       wait_vm(n_prev);     // this thread's copies issued two steps back have landed:
       lds_sync();     // K tile j+1 and V tile j-1 are resident, buffers of j+3 / j+1 free
       n_prev = 0;
-      if (j + 3 < nt) { issue_k<D>(a, sm, co, (j + 3) % kBufs, phys(k0 + j + 3), head, w, lane); n_prev += nk; }
-      if (j + 1 < nt) { issue_v<D>(a, sm, bn, phys(k0 + j + 1), head, w, lane); n_prev += nv; }
       bool fix = false;    // LDS bytes changed below: barrier before the products read them
       if (j >= 1) {
         const TileValid tvp = tile_valid(phys(k0 + j - 1), a.ring_head, a.filled, a.slots);
@@ -593,6 +594,9 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
       }
       if (fix) lds_sync();
       pipeline_step<D>(sm, bk, bp, bn, g, lo, qop, sc, pprev, pcur, st);
+      // this step's copies go out behind its QK products (the buffers are free all step)
+      if (j + 3 < nt) { issue_k<D>(a, sm, co, (j + 3) % kBufs, phys(k0 + j + 3), head, w, lane); n_prev += nk; }
+      if (j + 1 < nt) { issue_v<D>(a, sm, bn, phys(k0 + j + 1), head, w, lane); n_prev += nv; }
     };
     auto final_pv = [&](int jl, const PTile& pt) {   // PV of the last tile jl
       wait_vm(0);
