@@ -478,3 +478,12 @@ def test_attention_more_rows_than_work_groups(kv, torch):
     sched = _fill_steady(p, "many_rows", 150, 6)     # 900 tokens: wraps, ring full
     q = normal_bf16(tensor_seed("many_rows", 9, 0), (1500, 24, 128))
     check_attention(*p.attend(q, 0, 1 / math.sqrt(128)), label="288 rows")
+
+
+def test_attention_many_segments_per_work_group(kv, torch):
+    """2,000 queries x 24 heads over a 2,000-slot ring: 384 rows of 16 tiles, so most work-groups
+    run two or three segments (rows) one after the other."""
+    p = Pair(kv, torch, 24, 2000, 128)
+    sched = _fill_steady(p, "many_segs", 500, 5)     # 2,500 tokens: wraps, ring full
+    q = normal_bf16(tensor_seed("many_segs", 9, 0), (2000, 24, 128))
+    check_attention(*p.attend(q, 500, 1 / math.sqrt(128)), label="384 rows of 16 tiles")
