@@ -5,9 +5,12 @@
 // Two bandwidth-bound passes, no atomics:
 //   1. rope_absmax_partials: each work-group takes 32 tokens x 1 head, rotates K, and writes
 //      the max |K'| and max |V| of its rows to a per-(tensor, head, group) partial;
-//   2. write_quantize: each work-group takes one aligned 32-slot chunk of the ring x 1 head,
-//      reduces the head's partials to the write's absmax, rotates and quantises again, and
-//      stores K codes row-major and V codes into the transposed tile layout.
+//   2. quantize_pass: each write work-group takes one aligned 32-slot chunk of the ring x 1
+//      head, reduces the head's partials to the write's absmax, rotates and quantises again,
+//      and stores K and V codes into the tile layout (V transposed).
+// The attention's queries take the same two passes (their absmax partials, then rotation and
+// quantisation in the QK product's operand order), in the same launches when the attention
+// follows a write (kv_ring_write_attend).
 // The second read of the bf16 inputs is served mostly from the L2 / infinity cache.
 //
 // Arithmetic is float32 with every product and sum rounded separately (the translation

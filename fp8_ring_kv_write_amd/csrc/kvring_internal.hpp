@@ -1,4 +1,4 @@
-// Internal launch interface between the C ABI (kvring_abi.cpp) and the kernels.
+// Internal launch interface between the C ABI (kvring_abi.hip) and the kernels.
 // Arguments have been validated by the caller; every function only enqueues work on
 // `stream` and returns the HIP status of the launches.
 #pragma once

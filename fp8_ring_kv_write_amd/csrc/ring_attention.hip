@@ -3,8 +3,11 @@
 // per chunk; cpdf.ai blog, section "Blackwell, escalabilidade e limites do decodificador":
 // FP8 attention with per-head scales).
 //
-// Three launches per call:
+// Launches per call:
 //   1. rope_absmax_partials (shared with the write): per-(head, 32-query group) max |RoPE(q)|;
+//      then quantize_pass (shared with the write): the queries rotated and encoded with their
+//      head's scale, stored in the order the QK product takes them.  kv_ring_write_attend runs
+//      both inside the write's own two launches;
 //   2. attn_stream: a persistent grid of one 8-wavefront work-group per compute unit.  The work
 //      is the set of units (row, tile), a row being 128 queries of one head and a tile 128 ring
 //      slots; each work-group takes a contiguous range of units of equal weight (a tile weighs
@@ -19,8 +22,8 @@
 // Per tile: K tile and transposed V tile are copied straight from HBM into LDS with
 // global_load_lds (16 bytes per lane; the ring stores each tile in the order the products read
 // it, so copies and operand reads are linear 1 KB wavefront accesses free of bank conflicts;
-// three buffers per operand, each copy issued two pipeline steps before it is needed).  Each
-// wavefront owns 16 queries:
+// three buffers per operand, each copy issued at the end of the step two steps before the one
+// that reads it).  Each wavefront owns 16 queries:
 //   S^T = K Q^T           8 MFMA 16x16x128 FP8 (fp32 accumulate)
 //   online softmax        log2 domain, lazily rescaled (the running max may lag the true max
 //                         by up to 2^4, so P <= 16)
