@@ -198,3 +198,14 @@ def test_lds_copies_carry_hazard_wait_states(tmp_path):
     for i in copies:
         prev = [l for l in lines[max(0, i - 3):i] if l and not l.startswith(";")]
         assert prev and prev[-1] == "s_nop 4", lines[i - 3:i + 1]
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; --gpus above 1 exits with status 2 and a message, before any
+    device is touched."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
