@@ -487,3 +487,29 @@ def test_attention_many_segments_per_work_group(kv, torch):
     sched = _fill_steady(p, "many_segs", 500, 5)     # 2,500 tokens: wraps, ring full
     q = normal_bf16(tensor_seed("many_segs", 9, 0), (2000, 24, 128))
     check_attention(*p.attend(q, 500, 1 / math.sqrt(128)), label="384 rows of 16 tiles")
+
+
+def test_chunk_passes_rewrite_the_same_slots(kv, torch):
+    """A chunk of the method on two layers: each of four denoising passes rewrites the chunk's
+    slots at the same positions and attends (through kv_ring_write_attend); the ring head moves
+    after the last pass.  Every pass's ring bytes and attention are checked against the oracle."""
+    h, s, d, n = 4, 700, 128, 100
+    tab_dev, tab = tables(kv, torch, d)
+    for layer in range(2):
+        p = Pair(kv, torch, h, s, d)
+        sched = _fill_steady(p, f"chunk{layer}", n, 6)      # 600 of 700 slots, head 600
+        start, pos0 = p.head, sched[-1].pos0 + n             # the new chunk's slots and positions
+        head, filled = oracle.advance(start, n, p.filled, s)
+        for ps in range(4):
+            k = normal_bf16(tensor_seed("chunkpass", layer, ps, 1), (n, h, d))
+            v = normal_bf16(tensor_seed("chunkpass", layer, ps, 2), (n, h, d))
+            q = normal_bf16(tensor_seed("chunkpass", layer, ps, 0), (n, h, d))
+            out, lse = kv.kv_ring_write_attend(p.g, to_dev_bf16(k), to_dev_bf16(v), start, pos0, head,
+                                               filled, to_dev_bf16(q), pos0, tab_dev, 1 / math.sqrt(d))
+            torch.cuda.synchronize()
+            oracle.ring_write(p.o, k, v, start, pos0, tab)
+            p.head, p.filled = head, filled
+            p.assert_same(f"layer {layer} pass {ps}")
+            ro, rl = oracle.ring_attention(p.o, head, filled, q, pos0, tab, 1 / math.sqrt(d))
+            check_attention(bf16_dev_to_f64(out), lse.cpu().numpy().astype(np.float64), ro, rl,
+                            label=f"layer {layer} pass {ps}")
