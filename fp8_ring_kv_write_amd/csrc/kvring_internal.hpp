@@ -30,7 +30,7 @@ hipError_t launch_delta_rotate(const kv_ring_desc& r, int32_t ring_head, int32_t
 // the queries quantised for the QK product with their per-head scales.
 struct AttnWorkspace {
   float* q_partial;   // [heads][ceil(nq/32)]
-  float* part_o;      // [rows][8][128][head_dim]
+  float* part_o;      // [rows][8][128][head_dim] halves (the split rows' normalised outputs)
   float* part_ml;     // [rows][8][128][2]
   uint8_t* q_codes;   // [heads * ceil(nq/128)][8][64][32]
   float* q_scale;     // [heads]

@@ -13,8 +13,10 @@
 //      slots; each work-group takes a contiguous range of units of equal weight (a tile weighs
 //      one, the start of a row's segment kSegCost more), so a row may be split between
 //      work-groups.  A row held by one work-group is finished in place; the segments of
-//      a split row store unnormalised partial results.  Consecutive work-groups of one XCD get
-//      consecutive units, so the rows of one head share that XCD's L2;
+//      a split row store their own output, normalised by their own sum, in half precision
+//      (a weighted mean of dequantised V rows: within 2^-11 relative), with their (max, sum).
+//      Consecutive work-groups of one XCD get consecutive units, so the rows of one head share
+//      that XCD's L2;
 //   3. attn_combine: log-sum-exp merge of the split rows (skipped when no row is split).  Doing
 //      the merge in a kernel of its own avoids device-scope fences inside attn_stream, which on
 //      this multi-XCD part write back and invalidate L2.
@@ -54,6 +56,7 @@ constexpr int kSegCost = 2;             // weight of a segment start in tiles (U
 constexpr float kTau = 4.0f;            // lazy rescale threshold, log2 units
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));   // split rows' partial outputs
 
 struct AttnArgs {
   const uint8_t* kc;
@@ -64,7 +67,7 @@ struct AttnArgs {
   const float* q_scale;    // [heads]
   uint16_t* out;
   float* lse;
-  float* part_o;           // [rows][max_seg][kRowQ][D]
+  _Float16* part_o;        // [rows][max_seg][kRowQ][D]: segment output normalised by its l
   float* part_ml;          // [rows][max_seg][kRowQ][2]
   int64_t tiles;           // ring tiles per head
   int64_t units;           // rows * tv
@@ -637,11 +640,14 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
     if (row_split) {
       const int64_t slot0 = ((int64_t)row * a.max_seg + seg) * kRowQ;
       const int ql = w * 16 + li;
-      float* po = a.part_o + (slot0 + ql) * D + 4 * g;
+      const float il = lt > 0.0f ? 1.0f / lt : 0.0f;
+      _Float16* po = a.part_o + (slot0 + ql) * D + 4 * g;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const v4f o = st.acc[db];
-        *reinterpret_cast<float4*>(po + 16 * db) = make_float4(o[0], o[1], o[2], o[3]);
+        const v4h oh = {(_Float16)(o[0] * il), (_Float16)(o[1] * il), (_Float16)(o[2] * il),
+                        (_Float16)(o[3] * il)};
+        *reinterpret_cast<v4h*>(po + 16 * db) = oh;
       }
       if (g == 0) *reinterpret_cast<float2*>(a.part_ml + (slot0 + ql) * 2) = make_float2(st.m, lt);
     } else {
@@ -691,13 +697,13 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
   if (mx != -INFINITY) {
     for (int sgi = 0; sgi < nseg; ++sgi) {
       const int64_t sl = base + (int64_t)sgi * kRowQ;
-      const float wz = __builtin_amdgcn_exp2f(a.part_ml[sl * 2] - mx);
-      l += wz * a.part_ml[sl * 2 + 1];
-      const float4 oz = *reinterpret_cast<const float4*>(a.part_o + sl * D + 4 * c4);
-      o[0] += wz * oz.x;
-      o[1] += wz * oz.y;
-      o[2] += wz * oz.z;
-      o[3] += wz * oz.w;
+      const float wz = __builtin_amdgcn_exp2f(a.part_ml[sl * 2] - mx) * a.part_ml[sl * 2 + 1];
+      l += wz;
+      const v4h oz = *reinterpret_cast<const v4h*>(a.part_o + sl * D + 4 * c4);
+      o[0] += wz * float(oz[0]);
+      o[1] += wz * float(oz[1]);
+      o[2] += wz * float(oz[2]);
+      o[3] += wz * float(oz[3]);
     }
   }
   const float il = l > 0.0f ? 1.0f / l : 0.0f;
@@ -799,7 +805,7 @@ WsLayout ws_layout(int32_t heads, int32_t slots, int32_t head_dim, int32_t nq) {
   WsLayout l;
   l.q_partial = 0;
   l.part_o = l.q_partial + up4((int64_t)heads * ((nq + 31) / 32));
-  l.part_ml = l.part_o + (int64_t)p.rows * 8 * kRowQ * head_dim;
+  l.part_ml = l.part_o + (int64_t)p.rows * 8 * kRowQ * head_dim / 2;   // half precision
   l.q_codes = l.part_ml + (int64_t)p.rows * 8 * kRowQ * 2;
   l.q_scale = l.q_codes + (int64_t)p.rows * (kRowQ * 128) / 4;
   l.total = l.q_scale + up4(heads);
@@ -839,7 +845,7 @@ hipError_t launch_attention(const kv_ring_desc& r, int32_t ring_head, int32_t fi
   a.q_scale = aw.q_scale;
   a.out = out;
   a.lse = lse;
-  a.part_o = aw.part_o;
+  a.part_o = reinterpret_cast<_Float16*>(aw.part_o);
   a.part_ml = aw.part_ml;
   a.tiles = tile_count(r.slots);
   a.heads = r.heads;
