@@ -34,8 +34,11 @@ from .kvcache import (  # noqa: F401
     quantize_per_head,
     ring_write,
     ring_delta_rotate,
+    ring_delta_rotate_3d,
+    ring_rotate_by,
     q_prep,
     ring_attention,
     SCALE_FLOOR,
 )
+from .rope3d import default_bands, band_of_pairs, rope_rows_3d, delta_cos_sin_3d  # noqa: F401
 from .window import window_advance, read_time_ring, read_time_attention  # noqa: F401

@@ -33,6 +33,7 @@ import numpy as np
 
 from .fp8 import E4M3_MAX, e4m3_decode, e4m3_encode
 from .rope import delta_cos_sin, rope_rotate
+from .rope3d import delta_cos_sin_3d
 from .ring import valid_slots, write_slots
 
 SCALE_FLOOR = np.float32(2.0 ** -100)
@@ -118,11 +119,27 @@ def ring_delta_rotate(ring: OracleRing, head: int, filled: int, delta: int,
     delta, requantise all valid slots of each head with one new per-head scale.
 
     Returns the float32 rotated keys before requantisation, [heads, filled, D]."""
+    c, s = delta_cos_sin(delta, ring.head_dim, base)
+    return ring_rotate_by(ring, head, filled, c, s)
+
+
+def ring_delta_rotate_3d(ring: OracleRing, head: int, filled: int, delta, bands=None,
+                         base: float = 10000.0) -> np.ndarray:
+    """The same steps for three-axis positions: every valid key moves by the offset triple
+    delta = (dt, dy, dx), each band of channel pairs turning by its own coordinate's offset (a
+    position reset is (dt, 0, 0)).  Returns the float32 rotated keys before requantisation."""
+    c, s = delta_cos_sin_3d(delta, ring.head_dim, bands, base)
+    return ring_rotate_by(ring, head, filled, c, s)
+
+
+def ring_rotate_by(ring: OracleRing, head: int, filled: int, c: np.ndarray,
+                   s: np.ndarray) -> np.ndarray:
+    """Dequantise every valid key, rotate pair i by the float32 (c[i], s[i]), requantise all
+    valid slots of each head with one new per-head scale (V untouched)."""
     vs = valid_slots(head, filled, ring.slots)
     if filled == 0:
         return np.zeros((ring.heads, 0, ring.head_dim), np.float32)
     k = e4m3_decode(ring.k[:, vs, :]).astype(np.float32) * ring.k_scale[:, vs, None]
-    c, s = delta_cos_sin(delta, ring.head_dim, base)
     k_rot = rope_rotate(k.astype(np.float32), c, s)              # [heads, filled, D]
     codes, scale = quantize_per_head(k_rot.transpose(1, 0, 2))  # tokens first
     ring.k[:, vs, :] = codes.transpose(1, 0, 2)

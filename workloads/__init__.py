@@ -16,6 +16,7 @@ from .gen import (  # noqa: F401
     steady_ring_schedule,
     tiny_schedule,
     outlier_channels,
+    raster_positions,
     CONFIGS,
     ROPE_POSITIONS,
 )

@@ -97,6 +97,17 @@ def tiny_schedule(slots: int = 64, n: int = 16, writes: int = 6) -> list[WriteCa
     return [WriteCall((n * w) % slots, n * w, n) for w in range(writes)]
 
 
+def raster_positions(n: int, first: int = 0, rows: int = 22, cols: int = 34,
+                     t0: int = 0) -> np.ndarray:
+    """Synthetic (frame, row, column) positions of tokens first .. first+n-1 of a raster walk
+    over frames of rows x cols tokens (column fastest, then row, then frame), the first frame
+    being t0: int32 [n, 3].  The default frame of 22 x 34 = 748 tokens is a stand-in for a
+    video latent grid; with 757-token chunks the walk runs on into the next frame."""
+    i = first + np.arange(n, dtype=np.int64)
+    per = rows * cols
+    return np.stack([t0 + i // per, (i // cols) % rows, i % cols], axis=1).astype(np.int32)
+
+
 # The five workloads, as plain data.  Sizes per one GPU's share of heads.
 CONFIGS = {
     "tiny": dict(heads=1, head_dim=64, slots=64, n=16, writes=6, rope_base=10000.0,
