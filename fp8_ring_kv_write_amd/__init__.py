@@ -19,9 +19,11 @@ from ._lib import (  # noqa: F401
     k_offset,
     v_offset,
     rope_table,
+    rope_table_3d,
     workspace_bytes,
     kv_ring_write,
     kv_ring_delta_rotate,
+    kv_ring_delta_rotate_3d,
     ring_attention,
     kv_ring_write_attend,
     fp8_encode,

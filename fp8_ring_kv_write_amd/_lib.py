@@ -51,6 +51,8 @@ def _load() -> ctypes.CDLL:
         "kv_ring_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
         "kv_ring_write": (ctypes.c_int, [dp, vp, vp, i32, i32, i64, vp, i64, vp, sz, vp]),
         "kv_ring_delta_rotate": (ctypes.c_int, [dp, i32, i32, i64, f64, vp, sz, vp]),
+        "kv_ring_rope_table_3d": (ctypes.c_int, [vp, vp, i64, i32, vp, f64]),
+        "kv_ring_delta_rotate_3d": (ctypes.c_int, [dp, i32, i32, vp, vp, f64, vp, sz, vp]),
         "ring_attention": (ctypes.c_int, [dp, i32, i32, vp, i32, i64, vp, i64, f32, vp, vp, vp, sz, vp]),
         "kv_ring_fp8_encode": (ctypes.c_int, [vp, vp, i64, vp]),
         "kv_ring_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -100,6 +102,27 @@ def rope_table(n_pos: int, head_dim: int, base: float = 10000.0) -> np.ndarray:
     """Host float32 [n_pos, head_dim/2, 2] cos/sin table filled by the library."""
     out = np.empty((n_pos, head_dim // 2, 2), dtype=np.float32)
     _check("kv_ring_rope_table", lib.kv_ring_rope_table(out.ctypes.data, n_pos, head_dim, base))
+    return out
+
+
+def _bands_arg(band_pairs):
+    """(int32 array or None, pointer): band pair counts, or NULL for the library's default."""
+    if band_pairs is None:
+        return None, None
+    b = np.ascontiguousarray(np.asarray(band_pairs, dtype=np.int32).reshape(3))
+    return b, b.ctypes.data
+
+
+def rope_table_3d(positions, head_dim: int, band_pairs=None, base: float = 10000.0) -> np.ndarray:
+    """Host float32 [n, head_dim/2, 2] cos/sin rows for (frame, row, column) positions [n, 3]."""
+    pos = np.ascontiguousarray(np.asarray(positions, dtype=np.int32))
+    if pos.ndim != 2 or pos.shape[1] != 3:
+        raise ValueError("positions must be [n, 3]")
+    out = np.empty((pos.shape[0], head_dim // 2, 2), dtype=np.float32)
+    keep, bp = _bands_arg(band_pairs)
+    _check("kv_ring_rope_table_3d", lib.kv_ring_rope_table_3d(
+        out.ctypes.data, pos.ctypes.data, pos.shape[0], head_dim, bp, base))
+    del keep
     return out
 
 
@@ -168,6 +191,19 @@ def kv_ring_delta_rotate(ring: Ring, ring_head: int, filled: int, delta: int,
     ws, wsb = _ws(workspace, need, ring.device)
     _check("kv_ring_delta_rotate", lib.kv_ring_delta_rotate(
         ring.desc, ring_head, filled, delta, rope_base, _ptr(ws), wsb, _stream(stream, ring.device)))
+
+
+def kv_ring_delta_rotate_3d(ring: Ring, ring_head: int, filled: int, delta, band_pairs=None,
+                            rope_base: float = 10000.0, workspace=None, stream=None) -> None:
+    """Delta rotation by the (frame, row, column) offset triple `delta`."""
+    d = np.ascontiguousarray(np.asarray(delta, dtype=np.int64).reshape(3))
+    keep, bp = _bands_arg(band_pairs)
+    need = workspace_bytes(OP_DELTA_ROTATE, ring.heads, ring.slots, ring.head_dim, 0)
+    ws, wsb = _ws(workspace, need, ring.device)
+    _check("kv_ring_delta_rotate_3d", lib.kv_ring_delta_rotate_3d(
+        ring.desc, ring_head, filled, d.ctypes.data, bp, rope_base, _ptr(ws), wsb,
+        _stream(stream, ring.device)))
+    del keep
 
 
 def ring_attention(ring: Ring, ring_head: int, filled: int, q, q_pos0: int, rope,

@@ -51,6 +51,43 @@ double rope_theta(int32_t i, int32_t head_dim, double base) {
   return std::pow(base, -(2.0 * i) / (double)head_dim);
 }
 
+// Three-axis positions: the head_dim/2 pairs are cut into contiguous bands (frame, row,
+// column), each a 1-D rotary embedding of dimension 2 * pairs on its own coordinate.  Fills,
+// for every pair, its axis and its frequency; `bands` NULL gives row and column floor(P/3)
+// pairs each and the frame the rest.
+int band_frequencies(const int32_t* bands, int32_t head_dim, double base, int32_t axis[64],
+                     double theta[64]) {
+  const int32_t p = head_dim / 2;
+  int32_t cut[3] = {p - 2 * (p / 3), p / 3, p / 3};
+  if (bands) {
+    for (int b = 0; b < 3; ++b) {
+      if (bands[b] < 0 || bands[b] > p) return KV_RING_ERR_SHAPE;
+      cut[b] = bands[b];
+    }
+    if (cut[0] + cut[1] + cut[2] != p) return KV_RING_ERR_SHAPE;
+  }
+  int32_t k = 0;
+  for (int32_t b = 0; b < 3; ++b)
+    for (int32_t j = 0; j < cut[b]; ++j, ++k) {
+      axis[k] = b;
+      theta[k] = rope_theta(j, 2 * cut[b], base);
+    }
+  return KV_RING_OK;
+}
+
+int check_delta_rotate(const kv_ring_desc* ring, int32_t ring_head, int32_t filled, double rope_base,
+                       void* workspace, size_t workspace_bytes) {
+  int st = check_ring(ring);
+  if (st) return st;
+  if (ring_head < 0 || ring_head >= ring->slots || filled < 0 || filled > ring->slots) return KV_RING_ERR_RANGE;
+  if (!(rope_base > 0.0)) return KV_RING_ERR_SHAPE;
+  return check_workspace(workspace, workspace_bytes,
+                         kv_ring_workspace_bytes(KV_RING_OP_DELTA_ROTATE, ring->heads, ring->slots,
+                                                 ring->head_dim, 0));
+}
+
+bool delta_in_range(int64_t d) { return d > -(int64_t(1) << 31) && d < (int64_t(1) << 31); }
+
 }  // namespace
 
 extern "C" {
@@ -127,14 +164,9 @@ int kv_ring_write(const kv_ring_desc* ring, const void* k_new, const void* v_new
 
 int kv_ring_delta_rotate(const kv_ring_desc* ring, int32_t ring_head, int32_t filled, int64_t delta,
                          double rope_base, void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_ring(ring);
+  int st = check_delta_rotate(ring, ring_head, filled, rope_base, workspace, workspace_bytes);
   if (st) return st;
-  if (ring_head < 0 || ring_head >= ring->slots || filled < 0 || filled > ring->slots) return KV_RING_ERR_RANGE;
-  if (!(rope_base > 0.0)) return KV_RING_ERR_SHAPE;
-  if (delta <= -(int64_t(1) << 31) || delta >= (int64_t(1) << 31)) return KV_RING_ERR_POSITION;
-  st = check_workspace(workspace, workspace_bytes,
-                       kv_ring_workspace_bytes(KV_RING_OP_DELTA_ROTATE, ring->heads, ring->slots, ring->head_dim, 0));
-  if (st) return st;
+  if (!delta_in_range(delta)) return KV_RING_ERR_POSITION;
   // theta_i depends only on (head_dim, base): kept per thread between calls
   thread_local int32_t theta_dim = 0;
   thread_local double theta_base = 0.0, theta[64];
@@ -149,6 +181,55 @@ int kv_ring_delta_rotate(const kv_ring_desc* ring, int32_t ring_head, int32_t fi
     const double ang = (double)delta * theta[i];
     tab.cs[i][0] = (float)std::cos(ang);
     tab.cs[i][1] = (float)std::sin(ang);
+  }
+  return status_of(kvring::launch_delta_rotate(*ring, ring_head, filled, tab, static_cast<float*>(workspace),
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int kv_ring_rope_table_3d(float* host_out, const int32_t* positions, int64_t n, int32_t head_dim,
+                          const int32_t* band_pairs, double base) {
+  if (!host_out || !positions) return KV_RING_ERR_NULL;
+  if (n < 1 || (head_dim != 64 && head_dim != 128) || !(base > 0.0)) return KV_RING_ERR_SHAPE;
+  int32_t axis[64];
+  double theta[64];
+  const int st = band_frequencies(band_pairs, head_dim, base, axis, theta);
+  if (st) return st;
+  const int32_t half = head_dim / 2;
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t* p = positions + 3 * i;
+    float* row = host_out + i * half * 2;
+    for (int32_t k = 0; k < half; ++k) {
+      if (i > 0 && p[axis[k]] == p[axis[k] - 3]) {   // same coordinate as the previous token
+        row[2 * k] = row[2 * k - 2 * half];
+        row[2 * k + 1] = row[2 * k + 1 - 2 * half];
+        continue;
+      }
+      const double ang = (double)p[axis[k]] * theta[k];
+      row[2 * k] = (float)std::cos(ang);
+      row[2 * k + 1] = (float)std::sin(ang);
+    }
+  }
+  return KV_RING_OK;
+}
+
+int kv_ring_delta_rotate_3d(const kv_ring_desc* ring, int32_t ring_head, int32_t filled,
+                            const int64_t* delta, const int32_t* band_pairs, double rope_base,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_delta_rotate(ring, ring_head, filled, rope_base, workspace, workspace_bytes);
+  if (st) return st;
+  if (!delta) return KV_RING_ERR_NULL;
+  if (!delta_in_range(delta[0]) || !delta_in_range(delta[1]) || !delta_in_range(delta[2]))
+    return KV_RING_ERR_POSITION;
+  int32_t axis[64];
+  double theta[64];
+  st = band_frequencies(band_pairs, ring->head_dim, rope_base, axis, theta);
+  if (st) return st;
+  kvring::DeltaTable tab;
+  std::memset(&tab, 0, sizeof(tab));
+  for (int32_t k = 0; k < ring->head_dim / 2; ++k) {
+    const double ang = (double)delta[axis[k]] * theta[k];
+    tab.cs[k][0] = (float)std::cos(ang);
+    tab.cs[k][1] = (float)std::sin(ang);
   }
   return status_of(kvring::launch_delta_rotate(*ring, ring_head, filled, tab, static_cast<float*>(workspace),
                                                static_cast<hipStream_t>(stream)));

@@ -108,6 +108,24 @@ int64_t kv_ring_v_offset(int64_t slot, int32_t channel, int32_t head_dim);
  */
 int kv_ring_rope_table(float *host_out, int64_t n_pos, int32_t head_dim, double base);
 
+/*
+ * Three-axis positions for a video cache (the model of the pages is a video diffusion
+ * transformer; the pages do not give its rotary variant, so this is a reading).  A token's
+ * position is (t, y, x): frame, row, column.  The head_dim/2 interleaved pairs are cut into
+ * three contiguous bands, frame first, then row, then column, of band_pairs[0..2] pairs (NULL:
+ * row and column floor(head_dim/6) each, frame the rest: 22/21/21 at 128, 12/10/10 at 64);
+ * pair j of band b turns by coordinate_b * pow(base, -(2j)/(2 * band_pairs[b])), i.e. each band
+ * is kv_ring_rope_table's embedding of dimension 2 * band_pairs[b] on its own coordinate.
+ * Fills a host float32 table [n][head_dim/2][2] with one row per token (cos and sin computed in
+ * double by the C library, rounded once to float), for positions = host int32 [n][3].  Such a
+ * table serves kv_ring_write and ring_attention unchanged: pass it with pos0 = 0 (q_pos0 = 0)
+ * and rope_n_pos = n, and token i of the call is rotated by row i.
+ * Errors: NULL pointers, n < 1, head_dim not in {64, 128}, base <= 0, band_pairs negative or
+ * not summing to head_dim/2.
+ */
+int kv_ring_rope_table_3d(float *host_out, const int32_t *positions, int64_t n, int32_t head_dim,
+                          const int32_t *band_pairs, double base);
+
 /* Workspace bytes for `op` (KV_RING_OP_*) with n = new tokens (write), unused (delta
  * rotate), nq = queries (attention) or the larger of the two (write + attention).  Returns 0
  * for an unknown op or invalid shape. */
@@ -142,6 +160,20 @@ int kv_ring_write(const kv_ring_desc *ring, const void *k_new, const void *v_new
 int kv_ring_delta_rotate(const kv_ring_desc *ring, int32_t ring_head, int32_t filled,
                          int64_t delta, double rope_base, void *workspace,
                          size_t workspace_bytes, void *stream);
+
+/*
+ * The delta rotation for three-axis positions (bands as in kv_ring_rope_table_3d): every valid
+ * K slot moves by the offset triple delta = host int64 [3] (dt, dy, dx), pair j of band b
+ * turning by delta[b] * pow(base, -(2j)/(2 * band_pairs[b])); a band whose offset is zero turns
+ * by cos 0 = 1, sin 0 = 0.  A position reset of the frame axis is (dt, 0, 0).  Otherwise the
+ * same steps, results and arguments as kv_ring_delta_rotate (one new scale per head over all
+ * valid slots, V untouched, same workspace).
+ * Errors: those of kv_ring_delta_rotate; NULL delta; any |delta[b]| >= 2^31; band_pairs
+ * negative or not summing to head_dim/2.
+ */
+int kv_ring_delta_rotate_3d(const kv_ring_desc *ring, int32_t ring_head, int32_t filled,
+                            const int64_t *delta, const int32_t *band_pairs, double rope_base,
+                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Attention of nq new queries over every valid slot of the ring (abstract: 757 new-token

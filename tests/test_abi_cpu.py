@@ -46,6 +46,18 @@ def test_rope_table_matches_oracle_bit_for_bit(kv):
         assert ours.tobytes() == ref.tobytes()
 
 
+def test_rope_table_3d_matches_oracle_bit_for_bit(kv):
+    from oracle import rope_rows_3d
+    from workloads import raster_positions
+    rng = np.random.default_rng(5)
+    for d, bands in ((128, None), (64, None), (128, (40, 12, 12)), (64, (32, 0, 0))):
+        # a raster walk (runs of equal coordinates) and scattered, partly negative positions
+        for pos in (raster_positions(300, 700, 22, 34, 3),
+                    rng.integers(-5000, 5000, size=(64, 3)).astype(np.int32)):
+            ours = kv.rope_table_3d(pos, d, bands)
+            assert ours.tobytes() == rope_rows_3d(pos, d, bands).tobytes()
+
+
 def test_code_offsets_follow_the_documented_layout(kv):
     """The library's layout functions against the numpy reading of the kvring.h formulas, and
     each tile's offsets are a permutation of the tile's bytes."""
@@ -130,6 +142,29 @@ def test_argument_errors_are_reported_before_any_launch(kv):
     assert L.kv_ring_fp8_encode(F + 4, F, 5, None) == -2
     assert L.kv_ring_fp8_encode(F, F, 0, None) == 0
     assert L.kv_ring_rope_table(None, 10, 64, 10000.0) == -1
+    # three-axis table and delta rotation (host arrays for positions, bands and offsets)
+    pos3 = np.zeros((4, 3), np.int32)
+    out3 = np.empty((4, 32, 2), np.float32)
+    good_b = np.array([12, 10, 10], np.int32)
+    assert L.kv_ring_rope_table_3d(None, pos3.ctypes.data, 4, 64, None, 10000.0) == -1
+    assert L.kv_ring_rope_table_3d(out3.ctypes.data, None, 4, 64, None, 10000.0) == -1
+    assert L.kv_ring_rope_table_3d(out3.ctypes.data, pos3.ctypes.data, 0, 64, None, 10000.0) == -3
+    assert L.kv_ring_rope_table_3d(out3.ctypes.data, pos3.ctypes.data, 4, 96, None, 10000.0) == -3
+    assert L.kv_ring_rope_table_3d(out3.ctypes.data, pos3.ctypes.data, 4, 64, None, 0.0) == -3
+    for bad in ([12, 10, 9], [-1, 23, 10], [33, 0, -1]):
+        bb = np.array(bad, np.int32)
+        assert L.kv_ring_rope_table_3d(out3.ctypes.data, pos3.ctypes.data, 4, 64, bb.ctypes.data,
+                                       10000.0) == -3
+        assert L.kv_ring_delta_rotate_3d(d(good), 0, 10, np.zeros(3, np.int64).ctypes.data,
+                                         bb.ctypes.data, 10000.0, F, wr, None) == -3
+    dl = np.array([5, 0, 0], np.int64)
+    big = np.array([0, 1 << 31, 0], np.int64)
+    assert L.kv_ring_delta_rotate_3d(d(good), 0, 10, None, None, 10000.0, F, wr, None) == -1
+    assert L.kv_ring_delta_rotate_3d(d(good), 0, 10, big.ctypes.data, None, 10000.0, F, wr, None) == -5
+    assert L.kv_ring_delta_rotate_3d(d(good), 64, 10, dl.ctypes.data, None, 10000.0, F, wr, None) == -4
+    assert L.kv_ring_delta_rotate_3d(d(good), 0, 10, dl.ctypes.data, good_b.ctypes.data, 0.0, F, wr,
+                                     None) == -3
+    assert L.kv_ring_delta_rotate_3d(d(good), 0, 10, dl.ctypes.data, None, 10000.0, F, wr - 4, None) == -6
     # write + attention in one call: the checks of both
     wf = kv.workspace_bytes(kv.OP_WRITE_ATTEND, 2, 64, 64, 16)
     assert wf >= ws + wa - 16
