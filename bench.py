@@ -22,6 +22,11 @@ Also reported (one JSON line on stdout; progress on stderr):
               rewritten (the infinity cache no longer holds the ring, as between two calls of
               one layer in a 60-layer model);
   write_sweep kv_ring_write time and GB/s over the token count (32 .. 5,788);
+  fill_up     ring_attention time over the fill level after each of the 8 writes that fill
+              an empty ring (the first chunks of a session);
+  three_axis  the (frame, row, column) position variant: fused step, write and frame reset
+              (kv_ring_delta_rotate_3d by (-5, 0, 0)) with per-token rows, and the host time to
+              build one chunk's rows (kv_ring_rope_table_3d);
   read_time_baseline  the design the ring replaces, with the same kernels: per call the linear
               bfloat16 window is copied forward by the new tokens (kv_window_advance), rotated
               and quantised whole (kv_ring_write of all 5,788 tokens), then attended; its
@@ -74,7 +79,9 @@ def main() -> int:
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timings")
     ap.add_argument("--no-graph", action="store_true",
                     help="time repeated calls as issued from Python only (no graph replays; for profilers)")
-    ap.add_argument("--no-sweep", action="store_true", help="skip the write-size sweep")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the write-size and fill-up sweeps")
+    ap.add_argument("--no-three-axis", action="store_true",
+                    help="skip the three-axis (frame, row, column) position variant")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="also run one plain device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
@@ -297,6 +304,61 @@ def main() -> int:
                              to_dev(normal_bf16(tensor_seed("single_call", c, 2), (N, H, D))),
                              w.start_slot, w.pos0, tab)
 
+    # ---------------------------------------------------------------- fill-up
+    # the first chunks of a session attend over a ring that is still filling: attention time
+    # over the fill level after each of the 8 writes that fill the ring
+    fill = None
+    if not args.no_sweep:
+        fill = []
+        for c in range(8):
+            f_c = min((c + 1) * N, S)
+            h_c = ((c + 1) * N) % S
+            us = graph_us(lambda i: kv.ring_attention(ring, h_c, f_c, q, pos0, tab, scale, out=out, lse=lse,
+                                                      workspace=ws_a), 20)
+            fill.append({"filled": f_c, "call_us": round(us, 2),
+                         "TFLOPs": round(4.0 * N * f_c * D * H / (us * 1e-6) / 1e12, 1)})
+        log("fill-up: " + ", ".join(f"{x['filled']}: {x['call_us']:.1f} us" for x in fill))
+
+    # ---------------------------------------------------------------- three-axis positions
+    # (frame, row, column) positions: per-token cos/sin rows built on the host once per chunk,
+    # the same write / fused call / delta-rotation kernels; a frame reset moves one band
+    three = None
+    if not args.no_three_axis:
+        from workloads import raster_positions
+        pos3 = raster_positions(N, 7 * N)
+        t0 = time.perf_counter()
+        for _ in range(20):
+            rows3 = kv.rope_table_3d(pos3, D)
+        host_us = (time.perf_counter() - t0) / 20 * 1e6
+        tab3 = torch.from_numpy(rows3).to(dev)
+        w3_us = graph_us(lambda i: kv.kv_ring_write(ring, k_new, v_new, start, 0, tab3, workspace=ws_w), 50)
+        r3_us = graph_us(lambda i: kv.kv_ring_delta_rotate_3d(ring, head, filled, (-5 if i % 2 == 0 else 5, 0, 0),
+                                                              workspace=ws_r), 50)
+
+        def step3():
+            kv.kv_ring_write_attend(ring, k_new, v_new, start, 0, head, filled, q, 0, tab3, scale,
+                                    out=out, lse=lse, workspace=ws_f, stream=stream)
+        for _ in range(5):
+            step3()
+        e0.record(stream)
+        for _ in range(100):
+            step3()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        s3_us = 1000.0 * e0.elapsed_time(e1) / 100
+        three = {"step_us": round(s3_us, 2), "write_us": round(w3_us, 2),
+                 "write_GBps": round(WRITE_BYTES / (w3_us * 1e-6) / 1e9, 1),
+                 "frame_reset_us": round(r3_us, 2),
+                 "frame_reset_GBps": round(ROTATE_BYTES / (r3_us * 1e-6) / 1e9, 1),
+                 "host_rows_us": round(host_us, 1)}
+        log(f"three-axis: step {s3_us:.1f} us, write {w3_us:.1f} us, frame reset {r3_us:.1f} us, "
+            f"host rows {host_us:.0f} us per chunk")
+        # restore the 1-D ring contents for the measurements below
+        for c, w in enumerate(sched):
+            kv.kv_ring_write(ring, to_dev(normal_bf16(tensor_seed("single_call", c, 1), (N, H, D))),
+                             to_dev(normal_bf16(tensor_seed("single_call", c, 2), (N, H, D))),
+                             w.start_slot, w.pos0, tab)
+
     # ---------------------------------------------------------------- read-time baseline
     # The design the ring replaces: a linear bfloat16 window copied forward by the new tokens,
     # then rotated and quantised whole (one write of S tokens), then the same attention.
@@ -436,6 +498,8 @@ def main() -> int:
         "chunk": chunk,
         "cold_cache": cold,
         "write_sweep": sweep,
+        "fill_up": fill,
+        "three_axis": three,
         "read_time_baseline": read_time,
         # the pages' own figures (four H100, whole model, per diffusion step): context only, not
         # a target for this line's workload

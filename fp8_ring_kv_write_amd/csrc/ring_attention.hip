@@ -15,8 +15,9 @@
 //      work-groups.  A row held by one work-group is finished in place; the segments of
 //      a split row store their own output, normalised by their own sum, in half precision
 //      (a weighted mean of dequantised V rows: within 2^-11 relative), with their (max, sum).
-//      Consecutive work-groups of one XCD get consecutive units, so the rows of one head share
-//      that XCD's L2;
+//      When rows are short (a ring still filling up) and fit the grid, each work-group takes
+//      one whole row instead, and no merge pass is needed.  Consecutive work-groups of one XCD
+//      get consecutive units, so the rows of one head share that XCD's L2;
 //   3. attn_combine: log-sum-exp merge of the split rows (skipped when no row is split).  Doing
 //      the merge in a kernel of its own avoids device-scope fences inside attn_stream, which on
 //      this multi-XCD part write back and invalidate L2.
@@ -53,6 +54,7 @@ constexpr int kRowQ = 16 * kWaves;      // 128 queries per row, 16 per wavefront
 constexpr int kBufs = 3;                // LDS buffers per operand (see attn_stream's schedule)
 constexpr int kMaxGrid = 256;
 constexpr int kSegCost = 2;             // weight of a segment start in tiles (UnitSplit)
+constexpr int kCombineCost = 6;         // weight of the merge pass of split rows, in tiles
 constexpr float kTau = 4.0f;            // lazy rescale threshold, log2 units
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -770,6 +772,11 @@ Plan make_plan(int32_t heads, int32_t slots, int32_t nq, int32_t ring_head, int3
   if (p.tv > 0) {
     const int64_t min_w = (span + 6) / 7;
     if (g > p.cost / min_w) g = p.cost / min_w;
+    // one work-group per row (no row split, so no merge pass) when a whole row weighs no more
+    // than a share of the split plan plus the merge pass, which costs about kCombineCost tiles
+    // (its launch and its reads): the case of a short ring, as while the ring fills up
+    const int64_t cap = grid_cap < kMaxGrid ? grid_cap : kMaxGrid;
+    if (p.rows <= cap && g > 0 && span <= (p.cost + g - 1) / g + kCombineCost) g = p.rows;
   }
   p.grid = int(g < 1 ? 1 : g);
   // a row of weight span is shared by at most ceil(span / floor(cost / grid)) + 1 work-groups
