@@ -58,8 +58,8 @@ ATT_KERNEL = "attn_stream<128>"
 # (FETCH_SIZE, WRITE_SIZE) over this workload, each divided by the factor the same counter
 # reads for a torch copy of --calibrate-copy bytes.  Valid only for the kernel sources whose
 # hash is recorded; reported as null otherwise.
-ATT_TRAFFIC = {"sources": "a2598da443871db7", "bytes": 131_740_000,
-               "read_bytes": 118_760_000, "write_bytes": 12_980_000}
+ATT_TRAFFIC = {"sources": "14b454df175bfbaa", "bytes": 131_440_000,
+               "read_bytes": 118_460_000, "write_bytes": 12_980_000}
 WRITE_BYTES = 2 * N * H * D * 2 + 2 * N * H * D + 2 * N * H * 4
 ROTATE_BYTES = 2 * (H * S * D + H * S * 4)
 
