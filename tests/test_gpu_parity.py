@@ -252,6 +252,21 @@ def test_attention_single_call_full_size(kv, torch):
     check_attention(out, lse, ro, rl, label="single call")
 
 
+def test_attention_fill_up_full_size(kv, torch):
+    """The first chunks of a session: 757 queries over a 24-head d128 ring of 5,788 slots that
+    holds one, two and then three 757-token chunks (rows of 6, 12 and 18 tiles: one work-group
+    per row for the first two, rows split between work-groups for the third)."""
+    p = Pair(kv, torch, 24, 5788, 128)
+    for c in range(3):
+        k = normal_bf16(tensor_seed("fill_up", c, 1), (757, 24, 128))
+        v = normal_bf16(tensor_seed("fill_up", c, 2), (757, 24, 128))
+        p.write(k, v, 757 * c, 757 * c)
+        assert (p.head, p.filled) == (757 * (c + 1), 757 * (c + 1))
+        q = normal_bf16(tensor_seed("fill_up", c, 0), (757, 24, 128))
+        check_attention(*p.attend(q, 757 * c, 1 / math.sqrt(128)), label=f"fill-up filled={p.filled}")
+    p.assert_same("after three chunks")
+
+
 @pytest.mark.parametrize("slots,n,writes,nq", [
     (700, 100, 3, 1),       # partial ring, one query
     (700, 100, 8, 17),      # wrapped full ring, ragged queries
