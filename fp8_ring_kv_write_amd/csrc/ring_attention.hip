@@ -24,22 +24,26 @@
 //
 // Per tile: K tile and transposed V tile are copied straight from HBM into LDS with
 // global_load_lds (16 bytes per lane; the ring stores each tile in the order the products read
-// it, so copies and operand reads are linear 1 KB wavefront accesses free of bank conflicts;
-// three buffers per operand, each copy issued at the end of the step two steps before the one
-// that reads it).  Each wavefront owns 16 queries:
+// it, so copies and operand reads are linear 1 KB wavefront accesses free of bank conflicts).
+// K has three LDS buffers; each K copy is issued at the end of the step two steps before the
+// one that reads it.  An FP8 V tile lands in one of two buffers two steps ahead and is widened
+// to fp16 (exact: every E4M3 value is an fp16 value) at the end of the step that forms its
+// probabilities, each thread widening the very units it copied, so no barrier separates the
+// landing from the widening.  Each wavefront owns 16 queries:
 //   S^T = K Q^T           8 MFMA 16x16x128 FP8 (fp32 accumulate)
 //   online softmax        log2 domain, lazily rescaled (the running max may lag the true max
-//                         by up to 2^4, so P <= 16)
-//   P = hi + lo           hi = e4m3(P), lo = e4m3((P - hi) * 2^8)
-//   O^T += V^T P^T        8 x 2 MFMA 16x16x128 FP8; the B-operand exponent scale carries
-//                         the tile's power-of-two V-scale factor (and 2^-8 for lo)
+//                         by up to 2^4, so P <= 16); the running max is taken over the score
+//                         plus log2 of the slot's V scale, so P already carries that scale
+//   O^T += V^T P^T        32 MFMA 16x16x32 fp16 (fp32 accumulate): P rounded once to fp16,
+//                         V widened from E4M3
 // Computing S^T rather than S leaves one query per lane with its keys in registers, which is
 // exactly the B-operand layout of the PV product: probabilities never leave their lane.
 //
 // A tile whose 128 slots are all valid and come from one write (one K scale, one V scale) takes
 // the fast path: the max runs on raw scores, one FMA forms the exponent, and the V-scale factor
 // is folded into it.  Other tiles (ring edges, write boundaries, partially filled rings) take
-// the general path with per-slot scales, masking and zeroed V bytes for invalid slots.
+// the general path with per-slot scales, masking, and zeroed K bytes and fp16 V values for
+// invalid slots.
 
 #include "kvring_common.hpp"
 #include "kvring_internal.hpp"
@@ -51,7 +55,7 @@ namespace {
 constexpr int kWaves = 8;               // 2 wavefronts per SIMD
 constexpr int kThreads = 64 * kWaves;   // 512
 constexpr int kRowQ = 16 * kWaves;      // 128 queries per row, 16 per wavefront
-constexpr int kBufs = 3;                // LDS buffers per operand (see attn_stream's schedule)
+constexpr int kBufs = 3;                // LDS buffers of K tiles (see attn_stream's schedule)
 constexpr int kMaxGrid = 256;
 constexpr int kSegCost = 2;             // weight of a segment start in tiles (UnitSplit)
 constexpr int kCombineCost = 6;         // weight of the merge pass of split rows, in tiles
@@ -59,6 +63,9 @@ constexpr float kTau = 4.0f;            // lazy rescale threshold, log2 units
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));   // split rows' partial outputs
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));   // fp16 operand of the PV product
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 struct AttnArgs {
   const uint8_t* kc;
@@ -106,21 +113,31 @@ struct UnitSplit {
 // the factor arrays from the asynchronous tile copies landing in the tile and scale buffers.
 template <int D>
 struct Smem {
-  uint8_t (&k)[kBufs][kTile * D];   // K tile j of a segment in k[j % 3] (with ks, vs, factors)
-  uint8_t (&v)[kBufs][D * kTile];   // transposed V tile j in v[j % 3]
+  uint8_t (&k)[kBufs][kTile * D];    // K tile j of a segment in k[j % 3] (with ks, vs, factors)
+  uint8_t (&v8)[2][D * kTile];       // FP8 transposed V tile j lands in v8[j % 2]
+  uint8_t (&v16)[2][2 * D * kTile];  // V tile j widened to fp16 in v16[j % 2] (PV operand order)
   float (&ks)[kBufs][kTile];
   float (&vs)[kBufs][kTile];
   float (&ck)[kBufs][kTile];   // per slot: c0 * k_scale (valid) or 0
   float (&nb)[kBufs][kTile];   // per slot: log2(v_scale) (valid) or -inf
   float (&iv)[kBufs][kTile];   // per slot: 1 / v_scale (valid) or 0
-  int (&eg)[kBufs][4];         // exponent of the largest valid v_scale per 32 slots (-128: none)
   int (&uni)[kBufs][4];        // per 32 slots: all valid, one K scale and one V scale (1) or not
+  int (&full)[kBufs];          // the tile's 128 slots are all valid (1) or not (0)
   uint8_t (&q)[kRowQ * 128];   // the row's quantised queries (QK operands, 32 bytes per lane)
   float (&qs)[4];              // the head's query scale
 };
 
-__device__ inline v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c, int scale_b) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, scale_b);
+__device__ inline v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ inline v4f mfma_f16(const v8h& a, const v8h& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Two floats -> two fp16 values (round to nearest even), the first in the low half.
+__device__ inline uint32_t pack_f16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, v2h{(_Float16)a, (_Float16)b});
 }
 
 __device__ inline uint16_t f32_to_bf16(float f) {
@@ -198,7 +215,7 @@ __device__ inline void copy4(const void* base, uint32_t voff, const void* lds) {
 }
 
 // Asynchronous copies of ring tile t into LDS: K tile and both scale rows into K buffer b
-// (kLoads + 1 copies per lane), or the transposed V tile into V buffer b (kLoads per lane).
+// (kLoads + 1 copies per lane), or the transposed FP8 V tile into v8[b] (kLoads per lane).
 template <int D>
 __device__ inline void issue_k(const AttnArgs& a, Smem<D>& sm, const CopyOffs<D>& co, int b,
                                int64_t t, int h, int w, int lane) {
@@ -221,7 +238,7 @@ __device__ inline void issue_v(const AttnArgs& a, Smem<D>& sm, int b, int64_t t,
   const uint8_t* vbase = a.vc + ((int64_t)h * a.tiles + t) * (D * kTile);   // uniform
 #pragma unroll
   for (int j = 0; j < CopyOffs<D>::kLoads; ++j)
-    copy16(vbase, uint32_t(((j * kWaves + w) * 64 + lane) * 16), &sm.v[b][(j * kWaves + w) * 1024]);
+    copy16(vbase, uint32_t(((j * kWaves + w) * 64 + lane) * 16), &sm.v8[b][(j * kWaves + w) * 1024]);
 }
 
 // Wait until at most n of this thread's vector-memory operations are outstanding (they complete
@@ -257,10 +274,6 @@ __device__ inline uint32_t row_max16(uint32_t m) {
 // Per-slot factors of the tile in K buffer b, and zeroed K bytes for its invalid slots (so that
 // whatever they hold -- NaN codes included -- never reaches a product).  Wavefronts 0-3 (one per
 // SIMD) take 32 slots each, one per lane of their first half; the zeroing is shared by all.
-// With vmax = f * 2^e (f in [0.5, 1)) the largest valid V scale of the tile, the probabilities
-// enter the PV product as P * v_scale * 2^-e <= P, and the product's B-operand scale multiplies
-// back by 2^e (one exponent per tile: the scale of the FP8 matrix product applies per 32-element
-// block of its contraction, and a block gathers 16-slot pieces of two lane groups).
 template <int D>
 __device__ inline void prep_tile(Smem<D>& sm, int b, const TileValid& tvd, float c0, int tid) {
   constexpr int NCH = D / 16;
@@ -269,22 +282,13 @@ __device__ inline void prep_tile(Smem<D>& sm, int b, const TileValid& tvd, float
     const int u = (tid >> 6) * 32 + lane;
     const bool ok = tvd.has(u);
     const float ksu = sm.ks[b][u], vsu = sm.vs[b][u];
-    // the group's largest valid V scale (positive floats order as their bit patterns)
-    uint32_t m = row_max16(ok ? __float_as_uint(vsu) : 0u);
-    const auto sw = __builtin_amdgcn_permlane16_swap(m, m, false, false);   // rows 0 <-> 1
-    m = max(sw[0], sw[1]);
-    int e = -128;
-    if (m != 0u) {
-      (void)__builtin_frexpf(__uint_as_float(m), &e);
-      e = max(-110, min(120, e));
-    }
     sm.ck[b][u] = ok ? c0 * ksu : 0.0f;
     sm.nb[b][u] = ok ? __log2f(vsu) : -INFINITY;
     sm.iv[b][u] = ok ? __builtin_amdgcn_rcpf(vsu) : 0.0f;
-    if (lane == 0) sm.eg[b][u >> 5] = e;
     const bool same = ok && ksu == sm.ks[b][0] && vsu == sm.vs[b][0];
     const bool all_same = __all(same);   // over this wavefront's 32 active lanes
     if (lane == 0) sm.uni[b][u >> 5] = all_same ? 1 : 0;
+    if (tid == 0) sm.full[b] = tvd.count() == kTile ? 1 : 0;
   }
   if (tvd.count() < kTile) {
     uint8_t* kw = sm.k[b];
@@ -295,24 +299,45 @@ __device__ inline void prep_tile(Smem<D>& sm, int b, const TileValid& tvd, float
   }
 }
 
-// Zeroed V bytes of the invalid slots of the tile in V buffer b (tiles with invalid slots only).
+// Widening of the FP8 V tile in v8[b] to fp16 in v16[b], in the PV product's operand order, with
+// the invalid slots' values zeroed (a slot is valid exactly when its factor iv, in K buffer bf,
+// is non-zero: 1 / v_scale is finite and positive for every scale a write can store).  FP8 unit ((db*2 + r)*4 + g)*16 + li holds slots 32g + 16r ..
+// +15 of channel 16db + li; its first 8 slots become piece (db, kb = 2r) and its last 8 piece
+// (db, 2r + 1), where piece (db, kb) of lane (g, li) -- slots 32g + 8kb .. +7 of channel
+// 16db + li, 8 fp16 values -- sits at byte ((db*4 + kb)*64 + g*16 + li) * 16.  Each thread widens
+// the units its own tile copy brought in (unit (j*8 + w)*64 + lane), so its own wait for that
+// copy suffices; the fp16 tile is read by other wavefronts only after the next barrier.
 template <int D>
-__device__ inline void zero_invalid_v(Smem<D>& sm, int b, const TileValid& tvd, int tid) {
-  uint8_t* vw = sm.v[b];
-  for (int c = tid; c < D * 8; c += kThreads) {        // 16-byte units of the V tile
-    const int u0 = 32 * ((c >> 4) & 3) + 16 * ((c >> 6) & 1);   // first slot of the unit
-    uint4 x = *reinterpret_cast<uint4*>(vw + c * 16);
-    uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+__device__ inline void widen_v(Smem<D>& sm, int b, int bf, int w, int lane) {
+  constexpr int kLoads = (D * kTile / 16) / kThreads;
+  const bool full = __builtin_amdgcn_readfirstlane(sm.full[bf]) != 0;
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk)
-      if (!tvd.has(u0 + kk)) xw[kk >> 2] &= ~(0xFFu << (8 * (kk & 3)));
-    *reinterpret_cast<uint4*>(vw + c * 16) = make_uint4(xw[0], xw[1], xw[2], xw[3]);
+  for (int j = 0; j < kLoads; ++j) {
+    const int c = (j * kWaves + w) * 64 + lane;
+    const uint4 x = *reinterpret_cast<const uint4*>(&sm.v8[b][c * 16]);
+    const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+    uint32_t h[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(int(xw[i]), 1.0f, false));
+      h[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(int(xw[i]), 1.0f, true));
+    }
+    const int li = c & 15, g = (c >> 4) & 3, r = (c >> 6) & 1, db = c >> 7;
+    if (!full) {
+      const float* ivu = &sm.iv[bf][32 * g + 16 * r];
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk)
+        if (ivu[kk] == 0.0f) h[kk >> 1] &= (kk & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+    }
+    const int o0 = ((db * 4 + 2 * r) * 64 + g * 16 + li) * 16;
+    *reinterpret_cast<uint4*>(&sm.v16[b][o0]) = make_uint4(h[0], h[1], h[2], h[3]);
+    *reinterpret_cast<uint4*>(&sm.v16[b][o0 + 1024]) = make_uint4(h[4], h[5], h[6], h[7]);
   }
 }
 
 // Per-lane LDS byte offsets (within one buffer) of a lane's A operands: half r of score block bb
-// is K unit (bb*2 + r)*(D/32)*16 + lane, half r of channel block db is V unit (db*2 + r)*64 +
-// lane: every operand read is one contiguous 1 KB wavefront read.
+// is K unit (bb*2 + r)*(D/32)*16 + lane, piece (db, kb) of the fp16 V tile is 16-byte unit
+// (db*4 + kb)*64 + lane: every operand read is one contiguous 1 KB wavefront read.
 struct LaneOffs {
   int k, v;
 };
@@ -325,7 +350,7 @@ __device__ inline LaneOffs lane_offsets(int lane) {
   return o;
 }
 
-// A operand of score block bb (16 K rows) / of channel block db (16 transposed V rows).
+// A operand of score block bb (16 K rows).
 template <int D>
 __device__ inline v8i k_operand(const uint8_t* kt, const LaneOffs& o, int bb, int g) {
   const uint4 x0 = *reinterpret_cast<const uint4*>(kt + o.k + (bb * 2) * (D / 32) * 256);
@@ -334,23 +359,9 @@ __device__ inline v8i k_operand(const uint8_t* kt, const LaneOffs& o, int bb, in
   return v8i{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
 }
 
-__device__ inline v8i v_operand(const uint8_t* vt, const LaneOffs& o, int db) {
-  const uint4 x0 = *reinterpret_cast<const uint4*>(vt + o.v + (db * 2) * 1024);
-  const uint4 x1 = *reinterpret_cast<const uint4*>(vt + o.v + (db * 2 + 1) * 1024);
-  return v8i{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
-}
-
-// P (<= 16, non-negative) -> FP8 hi part and FP8 lo part of (P - hi) * 2^8, four values per dword.
-// old: any two dwords (dead values); each conversion pair writes both halves of its dword.
-__device__ inline int2 split_p(const float (&p)[4], int2 old) {
-  int hw = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], old.x, false);
-  hw = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], hw, true);
-  const v2f h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
-  const v2f h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
-  v2s lw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(__builtin_bit_cast(v2s, old.y),
-                                                    p[0] - h01[0], p[1] - h01[1], 0x1p-8f, false);
-  lw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lw, p[2] - h23[0], p[3] - h23[1], 0x1p-8f, true);
-  return make_int2(hw, int(uint32_t(uint16_t(lw[0])) | (uint32_t(uint16_t(lw[1])) << 16)));
+// A operand of the PV product of channel block db over slot block kb (16 fp16 V^T rows).
+__device__ inline v8h v_operand(const uint8_t* vt, const LaneOffs& o, int db, int kb) {
+  return *reinterpret_cast<const v8h*>(vt + o.v + (db * 4 + kb) * 1024);
 }
 
 // Running softmax state and output accumulator of one wavefront (16 queries; lane (g, li)
@@ -362,36 +373,36 @@ struct RowState {
   float l;   // this lane's share of the running sum
 };
 
-// Probabilities of one tile as the B operand of the PV product, with their exponent scales.
+// Probabilities of one tile as the B operands of the PV product, in fp16: lane (g, li) holds
+// query li's probabilities of slots 32g .. 32g+31, two per dword in slot order; dwords 4kb ..
+// 4kb+3 (slots 32g + 8kb .. +7) are its operand of slot block kb.
 struct PTile {
-  v8i hi, lo;
-  int sc_hi, sc_lo;
+  uint32_t w[16];
 };
+
+__device__ inline v8h p_operand(const PTile& p, int kb) {
+  return __builtin_bit_cast(v8h, v4u{p.w[4 * kb], p.w[4 * kb + 1], p.w[4 * kb + 2], p.w[4 * kb + 3]});
+}
 
 // One pipeline step of a wavefront:
 //   softmax of tile k   (raw scores s; factors in LDS buffer bk) -> probabilities pc
-//   PV of tile k-1      (probabilities pp; V in LDS buffer bp), interleaved with the softmax
+//   PV of tile k-1      (probabilities pp; fp16 V in LDS buffer bp), interleaved with the softmax
 //   QK of tile k+1      (K in LDS buffer bn) -> raw scores, into s
 // The PV products do not depend on tile k, so the matrix cores work while the vector units
 // form tile k's probabilities.  A rescale found by tile k's max is applied to the accumulator
 // after the PV of tile k-1, whose probabilities were formed against the old max.
 //
 // Per score (slot j, query i):  t = raw * ck_j + nb_j, the log2-domain score plus log2 of the
-// slot's V scale; P' = 2^(t - e - m) goes to the PV product (whose B-operand scale is 2^e) and
-// P' * iv_j * 2^e = 2^(score - m) to the row sum.  The running max m tracks max (t - e).
+// slot's V scale; P' = 2^(t - m) goes to the PV product (with V decoded but not scaled) and
+// P' * iv_j = 2^(score - m) to the row sum.  The running max m tracks max t.
 template <int D>
 __device__ __forceinline__ void pipeline_step(const Smem<D>& sm, int bk, int bp, int bn, int g,
                                               const LaneOffs& lo, const v8i& qop, v4f (&sc)[8],
                                               const PTile& pp, PTile& pc, RowState<D>& st) {
   constexpr int NDB = D / 16;
-  const uint8_t* vt = sm.v[bp];
+  constexpr int NPV = NDB / 2;   // PV products per score block: NDB * 4 over 8 blocks
+  const uint8_t* vt = sm.v16[bp];
   const uint8_t* kt = sm.k[bn];
-  const int4 egv = *reinterpret_cast<const int4*>(&sm.eg[bk][0]);
-  int e = max(max(egv.x, egv.y), max(egv.z, egv.w));
-  e = e == -128 ? 0 : e;
-  const float fe = float(e);
-  pc.sc_hi = 127 + e;
-  pc.sc_lo = 127 + e - 8;
 
   // ---- tile k: scores with their factors, max, rescale decision.  A uniform tile (all slots
   // valid, one K scale, one V scale) keeps its raw scores: t = raw * c + b for every slot.
@@ -405,7 +416,7 @@ __device__ __forceinline__ void pipeline_step(const Smem<D>& sm, int bk, int bp,
     for (int bb = 0; bb < 8; ++bb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) rmax = __builtin_fmaxf(rmax, sc[bb][r]);
-    tmax = max_over_groups(rmax) * cf + bf - fe;
+    tmax = max_over_groups(rmax) * cf + bf;
   } else {
     tmax = -INFINITY;
 #pragma unroll
@@ -419,7 +430,7 @@ __device__ __forceinline__ void pipeline_step(const Smem<D>& sm, int bk, int bp,
 #pragma unroll
       for (int r = 0; r < 4; ++r) tmax = __builtin_fmaxf(tmax, sc[bb][r]);
     }
-    tmax = max_over_groups(tmax) - fe;
+    tmax = max_over_groups(tmax);
   }
   const bool need = __any(tmax > st.m + kTau);
   float alpha = 1.0f;
@@ -428,20 +439,24 @@ __device__ __forceinline__ void pipeline_step(const Smem<D>& sm, int bk, int bp,
     alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(st.m - m_new);
     st.m = m_new;
   }
-  const float bm = bf - ((st.m == -INFINITY ? 0.0f : st.m) + fe);   // P' = 2^(s * cf + bm)
+  const float bm = bf - (st.m == -INFINITY ? 0.0f : st.m);   // P' = 2^(s * cf + bm)
 
-  // ---- PV(k-1) interleaved with tile k's probabilities.  V operands are read from LDS one
-  // block ahead; the scheduling barriers keep the blocks in order so that few are live.
+  // ---- PV(k-1) interleaved with tile k's probabilities: product n takes channel block n % NDB
+  // and slot block n / NDB, so consecutive products accumulate into different blocks.  V
+  // operands are read from LDS one product ahead; the scheduling barriers keep the blocks in
+  // order so that few are live.
   float lsum = 0.0f;
-  v8i vo_n = v_operand(vt, lo, 0);
+  v8h vo_n = v_operand(vt, lo, 0, 0);
+  auto pv = [&](int n) {
+    const v8h vo = vo_n;
+    if (n + 1 < NDB * 4) vo_n = v_operand(vt, lo, (n + 1) % NDB, (n + 1) / NDB);
+    st.acc[n % NDB] = mfma_f16(vo, p_operand(pp, n / NDB), st.acc[n % NDB]);
+  };
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int s8 = 0; s8 < 8; ++s8) {
-    const int db = s8 * NDB / 8;                 // channel block of this step (D = 64: every other)
-    const bool pv = (s8 * NDB) % 8 == 0;
-    v8i vo = vo_n;
-    if (pv && db + 1 < NDB) vo_n = v_operand(vt, lo, db + 1);
-    if (pv) st.acc[db] = mfma_fp8(vo, pp.hi, st.acc[db], pp.sc_hi);
+#pragma unroll
+    for (int i = 0; i < (NPV + 1) / 2; ++i) pv(s8 * NPV + i);
     const float4 iv = *reinterpret_cast<const float4*>(&sm.iv[bk][32 * g + 4 * s8]);
     const float ivr[4] = {iv.x, iv.y, iv.z, iv.w};
     float p[4];
@@ -450,13 +465,14 @@ __device__ __forceinline__ void pipeline_step(const Smem<D>& sm, int bk, int bp,
       p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[s8][r], cf, bm));
       lsum = __builtin_fmaf(p[r], ivr[r], lsum);
     }
-    int2 hl = split_p(p, make_int2(pc.hi[s8], pc.lo[s8]));
-    // pin the block's vector work here, between its two products (otherwise it is sunk
-    // below the branches that follow, away from the products it should overlap)
-    asm volatile("" : "+v"(hl.x), "+v"(hl.y), "+v"(lsum));
-    pc.hi[s8] = hl.x;
-    pc.lo[s8] = hl.y;
-    if (pv) st.acc[db] = mfma_fp8(vo, pp.lo, st.acc[db], pp.sc_lo);
+    uint32_t h0 = pack_f16(p[0], p[1]), h1 = pack_f16(p[2], p[3]);
+    // pin the block's vector work here, between its products (otherwise it is sunk below the
+    // branches that follow, away from the products it should overlap)
+    asm volatile("" : "+v"(h0), "+v"(h1), "+v"(lsum));
+    pc.w[2 * s8] = h0;
+    pc.w[2 * s8 + 1] = h1;
+#pragma unroll
+    for (int i = (NPV + 1) / 2; i < NPV; ++i) pv(s8 * NPV + i);
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -466,31 +482,36 @@ __device__ __forceinline__ void pipeline_step(const Smem<D>& sm, int bk, int bp,
   for (int bb = 0; bb < 8; ++bb) {
     const v8i ko = ko_n;
     if (bb + 1 < 8) ko_n = k_operand<D>(kt, lo, bb + 1, g);
-    sc[bb] = mfma_fp8(ko, qop, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 127);
+    sc[bb] = mfma_fp8(ko, qop, v4f{0.0f, 0.0f, 0.0f, 0.0f});
   }
   if (need) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) st.acc[db] *= alpha;
     st.l *= alpha;
   }
-  st.l += lsum * __builtin_ldexpf(1.0f, e);
+  st.l += lsum;
 }
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
   constexpr int NDB = D / 16;
   __shared__ __align__(16) uint8_t s_k[kBufs][kTile * D];
-  __shared__ __align__(16) uint8_t s_v[kBufs][D * kTile];
+  __shared__ __align__(16) uint8_t s_v8[2][D * kTile];
+  __shared__ __align__(16) uint8_t s_v16[2][2 * D * kTile];
   __shared__ __align__(16) float s_ks[kBufs][kTile];
   __shared__ __align__(16) float s_vs[kBufs][kTile];
   __shared__ __align__(16) float s_ck[kBufs][kTile];
   __shared__ __align__(16) float s_nb[kBufs][kTile];
   __shared__ __align__(16) float s_iv[kBufs][kTile];
-  __shared__ __align__(16) int s_eg[kBufs][4];
   __shared__ __align__(16) int s_uni[kBufs][4];
-  __shared__ __align__(16) uint8_t s_q[kRowQ * 128];
+  __shared__ int s_full[kBufs];
+  // the row's query codes: for head_dim 128 they land in K buffer 2 (a K tile is exactly their
+  // size), read before K tile 2 is copied there; 152 KB of LDS in all
+  __shared__ __align__(16) uint8_t s_qx[D == 128 ? 16 : kRowQ * 128];
   __shared__ __align__(16) float s_qs[4];
-  Smem<D> sm{s_k, s_v, s_ks, s_vs, s_ck, s_nb, s_iv, s_eg, s_uni, s_q, s_qs};
+  uint8_t (&s_q)[kRowQ * 128] =
+      *reinterpret_cast<uint8_t (*)[kRowQ * 128]>(D == 128 ? &s_k[2][0] : &s_qx[0]);
+  Smem<D> sm{s_k, s_v8, s_v16, s_ks, s_vs, s_ck, s_nb, s_iv, s_uni, s_full, s_q, s_qs};
 
   const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);   // wavefront (uniform)
 
@@ -519,15 +540,18 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
     auto phys = [&](int k) -> int64_t { return k < a.n1 ? a.first1 + k : a.first2 + (k - a.n1); };
 
     // Copy schedule (j = tile index within the segment; step j forms tile j's probabilities,
-    // runs the PV product of tile j-1 and the QK product of tile j+1):
+    // runs the PV product of tile j-1 and the QK product of tile j+1, then widens V tile j):
     //   K tile j (+ scales) -> K buffer j % 3, issued at the end of step j-3, needed from step
     //                          j-1 on;
-    //   V tile j            -> V buffer j % 3, issued at the end of step j-1, needed in step j+1.
+    //   FP8 V tile j        -> v8[j % 2], issued at the end of step j-2, widened at the end of
+    //                          step j into v16[j % 2] (read by step j+1).
     // A step waits only for the copies issued two steps back, so each copy has a step to land.
     // Issued after the step's products rather than before them, the copies queue in the memory
     // pipeline while the matrix cores finish, instead of holding every wavefront at the start.
+    // A thread's V copy lands in the units that thread widens, so reusing v8[j % 2] for tile
+    // j+2 right after widening tile j needs no barrier.
     // The row's quantised queries (16 KB, 32 bytes per lane) and the head's query scale are
-    // copied first, then K tiles 0 and 1, so that one memory round trip covers all of them.
+    // copied first, then K tiles 0 and 1 and V tile 0, so that one memory round trip covers all.
     {
       const uint8_t* qbase = a.q_codes + (int64_t)row * (kRowQ * 128);   // uniform
 #pragma unroll
@@ -535,16 +559,18 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
         copy16(qbase, uint32_t(((j * kWaves + w) * 64 + lane) * 16), &sm.q[(j * kWaves + w) * 1024]);
       if (w == 0 && lane == 0) copy4(a.q_scale, uint32_t(head) * 4u, &sm.qs[0]);
     }
+    const int nk = CopyOffs<D>::kLoads + 1, nv = CopyOffs<D>::kLoads;
     issue_k<D>(a, sm, co, 0, phys(k0), head, w, lane);
     if (nt > 1) issue_k<D>(a, sm, co, 1, phys(k0 + 1), head, w, lane);
-    const int nk = CopyOffs<D>::kLoads + 1, nv = CopyOffs<D>::kLoads;
+    issue_v<D>(a, sm, 0, phys(k0), head, w, lane);
 
-    // the PV of the first step reads "tile -1" from the last V buffer: zeros
+    // the PV of the first step reads "tile -1" from v16[1] with zero probabilities: zero it, so
+    // that no stale value (NaN included) meets them
     {
-      uint4* vz = reinterpret_cast<uint4*>(sm.v[kBufs - 1]);
-      for (int c = tid; c < D * kTile / 16; c += kThreads) vz[c] = make_uint4(0, 0, 0, 0);
+      uint4* vz = reinterpret_cast<uint4*>(sm.v16[1]);
+      for (int c = tid; c < 2 * D * kTile / 16; c += kThreads) vz[c] = make_uint4(0, 0, 0, 0);
     }
-    wait_vm(nt > 1 ? 2 * nk : nk);   // this thread's query copies have landed (K tiles may not)
+    wait_vm((nt > 1 ? 2 * nk : nk) + nv);   // this thread's query copies have landed
     lds_sync();
     const float c0 = a.score_scale * sm.qs[0];
     v8i qop;
@@ -560,67 +586,52 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) st.acc[db] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     PTile pa, pb;
-    pa.hi = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-    pa.lo = pa.hi;
-    pa.sc_hi = pa.sc_lo = 127;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pa.w[i] = 0u;
     pb = pa;
     v4f sc[8];
 
     // ---- prologue: K tile 0 resident and prepared, its raw scores in sc
-    wait_vm(nt > 1 ? nk : 0);
+    wait_vm((nt > 1 ? nk : 0) + nv);
     lds_sync();
     {
       const TileValid tvd = tile_valid(phys(k0), a.ring_head, a.filled, a.slots);
       prep_tile(sm, 0, tvd, c0, tid);
     }
-    lds_sync();
+    lds_sync();   // also: every wavefront has read its queries out of K buffer 2
 #pragma unroll
     for (int bb = 0; bb < 8; ++bb)
-      sc[bb] = mfma_fp8(k_operand<D>(sm.k[0], lo, bb, g), qop, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 127);
-    // copies of step -1: K tile 2, V tile 0
+      sc[bb] = mfma_fp8(k_operand<D>(sm.k[0], lo, bb, g), qop, v4f{0.0f, 0.0f, 0.0f, 0.0f});
+    // copies of step -1: K tile 2, V tile 1
     int n_prev = 0;
     if (nt > 2) { issue_k<D>(a, sm, co, 2, phys(k0 + 2), head, w, lane); n_prev += nk; }
-    issue_v<D>(a, sm, 0, phys(k0), head, w, lane);
-    n_prev += nv;
+    if (nt > 1) { issue_v<D>(a, sm, 1, phys(k0 + 1), head, w, lane); n_prev += nv; }
 
     // ---- pipeline over the segment's tiles; two steps per trip so that the two probability
     // tiles swap roles without register copies
     auto step = [&](int j, const PTile& pprev, PTile& pcur) {
-      const int bk = j % kBufs, bn = (j + 1) % kBufs, bp = (j + kBufs - 1) % kBufs;
-      wait_vm(n_prev);     // this thread's copies issued two steps back have landed:
-      lds_sync();     // K tile j+1 and V tile j-1 are resident, buffers of j+3 / j+1 free
+      const int bk = j % kBufs, bn = (j + 1) % kBufs;
+      wait_vm(n_prev);   // this thread's copies issued two steps back have landed: K tile j+1
+      lds_sync();        // and V tile j; fp16 V tile j-1 complete; K buffer of j+3 free
       n_prev = 0;
-      bool fix = false;    // LDS bytes changed below: barrier before the products read them
-      if (j >= 1) {
-        const TileValid tvp = tile_valid(phys(k0 + j - 1), a.ring_head, a.filled, a.slots);
-        if (tvp.count() < kTile) { zero_invalid_v(sm, bp, tvp, tid); fix = true; }
-      }
       if (j + 1 < nt) {
         const TileValid tvn = tile_valid(phys(k0 + j + 1), a.ring_head, a.filled, a.slots);
         prep_tile(sm, bn, tvn, c0, tid);
-        fix = fix || tvn.count() < kTile;
+        if (tvn.count() < kTile) lds_sync();   // K bytes zeroed: barrier before the QK reads them
       }
-      if (fix) lds_sync();
-      pipeline_step<D>(sm, bk, bp, bn, g, lo, qop, sc, pprev, pcur, st);
-      // this step's copies go out behind its QK products (the buffers are free all step)
+      pipeline_step<D>(sm, bk, (j + 1) & 1, bn, g, lo, qop, sc, pprev, pcur, st);
+      widen_v(sm, j & 1, bk, w, lane);
+      // this step's copies go out behind its products (the buffers are free)
       if (j + 3 < nt) { issue_k<D>(a, sm, co, (j + 3) % kBufs, phys(k0 + j + 3), head, w, lane); n_prev += nk; }
-      if (j + 1 < nt) { issue_v<D>(a, sm, bn, phys(k0 + j + 1), head, w, lane); n_prev += nv; }
+      if (j + 2 < nt) { issue_v<D>(a, sm, j & 1, phys(k0 + j + 2), head, w, lane); n_prev += nv; }
     };
     auto final_pv = [&](int jl, const PTile& pt) {   // PV of the last tile jl
       wait_vm(0);
-      lds_sync();
-      const TileValid tvl = tile_valid(phys(k0 + jl), a.ring_head, a.filled, a.slots);
-      if (tvl.count() < kTile) {
-        zero_invalid_v(sm, jl % kBufs, tvl, tid);
-        lds_sync();
-      }
-      const uint8_t* vt = sm.v[jl % kBufs];
+      lds_sync();   // fp16 V tile jl complete
+      const uint8_t* vt = sm.v16[jl & 1];
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const v8i vo = v_operand(vt, lo, db);
-        st.acc[db] = mfma_fp8(vo, pt.hi, st.acc[db], pt.sc_hi);
-        st.acc[db] = mfma_fp8(vo, pt.lo, st.acc[db], pt.sc_lo);
-      }
+      for (int n = 0; n < NDB * 4; ++n)
+        st.acc[n % NDB] = mfma_f16(v_operand(vt, lo, n % NDB, n / NDB), p_operand(pt, n / NDB), st.acc[n % NDB]);
     };
     for (int j = 0;;) {
       step(j, pa, pb);
