@@ -271,12 +271,10 @@ __device__ inline uint32_t row_max16(uint32_t m) {
   return m;
 }
 
-// Per-slot factors of the tile in K buffer b, and zeroed K bytes for its invalid slots (so that
-// whatever they hold -- NaN codes included -- never reaches a product).  Wavefronts 0-3 (one per
-// SIMD) take 32 slots each, one per lane of their first half; the zeroing is shared by all.
+// Per-slot factors of the tile in K buffer b.  Wavefronts 0-3 (one per SIMD) take 32 slots
+// each, one per lane of their first half.
 template <int D>
-__device__ inline void prep_tile(Smem<D>& sm, int b, const TileValid& tvd, float c0, int tid) {
-  constexpr int NCH = D / 16;
+__device__ inline void tile_factors(Smem<D>& sm, int b, const TileValid& tvd, float c0, int tid) {
   const int lane = tid & 63;
   if (tid < 4 * 64 && lane < 32) {
     const int u = (tid >> 6) * 32 + lane;
@@ -290,12 +288,17 @@ __device__ inline void prep_tile(Smem<D>& sm, int b, const TileValid& tvd, float
     if (lane == 0) sm.uni[b][u >> 5] = all_same ? 1 : 0;
     if (tid == 0) sm.full[b] = tvd.count() == kTile ? 1 : 0;
   }
-  if (tvd.count() < kTile) {
-    uint8_t* kw = sm.k[b];
-    for (int c = tid; c < kTile * NCH; c += kThreads) {   // 16-byte units of the K tile
-      const int li = c & 15, bb = c / (16 * (D / 32)) / 2;
-      if (!tvd.has(32 * (li >> 2) + 4 * bb + (li & 3))) *reinterpret_cast<uint4*>(kw + c * 16) = make_uint4(0, 0, 0, 0);
-    }
+}
+
+// Zeroed K bytes for the invalid slots of the tile in K buffer b (so that whatever they hold --
+// NaN codes included -- never reaches a product); tiles with invalid slots only.
+template <int D>
+__device__ inline void zero_invalid_k(Smem<D>& sm, int b, const TileValid& tvd, int tid) {
+  constexpr int NCH = D / 16;
+  uint8_t* kw = sm.k[b];
+  for (int c = tid; c < kTile * NCH; c += kThreads) {   // 16-byte units of the K tile
+    const int li = c & 15, bb = c / (16 * (D / 32)) / 2;
+    if (!tvd.has(32 * (li >> 2) + 4 * bb + (li & 3))) *reinterpret_cast<uint4*>(kw + c * 16) = make_uint4(0, 0, 0, 0);
   }
 }
 
@@ -306,33 +309,30 @@ __device__ inline void prep_tile(Smem<D>& sm, int b, const TileValid& tvd, float
 // (db, 2r + 1), where piece (db, kb) of lane (g, li) -- slots 32g + 8kb .. +7 of channel
 // 16db + li, 8 fp16 values -- sits at byte ((db*4 + kb)*64 + g*16 + li) * 16.  Each thread widens
 // the units its own tile copy brought in (unit (j*8 + w)*64 + lane), so its own wait for that
-// copy suffices; the fp16 tile is read by other wavefronts only after the next barrier.
+// copy suffices; the fp16 tile is read by other wavefronts only after the next barrier.  One
+// call widens unit j of the thread's kLoads units.
 template <int D>
-__device__ inline void widen_v(Smem<D>& sm, int b, int bf, int w, int lane) {
-  constexpr int kLoads = (D * kTile / 16) / kThreads;
+__device__ inline void widen_unit(Smem<D>& sm, int b, int bf, int j, int w, int lane) {
   const bool full = __builtin_amdgcn_readfirstlane(sm.full[bf]) != 0;
+  const int c = (j * kWaves + w) * 64 + lane;
+  const uint4 x = *reinterpret_cast<const uint4*>(&sm.v8[b][c * 16]);
+  const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+  uint32_t h[8];
 #pragma unroll
-  for (int j = 0; j < kLoads; ++j) {
-    const int c = (j * kWaves + w) * 64 + lane;
-    const uint4 x = *reinterpret_cast<const uint4*>(&sm.v8[b][c * 16]);
-    const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
-    uint32_t h[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      h[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(int(xw[i]), 1.0f, false));
-      h[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(int(xw[i]), 1.0f, true));
-    }
-    const int li = c & 15, g = (c >> 4) & 3, r = (c >> 6) & 1, db = c >> 7;
-    if (!full) {
-      const float* ivu = &sm.iv[bf][32 * g + 16 * r];
-#pragma unroll
-      for (int kk = 0; kk < 16; ++kk)
-        if (ivu[kk] == 0.0f) h[kk >> 1] &= (kk & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-    }
-    const int o0 = ((db * 4 + 2 * r) * 64 + g * 16 + li) * 16;
-    *reinterpret_cast<uint4*>(&sm.v16[b][o0]) = make_uint4(h[0], h[1], h[2], h[3]);
-    *reinterpret_cast<uint4*>(&sm.v16[b][o0 + 1024]) = make_uint4(h[4], h[5], h[6], h[7]);
+  for (int i = 0; i < 4; ++i) {
+    h[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(int(xw[i]), 1.0f, false));
+    h[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(int(xw[i]), 1.0f, true));
   }
+  const int li = c & 15, g = (c >> 4) & 3, r = (c >> 6) & 1, db = c >> 7;
+  if (!full) {
+    const float* ivu = &sm.iv[bf][32 * g + 16 * r];
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk)
+      if (ivu[kk] == 0.0f) h[kk >> 1] &= (kk & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+  }
+  const int o0 = ((db * 4 + 2 * r) * 64 + g * 16 + li) * 16;
+  *reinterpret_cast<uint4*>(&sm.v16[b][o0]) = make_uint4(h[0], h[1], h[2], h[3]);
+  *reinterpret_cast<uint4*>(&sm.v16[b][o0 + 1024]) = make_uint4(h[4], h[5], h[6], h[7]);
 }
 
 // Per-lane LDS byte offsets (within one buffer) of a lane's A operands: half r of score block bb
@@ -387,7 +387,8 @@ __device__ inline v8h p_operand(const PTile& p, int kb) {
 // One pipeline step of a wavefront:
 //   softmax of tile k   (raw scores s; factors in LDS buffer bk) -> probabilities pc
 //   PV of tile k-1      (probabilities pp; fp16 V in LDS buffer bp), interleaved with the softmax
-//   QK of tile k+1      (K in LDS buffer bn) -> raw scores, into s
+//   QK of tile k+1      (K in LDS buffer bn) -> raw scores, into s, block by block as the
+//                       softmax frees them
 // The PV products do not depend on tile k, so the matrix cores work while the vector units
 // form tile k's probabilities.  A rescale found by tile k's max is applied to the accumulator
 // after the PV of tile k-1, whose probabilities were formed against the old max.
@@ -395,20 +396,34 @@ __device__ inline v8h p_operand(const PTile& p, int kb) {
 // Per score (slot j, query i):  t = raw * ck_j + nb_j, the log2-domain score plus log2 of the
 // slot's V scale; P' = 2^(t - m) goes to the PV product (with V decoded but not scaled) and
 // P' * iv_j = 2^(score - m) to the row sum.  The running max m tracks max t.
-template <int D>
+template <int D, class Bg>
 __device__ __forceinline__ void pipeline_step(const Smem<D>& sm, int bk, int bp, int bn, int g,
                                               const LaneOffs& lo, const v8i& qop, v4f (&sc)[8],
-                                              const PTile& pp, PTile& pc, RowState<D>& st) {
+                                              const PTile& pp, PTile& pc, RowState<D>& st, Bg&& bg) {
   constexpr int NDB = D / 16;
-  constexpr int NPV = NDB / 2;   // PV products per score block: NDB * 4 over 8 blocks
   const uint8_t* vt = sm.v16[bp];
   const uint8_t* kt = sm.k[bn];
+  constexpr int kEarly = 8;   // PV products issued before the max (they do not depend on it)
+  static_assert((NDB * 4 - kEarly) % 8 == 0, "the other products spread evenly over 8 blocks");
+
+  // ---- PV(k-1), first products: product n takes channel block n % NDB and slot block n / NDB,
+  // so consecutive products accumulate into different blocks.  V operands are read from LDS
+  // one product ahead.
+  v8h vo_n = v_operand(vt, lo, 0, 0);
+  auto pv = [&](int n) {
+    const v8h vo = vo_n;
+    if (n + 1 < NDB * 4) vo_n = v_operand(vt, lo, (n + 1) % NDB, (n + 1) / NDB);
+    st.acc[n % NDB] = mfma_f16(vo, p_operand(pp, n / NDB), st.acc[n % NDB]);
+  };
+#pragma unroll
+  for (int n = 0; n < kEarly; ++n) pv(n);
 
   // ---- tile k: scores with their factors, max, rescale decision.  A uniform tile (all slots
   // valid, one K scale, one V scale) keeps its raw scores: t = raw * c + b for every slot.
   const int4 un = *reinterpret_cast<const int4*>(&sm.uni[bk][0]);
+  const bool uniform = __builtin_amdgcn_readfirstlane(un.x & un.y & un.z & un.w) != 0;
   float cf = 1.0f, bf = 0.0f, tmax;
-  if (un.x & un.y & un.z & un.w) {
+  if (uniform) {
     cf = sm.ck[bk][0];
     bf = sm.nb[bk][0];
     float rmax = sc[0][0];
@@ -441,22 +456,16 @@ __device__ __forceinline__ void pipeline_step(const Smem<D>& sm, int bk, int bp,
   }
   const float bm = bf - (st.m == -INFINITY ? 0.0f : st.m);   // P' = 2^(s * cf + bm)
 
-  // ---- PV(k-1) interleaved with tile k's probabilities: product n takes channel block n % NDB
-  // and slot block n / NDB, so consecutive products accumulate into different blocks.  V
-  // operands are read from LDS one product ahead; the scheduling barriers keep the blocks in
-  // order so that few are live.
+  // ---- the rest of PV(k-1) interleaved with tile k's probabilities; the scheduling barriers
+  // keep the blocks in order so that few values are live.
   float lsum = 0.0f;
-  v8h vo_n = v_operand(vt, lo, 0, 0);
-  auto pv = [&](int n) {
-    const v8h vo = vo_n;
-    if (n + 1 < NDB * 4) vo_n = v_operand(vt, lo, (n + 1) % NDB, (n + 1) / NDB);
-    st.acc[n % NDB] = mfma_f16(vo, p_operand(pp, n / NDB), st.acc[n % NDB]);
-  };
+  constexpr int kLate = (NDB * 4 - kEarly) / 8;   // products per softmax block
+  v8i ko_n = k_operand<D>(kt, lo, 0, g);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int s8 = 0; s8 < 8; ++s8) {
 #pragma unroll
-    for (int i = 0; i < (NPV + 1) / 2; ++i) pv(s8 * NPV + i);
+    for (int i = 0; i < (kLate + 1) / 2; ++i) pv(kEarly + s8 * kLate + i);
     const float4 iv = *reinterpret_cast<const float4*>(&sm.iv[bk][32 * g + 4 * s8]);
     const float ivr[4] = {iv.x, iv.y, iv.z, iv.w};
     float p[4];
@@ -471,19 +480,18 @@ __device__ __forceinline__ void pipeline_step(const Smem<D>& sm, int bk, int bp,
     asm volatile("" : "+v"(h0), "+v"(h1), "+v"(lsum));
     pc.w[2 * s8] = h0;
     pc.w[2 * s8 + 1] = h1;
+    bg(s8);
 #pragma unroll
-    for (int i = (NPV + 1) / 2; i < NPV; ++i) pv(s8 * NPV + i);
+    for (int i = (kLate + 1) / 2; i < kLate; ++i) pv(kEarly + s8 * kLate + i);
+    // QK(k+1) of score block s8: its raw scores replace the ones this block just consumed
+    {
+      const v8i ko = ko_n;
+      if (s8 + 1 < 8) ko_n = k_operand<D>(kt, lo, s8 + 1, g);
+      sc[s8] = mfma_fp8(ko, qop, v4f{0.0f, 0.0f, 0.0f, 0.0f});
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- QK(k+1): the raw scores of the next tile replace this tile's
-  v8i ko_n = k_operand<D>(kt, lo, 0, g);
-#pragma unroll
-  for (int bb = 0; bb < 8; ++bb) {
-    const v8i ko = ko_n;
-    if (bb + 1 < 8) ko_n = k_operand<D>(kt, lo, bb + 1, g);
-    sc[bb] = mfma_fp8(ko, qop, v4f{0.0f, 0.0f, 0.0f, 0.0f});
-  }
   if (need) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) st.acc[db] *= alpha;
@@ -596,7 +604,8 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
     lds_sync();
     {
       const TileValid tvd = tile_valid(phys(k0), a.ring_head, a.filled, a.slots);
-      prep_tile(sm, 0, tvd, c0, tid);
+      tile_factors(sm, 0, tvd, c0, tid);
+      if (tvd.count() < kTile) zero_invalid_k(sm, 0, tvd, tid);
     }
     lds_sync();   // also: every wavefront has read its queries out of K buffer 2
 #pragma unroll
@@ -614,16 +623,25 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
       wait_vm(n_prev);   // this thread's copies issued two steps back have landed: K tile j+1
       lds_sync();        // and V tile j; fp16 V tile j-1 complete; K buffer of j+3 free
       n_prev = 0;
-      if (j + 1 < nt) {
-        const TileValid tvn = tile_valid(phys(k0 + j + 1), a.ring_head, a.filled, a.slots);
-        prep_tile(sm, bn, tvn, c0, tid);
-        if (tvn.count() < kTile) lds_sync();   // K bytes zeroed: barrier before the QK reads them
+      const bool next = j + 1 < nt;
+      const TileValid tvn = tile_valid(phys(k0 + (next ? j + 1 : j)), a.ring_head, a.filled, a.slots);
+      if (next && tvn.count() < kTile) {
+        zero_invalid_k(sm, bn, tvn, tid);
+        lds_sync();   // K bytes zeroed: barrier before the QK reads them
       }
-      pipeline_step<D>(sm, bk, (j + 1) & 1, bn, g, lo, qop, sc, pprev, pcur, st);
-      widen_v(sm, j & 1, bk, w, lane);
-      // this step's copies go out behind its products (the buffers are free)
-      if (j + 3 < nt) { issue_k<D>(a, sm, co, (j + 3) % kBufs, phys(k0 + j + 3), head, w, lane); n_prev += nk; }
-      if (j + 2 < nt) { issue_v<D>(a, sm, j & 1, phys(k0 + j + 2), head, w, lane); n_prev += nv; }
+      // Work spread over the softmax blocks, between their products: the factors of tile j+1
+      // (read from the next step on), widening V tile j (its units first, then this thread's
+      // copy of V tile j+2 into the same units), and the copy of K tile j+3 (its buffer is
+      // free all step).
+      constexpr int kWu = (D * kTile / 16) / kThreads;
+      const bool more_k = j + 3 < nt, more_v = j + 2 < nt;
+      pipeline_step<D>(sm, bk, (j + 1) & 1, bn, g, lo, qop, sc, pprev, pcur, st, [&](int s8) {
+        if (s8 == 0 && next) tile_factors(sm, bn, tvn, c0, tid);
+        if (s8 >= 1 && s8 <= kWu) widen_unit(sm, j & 1, bk, s8 - 1, w, lane);
+        if (s8 == 3 && more_k) issue_k<D>(a, sm, co, (j + 3) % kBufs, phys(k0 + j + 3), head, w, lane);
+        if (s8 == 5 && more_v) issue_v<D>(a, sm, j & 1, phys(k0 + j + 2), head, w, lane);
+      });
+      n_prev = (more_k ? nk : 0) + (more_v ? nv : 0);
     };
     auto final_pv = [&](int jl, const PTile& pt) {   // PV of the last tile jl
       wait_vm(0);
