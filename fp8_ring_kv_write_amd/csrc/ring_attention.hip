@@ -272,18 +272,37 @@ __device__ inline uint32_t row_max16(uint32_t m) {
 }
 
 // Per-slot factors of the tile in K buffer b.  Wavefronts 0-3 (one per SIMD) take 32 slots
-// each, one per lane of their first half.
+// each, one per lane of their first half.  Split in two so that the LDS reads can be issued well
+// before the arithmetic that needs them: factor_inputs, then tile_factors.
+struct FactorIn {
+  float ks, vs, ks0, vs0;
+};
+
 template <int D>
-__device__ inline void tile_factors(Smem<D>& sm, int b, const TileValid& tvd, float c0, int tid) {
+__device__ inline FactorIn factor_inputs(const Smem<D>& sm, int b, int tid) {
+  FactorIn f{0.0f, 0.0f, 0.0f, 0.0f};
+  const int lane = tid & 63;
+  if (tid < 4 * 64 && lane < 32) {
+    const int u = (tid >> 6) * 32 + lane;
+    f.ks = sm.ks[b][u];
+    f.vs = sm.vs[b][u];
+    f.ks0 = sm.ks[b][0];
+    f.vs0 = sm.vs[b][0];
+  }
+  return f;
+}
+
+template <int D>
+__device__ inline void tile_factors(Smem<D>& sm, int b, const TileValid& tvd, float c0, int tid,
+                                    const FactorIn& f) {
   const int lane = tid & 63;
   if (tid < 4 * 64 && lane < 32) {
     const int u = (tid >> 6) * 32 + lane;
     const bool ok = tvd.has(u);
-    const float ksu = sm.ks[b][u], vsu = sm.vs[b][u];
-    sm.ck[b][u] = ok ? c0 * ksu : 0.0f;
-    sm.nb[b][u] = ok ? __log2f(vsu) : -INFINITY;
-    sm.iv[b][u] = ok ? __builtin_amdgcn_rcpf(vsu) : 0.0f;
-    const bool same = ok && ksu == sm.ks[b][0] && vsu == sm.vs[b][0];
+    sm.ck[b][u] = ok ? c0 * f.ks : 0.0f;
+    sm.nb[b][u] = ok ? __log2f(f.vs) : -INFINITY;
+    sm.iv[b][u] = ok ? __builtin_amdgcn_rcpf(f.vs) : 0.0f;
+    const bool same = ok && f.ks == f.ks0 && f.vs == f.vs0;
     const bool all_same = __all(same);   // over this wavefront's 32 active lanes
     if (lane == 0) sm.uni[b][u >> 5] = all_same ? 1 : 0;
     if (tid == 0) sm.full[b] = tvd.count() == kTile ? 1 : 0;
@@ -309,13 +328,18 @@ __device__ inline void zero_invalid_k(Smem<D>& sm, int b, const TileValid& tvd, 
 // (db, 2r + 1), where piece (db, kb) of lane (g, li) -- slots 32g + 8kb .. +7 of channel
 // 16db + li, 8 fp16 values -- sits at byte ((db*4 + kb)*64 + g*16 + li) * 16.  Each thread widens
 // the units its own tile copy brought in (unit (j*8 + w)*64 + lane), so its own wait for that
-// copy suffices; the fp16 tile is read by other wavefronts only after the next barrier.  One
-// call widens unit j of the thread's kLoads units.
+// copy suffices; the fp16 tile is read by other wavefronts only after the next barrier.  Unit
+// j of the thread's kLoads units is read by widen_load and converted and stored by widen_store.
 template <int D>
-__device__ inline void widen_unit(Smem<D>& sm, int b, int bf, int j, int w, int lane) {
+__device__ inline uint4 widen_load(const Smem<D>& sm, int b, int j, int w, int lane) {
+  const int c = (j * kWaves + w) * 64 + lane;
+  return *reinterpret_cast<const uint4*>(&sm.v8[b][c * 16]);
+}
+
+template <int D>
+__device__ inline void widen_store(Smem<D>& sm, int b, int bf, int j, int w, int lane, const uint4& x) {
   const bool full = __builtin_amdgcn_readfirstlane(sm.full[bf]) != 0;
   const int c = (j * kWaves + w) * 64 + lane;
-  const uint4 x = *reinterpret_cast<const uint4*>(&sm.v8[b][c * 16]);
   const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
   uint32_t h[8];
 #pragma unroll
@@ -604,7 +628,7 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
     lds_sync();
     {
       const TileValid tvd = tile_valid(phys(k0), a.ring_head, a.filled, a.slots);
-      tile_factors(sm, 0, tvd, c0, tid);
+      tile_factors(sm, 0, tvd, c0, tid, factor_inputs(sm, 0, tid));
       if (tvd.count() < kTile) zero_invalid_k(sm, 0, tvd, tid);
     }
     lds_sync();   // also: every wavefront has read its queries out of K buffer 2
@@ -635,9 +659,17 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
       // free all step).
       constexpr int kWu = (D * kTile / 16) / kThreads;
       const bool more_k = j + 3 < nt, more_v = j + 2 < nt;
+      uint4 vx[kWu];
+      FactorIn fin;
       pipeline_step<D>(sm, bk, (j + 1) & 1, bn, g, lo, qop, sc, pprev, pcur, st, [&](int s8) {
-        if (s8 == 0 && next) tile_factors(sm, bn, tvn, c0, tid);
-        if (s8 >= 1 && s8 <= kWu) widen_unit(sm, j & 1, bk, s8 - 1, w, lane);
+        // LDS reads a block ahead of the arithmetic that needs them
+        if (s8 == 0) {
+#pragma unroll
+          for (int u = 0; u < kWu; ++u) vx[u] = widen_load(sm, j & 1, u, w, lane);
+          if (next) fin = factor_inputs(sm, bn, tid);
+        }
+        if (s8 == 1 && next) tile_factors(sm, bn, tvn, c0, tid, fin);
+        if (s8 >= 2 && s8 < 2 + kWu) widen_store(sm, j & 1, bk, s8 - 2, w, lane, vx[s8 - 2]);
         if (s8 == 3 && more_k) issue_k<D>(a, sm, co, (j + 3) % kBufs, phys(k0 + j + 3), head, w, lane);
         if (s8 == 5 && more_v) issue_v<D>(a, sm, j & 1, phys(k0 + j + 2), head, w, lane);
       });
