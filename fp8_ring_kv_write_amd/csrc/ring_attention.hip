@@ -432,11 +432,12 @@ __device__ __forceinline__ void pipeline_step(const Smem<D>& sm, int bk, int bp,
 
   // ---- PV(k-1), first products: product n takes channel block n % NDB and slot block n / NDB,
   // so consecutive products accumulate into different blocks.  V operands are read from LDS
-  // one product ahead.
-  v8h vo_n = v_operand(vt, lo, 0, 0);
+  // two products ahead.
+  v8h vo_n = v_operand(vt, lo, 0, 0), vo_nn = v_operand(vt, lo, 1 % NDB, 1 / NDB);
   auto pv = [&](int n) {
     const v8h vo = vo_n;
-    if (n + 1 < NDB * 4) vo_n = v_operand(vt, lo, (n + 1) % NDB, (n + 1) / NDB);
+    vo_n = vo_nn;
+    if (n + 2 < NDB * 4) vo_nn = v_operand(vt, lo, (n + 2) % NDB, (n + 2) / NDB);
     st.acc[n % NDB] = mfma_f16(vo, p_operand(pp, n / NDB), st.acc[n % NDB]);
   };
 #pragma unroll
