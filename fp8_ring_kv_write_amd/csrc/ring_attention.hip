@@ -322,8 +322,9 @@ __device__ inline void zero_invalid_k(Smem<D>& sm, int b, const TileValid& tvd, 
 }
 
 // Widening of the FP8 V tile in v8[b] to fp16 in v16[b], in the PV product's operand order, with
-// the invalid slots' values zeroed (a slot is valid exactly when its factor iv, in K buffer bf,
-// is non-zero: 1 / v_scale is finite and positive for every scale a write can store).  FP8 unit ((db*2 + r)*4 + g)*16 + li holds slots 32g + 16r ..
+// the invalid slots' values zeroed when the tile is not full (a slot is valid exactly when its
+// factor iv, in K buffer bf, is non-zero: 1 / v_scale is finite and positive for every scale a
+// write can store).  FP8 unit ((db*2 + r)*4 + g)*16 + li holds slots 32g + 16r ..
 // +15 of channel 16db + li; its first 8 slots become piece (db, kb = 2r) and its last 8 piece
 // (db, 2r + 1), where piece (db, kb) of lane (g, li) -- slots 32g + 8kb .. +7 of channel
 // 16db + li, 8 fp16 values -- sits at byte ((db*4 + kb)*64 + g*16 + li) * 16.  Each thread widens
@@ -337,8 +338,8 @@ __device__ inline uint4 widen_load(const Smem<D>& sm, int b, int j, int w, int l
 }
 
 template <int D>
-__device__ inline void widen_store(Smem<D>& sm, int b, int bf, int j, int w, int lane, const uint4& x) {
-  const bool full = __builtin_amdgcn_readfirstlane(sm.full[bf]) != 0;
+__device__ inline void widen_store(Smem<D>& sm, int b, int bf, int j, int w, int lane, const uint4& x,
+                                   bool full) {
   const int c = (j * kWaves + w) * 64 + lane;
   const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
   uint32_t h[8];
@@ -661,6 +662,8 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
       constexpr int kWu = (D * kTile / 16) / kThreads;
       const bool more_k = j + 3 < nt, more_v = j + 2 < nt;
       uint4 vx[kWu];
+      // read here, once: a read inside the blocks would wait for every operand read before it
+      const bool vfull = __builtin_amdgcn_readfirstlane(sm.full[bk]) != 0;
       FactorIn fin;
       pipeline_step<D>(sm, bk, (j + 1) & 1, bn, g, lo, qop, sc, pprev, pcur, st, [&](int s8) {
         // LDS reads a block ahead of the arithmetic that needs them
@@ -670,7 +673,7 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
           if (next) fin = factor_inputs(sm, bn, tid);
         }
         if (s8 == 1 && next) tile_factors(sm, bn, tvn, c0, tid, fin);
-        if (s8 >= 2 && s8 < 2 + kWu) widen_store(sm, j & 1, bk, s8 - 2, w, lane, vx[s8 - 2]);
+        if (s8 >= 2 && s8 < 2 + kWu) widen_store(sm, j & 1, bk, s8 - 2, w, lane, vx[s8 - 2], vfull);
         if (s8 == 3 && more_k) issue_k<D>(a, sm, co, (j + 3) % kBufs, phys(k0 + j + 3), head, w, lane);
         if (s8 == 5 && more_v) issue_v<D>(a, sm, j & 1, phys(k0 + j + 2), head, w, lane);
       });
