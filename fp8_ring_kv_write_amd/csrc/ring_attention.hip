@@ -741,44 +741,63 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
   }
 }
 
-// Merge of split rows: thread = (query of a row, 4 channels); rows held by one work-group were
-// written directly by attn_stream and are skipped.  Segments are merged in order.
+// Merge of split rows: thread = (query of a row, 8 channels); rows held by one work-group were
+// written directly by attn_stream and are skipped.  A row has at most 8 segments (make_plan);
+// every load of a thread is issued before any arithmetic (one memory round trip), and the
+// segments are merged in order.
+typedef _Float16 v8hc __attribute__((ext_vector_type(8)));
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
+  constexpr int kMaxSeg = 8;
   const int row = blockIdx.y;
   const UnitSplit split{a.tv, a.seg_cost, a.cost, a.grid};
-  const auto owner = [&](int64_t u) -> int { return split.owner(u); };
-  const int first = owner((int64_t)row * a.tv);
-  const int nseg = owner((int64_t)row * a.tv + a.tv - 1) - first + 1;
+  const int first = split.owner((int64_t)row * a.tv);
+  const int nseg = split.owner((int64_t)row * a.tv + a.tv - 1) - first + 1;
   if (nseg <= 1) return;
   const int item = blockIdx.x * 256 + threadIdx.x;
-  const int ql = item / (D / 4), c4 = item % (D / 4);
+  const int ql = item / (D / 8), c8 = item % (D / 8);
   if (ql >= kRowQ) return;
   const int head = row / a.qtiles, qt = row % a.qtiles;
   const int i = qt * kRowQ + ql;
   if (i >= a.nq) return;
   const int64_t base = (int64_t)row * a.max_seg * kRowQ + ql;
-  float mx = -INFINITY;
-  for (int sgi = 0; sgi < nseg; ++sgi) mx = __builtin_fmaxf(mx, a.part_ml[(base + (int64_t)sgi * kRowQ) * 2]);
-  float l = 0.0f, o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (mx != -INFINITY) {
-    for (int sgi = 0; sgi < nseg; ++sgi) {
+  float2 ml[kMaxSeg];
+  v8hc oz[kMaxSeg];
+#pragma unroll
+  for (int sgi = 0; sgi < kMaxSeg; ++sgi) {
+    if (sgi < nseg) {
       const int64_t sl = base + (int64_t)sgi * kRowQ;
-      const float wz = __builtin_amdgcn_exp2f(a.part_ml[sl * 2] - mx) * a.part_ml[sl * 2 + 1];
-      l += wz;
-      const v4h oz = *reinterpret_cast<const v4h*>(a.part_o + sl * D + 4 * c4);
-      o[0] += wz * float(oz[0]);
-      o[1] += wz * float(oz[1]);
-      o[2] += wz * float(oz[2]);
-      o[3] += wz * float(oz[3]);
+      ml[sgi] = *reinterpret_cast<const float2*>(a.part_ml + sl * 2);
+      oz[sgi] = *reinterpret_cast<const v8hc*>(a.part_o + sl * D + 8 * c8);
+    }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int sgi = 0; sgi < kMaxSeg; ++sgi)
+    if (sgi < nseg) mx = __builtin_fmaxf(mx, ml[sgi].x);
+  float l = 0.0f, o[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  if (mx != -INFINITY) {
+#pragma unroll
+    for (int sgi = 0; sgi < kMaxSeg; ++sgi) {
+      if (sgi < nseg) {
+        const float wz = __builtin_amdgcn_exp2f(ml[sgi].x - mx) * ml[sgi].y;
+        l += wz;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o[c] += wz * float(oz[sgi][c]);
+      }
     }
   }
   const float il = l > 0.0f ? 1.0f / l : 0.0f;
-  uint16_t* dst = a.out + ((int64_t)i * a.heads + head) * D + 4 * c4;
-  const uint32_t lo = uint32_t(f32_to_bf16(o[0] * il)) | (uint32_t(f32_to_bf16(o[1] * il)) << 16);
-  const uint32_t hi = uint32_t(f32_to_bf16(o[2] * il)) | (uint32_t(f32_to_bf16(o[3] * il)) << 16);
-  *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
-  if (c4 == 0) a.lse[(int64_t)head * a.nq + i] = l > 0.0f ? (mx + __log2f(l)) * kLn2 : -INFINITY;
+  uint16_t* dst = a.out + ((int64_t)i * a.heads + head) * D + 8 * c8;
+  uint32_t wv[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    wv[c] = uint32_t(f32_to_bf16(o[2 * c] * il)) | (uint32_t(f32_to_bf16(o[2 * c + 1] * il)) << 16);
+  // out is 8-byte aligned (its documented alignment): two 8-byte stores
+  *reinterpret_cast<uint2*>(dst) = make_uint2(wv[0], wv[1]);
+  *reinterpret_cast<uint2*>(dst + 4) = make_uint2(wv[2], wv[3]);
+  if (c8 == 0) a.lse[(int64_t)head * a.nq + i] = l > 0.0f ? (mx + __log2f(l)) * kLn2 : -INFINITY;
 }
 
 struct Plan {
@@ -969,7 +988,7 @@ hipError_t launch_attention(const kv_ring_desc& r, int32_t ring_head, int32_t fi
     split = us.owner((int64_t)row * a.tv + a.tv - 1) != us.owner((int64_t)row * a.tv);
   }
   if (!split) return e;
-  dim3 gc((kRowQ * r.head_dim / 4 + 255) / 256, p.rows);
+  dim3 gc((kRowQ * r.head_dim / 8 + 255) / 256, p.rows);
   if (r.head_dim == 128)
     hipLaunchKernelGGL(attn_combine<128>, gc, dim3(256), 0, stream, a);
   else
