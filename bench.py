@@ -58,8 +58,8 @@ ATT_KERNEL = "attn_stream<128>"
 # (FETCH_SIZE, WRITE_SIZE) over this workload, each divided by the factor the same counter
 # reads for a torch copy of --calibrate-copy bytes.  Valid only for the kernel sources whose
 # hash is recorded; reported as null otherwise.
-ATT_TRAFFIC = {"sources": "14b454df175bfbaa", "bytes": 131_440_000,
-               "read_bytes": 118_460_000, "write_bytes": 12_980_000}
+ATT_TRAFFIC = {"sources": "ff08af58f5635b40", "bytes": 128_350_000,
+               "read_bytes": 115_370_000, "write_bytes": 12_980_000}
 WRITE_BYTES = 2 * N * H * D * 2 + 2 * N * H * D + 2 * N * H * 4
 ROTATE_BYTES = 2 * (H * S * D + H * S * 4)
 
@@ -477,7 +477,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3",
+        "dtype": "fp8e4m3+fp16",   # E4M3 cache and QK product; fp16 P and widened V in PV
         "data": "synthetic: seeded N(0,1) bfloat16 Q/K/V, ring pre-filled by 8 writes",
         "config": {
             "workload": "one layer call: kv_ring_write of 757 tokens + ring_attention of 757 queries "
