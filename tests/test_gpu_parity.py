@@ -11,7 +11,8 @@ import pytest
 
 import oracle
 from workloads import (normal_bf16, student_t_outlier_bf16, outlier_channels, tensor_seed,
-                       tiny_schedule, steady_ring_schedule, ROPE_POSITIONS)
+                       tiny_schedule, steady_ring_schedule, ROPE_POSITIONS, bf16_bits_from_f32,
+                       f32_from_bf16_bits)
 
 from kvhelpers import (ring_to_host, to_dev_bf16, bf16_dev_to_f64, attention_errors,
                        poison_free_slots_gpu, mfma_lse_bound)
@@ -290,6 +291,33 @@ def test_attention_ignores_poisoned_free_slots(kv, torch):
     out1, lse1, _, _ = p.attend(q, sched[-1].pos0, 1 / math.sqrt(128))
     assert np.array_equal(out0, out1) and np.array_equal(lse0, lse1)
     check_attention(out1, lse1, ro, rl, label="poisoned")
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_attention_mixed_write_scales(kv, torch, d):
+    """A ring whose writes differ in scale by orders of magnitude, with write boundaries inside
+    tiles: N(0,1) writes, an all-zero write (its scales at the absmax floor, 2^-100 / 448), a
+    write with K x4 and V x1000 and one with V x1e-3.  The attention forms its probabilities
+    against the running max of score plus log2 of the slot's V scale, so slots of very
+    different V scales meet in one tile and across tiles."""
+    H, S, n = 3, 700, 100
+    p = Pair(kv, torch, H, S, d)
+    sched = steady_ring_schedule(S, n, 8)          # 800 tokens: the last write wraps
+    for c, w in enumerate(sched):
+        k = normal_bf16(tensor_seed("mixed_scales", d, c, 1), (n, H, d))
+        v = normal_bf16(tensor_seed("mixed_scales", d, c, 2), (n, H, d))
+        if c == 2:
+            k[:] = 0
+            v[:] = 0
+        elif c == 4:
+            k = bf16_bits_from_f32(f32_from_bf16_bits(k) * np.float32(4.0))
+            v = bf16_bits_from_f32(f32_from_bf16_bits(v) * np.float32(1000.0))
+        elif c == 6:
+            v = bf16_bits_from_f32(f32_from_bf16_bits(v) * np.float32(1e-3))
+        p.write(k, v, w.start_slot, w.pos0)
+    p.assert_same("mixed write scales")
+    q = normal_bf16(tensor_seed("mixed_scales", d, 99, 0), (150, H, d))
+    check_attention(*p.attend(q, sched[-1].pos0, 1 / math.sqrt(d)), label=f"mixed write scales d{d}")
 
 
 def test_attention_empty_ring_and_no_queries(kv, torch):
