@@ -88,15 +88,43 @@ __device__ inline void scale_from_absmax(float amax, float& scale, float& inv) {
   inv = kE4M3Max / a;
 }
 
-// Max over a work-group of 256 threads; `red` is LDS scratch of >= 4 floats.  Every thread
-// gets the result.
+// Max over the 64 lanes of a wavefront, every lane receiving it, by lane moves only (DPP within
+// rows of 16 lanes, then permlane swaps across rows): no LDS traffic and no barrier.  fmaxf
+// semantics: a NaN operand is ignored.
+__device__ inline float wave_max(float v) {
+  auto dpp = [](float x, int ctrl) -> float {
+    switch (ctrl) {   // the control must be a constant
+      case 0: return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0xB1, 0xF, 0xF, false));
+      case 1: return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x4E, 0xF, 0xF, false));
+      case 2: return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x141, 0xF, 0xF, false));
+      default: return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x140, 0xF, 0xF, false));
+    }
+  };
+  v = __builtin_fmaxf(v, dpp(v, 0));   // lane ^ 1
+  v = __builtin_fmaxf(v, dpp(v, 1));   // lane ^ 2
+  v = __builtin_fmaxf(v, dpp(v, 2));   // 7 - lane (of 8)
+  v = __builtin_fmaxf(v, dpp(v, 3));   // 15 - lane (of 16): every lane of a row holds its max
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __builtin_fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __builtin_fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Max over a work-group of 256 threads; `red` is LDS scratch of >= 4 floats used by this call
+// only (no other call may share it).  Every thread gets the result.
 __device__ inline float block_max_256(float v, float* red) {
-  for (int off = 32; off > 0; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, 64));
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = v;
+  v = wave_max(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   return __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+}
+
+// Max of n floats at p (n small: a list of partial maxima), computed by every wavefront on its
+// own; every lane gets it.  No barrier.
+__device__ inline float list_max(const float* __restrict__ p, int n) {
+  float m = 0.0f;
+  for (int j = threadIdx.x & 63; j < n; j += 64) m = __builtin_fmaxf(m, p[j]);
+  return wave_max(m);
 }
 
 // Whether `slot` holds a token of the ring whose valid interval is the `filled` slots just
