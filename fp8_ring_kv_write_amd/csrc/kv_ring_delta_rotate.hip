@@ -115,13 +115,15 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void rotate_requantize(
     uint8_t* __restrict__ kc, float* __restrict__ k_scale, RotGeom g, DeltaTable tab,
     const float* __restrict__ partial) {
+  __shared__ float red[4];
   const int t = blockIdx.x, h = blockIdx.y;
   uint8_t* tile = kc + ((int64_t)h * g.tiles + t) * kTile * D;
   float* srow = k_scale + (int64_t)h * g.slots;
   Units<D> x;
   load_units<D>(tile, srow, t, g, x);
-  // the head's new absmax: each wavefront reduces the per-tile partials itself
-  const float a = list_max(partial + (int64_t)h * g.tiles, int(g.tiles));
+  // the head's new absmax from the per-tile partials (rings of up to 64 tiles: each wavefront
+  // reduces them itself)
+  const float a = list_max(partial + (int64_t)h * g.tiles, int(g.tiles), red);
   __syncthreads();   // every thread's reads of the old slot scales precede the writes below
   float scale, inv;
   scale_from_absmax(a, scale, inv);

@@ -144,6 +144,7 @@ struct QuantQArgs {
 template <int D>
 __device__ inline void write_chunk(const WriteArgs& wa, const float* __restrict__ rope, int blk, int h) {
   constexpr int CPT = D / 8;
+  __shared__ float red[2][4];
   __shared__ __align__(16) uint8_t vlds[kChunk][D];
   const WriteGeom& g = wa.g;
   const uint16_t* __restrict__ k_new = wa.k_new;
@@ -173,10 +174,10 @@ __device__ inline void write_chunk(const WriteArgs& wa, const float* __restrict_
     for (int j = 0; j < CPT / 4; ++j) tab[j] = t4[j];
   }
 
-  // the write's per-head absmax of K' and V from the pass-1 partials (each wavefront reduces
-  // the short partial lists itself: no barrier)
-  const float ak = list_max(partial + (int64_t)h * g.n_partial_groups, g.n_partial_groups);
-  const float av = list_max(partial + ((int64_t)g.heads + h) * g.n_partial_groups, g.n_partial_groups);
+  // the write's per-head absmax of K' and V from the pass-1 partials (up to 2,048 tokens each
+  // wavefront reduces the partial lists itself, with no barrier)
+  const float ak = list_max(partial + (int64_t)h * g.n_partial_groups, g.n_partial_groups, red[0]);
+  const float av = list_max(partial + ((int64_t)g.heads + h) * g.n_partial_groups, g.n_partial_groups, red[1]);
   float sk, ik, sv, iv;
   scale_from_absmax(ak, sk, ik);
   scale_from_absmax(av, sv, iv);
@@ -252,6 +253,7 @@ __device__ inline void write_chunk(const WriteArgs& wa, const float* __restrict_
 template <int D>
 __device__ inline void quantize_q_half(const QuantQArgs& qa_, const float* __restrict__ rope, int blk,
                                        int h, int heads) {
+  __shared__ float red[4];
   const int qt = blk >> 1, w = 4 * (blk & 1) + (int(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
   const int i = qt * 128 + w * 16 + li;
@@ -266,7 +268,7 @@ __device__ inline void quantize_q_half(const QuantQArgs& qa_, const float* __res
 #pragma unroll
     for (int j = 0; j < 8; ++j) tab[j] = t4[j];
   }
-  const float a = list_max(qa_.partial + (int64_t)h * qa_.groups, qa_.groups);
+  const float a = list_max(qa_.partial + (int64_t)h * qa_.groups, qa_.groups, red);
   float scale, inv;
   scale_from_absmax(a, scale, inv);
   if (blk == 0 && threadIdx.x == 0) qa_.scale[h] = scale;

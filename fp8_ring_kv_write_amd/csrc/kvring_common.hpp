@@ -119,12 +119,18 @@ __device__ inline float block_max_256(float v, float* red) {
   return __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
 }
 
-// Max of n floats at p (n small: a list of partial maxima), computed by every wavefront on its
-// own; every lane gets it.  No barrier.
-__device__ inline float list_max(const float* __restrict__ p, int n) {
+// Max of n floats at p (a list of partial maxima), every thread of a 256-thread work-group
+// receiving it.  Lists of at most 64 entries are reduced by every wavefront on its own (one load
+// per lane, lane moves, no barrier); longer ones by the work-group (`red`: LDS scratch of >= 4
+// floats used by this call only).  The branch is uniform over the work-group.
+__device__ inline float list_max(const float* __restrict__ p, int n, float* red) {
+  if (n <= 64) {
+    const int lane = threadIdx.x & 63;
+    return wave_max(lane < n ? p[lane] : 0.0f);
+  }
   float m = 0.0f;
-  for (int j = threadIdx.x & 63; j < n; j += 64) m = __builtin_fmaxf(m, p[j]);
-  return wave_max(m);
+  for (int j = threadIdx.x; j < n; j += 256) m = __builtin_fmaxf(m, p[j]);
+  return block_max_256(m, red);
 }
 
 // Whether `slot` holds a token of the ring whose valid interval is the `filled` slots just
