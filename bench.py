@@ -31,6 +31,9 @@ Also reported (one JSON line on stdout; progress on stderr):
               bfloat16 window is copied forward by the new tokens (kv_window_advance), rotated
               and quantised whole (kv_ring_write of all 5,788 tokens), then attended; its
               cache-maintenance time per call against the ring's write;
+  hbm_copy_GBps a plain 512 MiB device-to-device copy, bytes read + written per second: the
+              achievable HBM line beside the 8 TB/s peak (write and delta_rotate give both
+              fractions);
   cpu_baseline the CPU oracle on the same step (full call), on the host's cores.
 """
 
@@ -58,8 +61,8 @@ ATT_KERNEL = "attn_stream<128>"
 # (FETCH_SIZE, WRITE_SIZE) over this workload, each divided by the factor the same counter
 # reads for a torch copy of --calibrate-copy bytes.  Valid only for the kernel sources whose
 # hash is recorded; reported as null otherwise.
-ATT_TRAFFIC = {"sources": "ff08af58f5635b40", "bytes": 128_350_000,
-               "read_bytes": 115_370_000, "write_bytes": 12_980_000}
+ATT_TRAFFIC = {"sources": "64c5e520db199e3d", "bytes": 133_040_000,
+               "read_bytes": 120_060_000, "write_bytes": 12_980_000}
 WRITE_BYTES = 2 * N * H * D * 2 + 2 * N * H * D + 2 * N * H * 4
 ROTATE_BYTES = 2 * (H * S * D + H * S * 4)
 
@@ -80,6 +83,8 @@ def main() -> int:
     ap.add_argument("--no-graph", action="store_true",
                     help="time repeated calls as issued from Python only (no graph replays; for profilers)")
     ap.add_argument("--no-sweep", action="store_true", help="skip the write-size and fill-up sweeps")
+    ap.add_argument("--no-copy-line", action="store_true",
+                    help="skip the device-copy measurement (the achievable HBM rate)")
     ap.add_argument("--no-three-axis", action="store_true",
                     help="skip the three-axis (frame, row, column) position variant")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -251,6 +256,24 @@ def main() -> int:
                                                             workspace=ws_r), 50)
     rot_gbps = ROTATE_BYTES / (rot_gpu_us * 1e-6) / 1e9
     log(f"delta rotate {rot_gpu_us:.1f} us GPU ({rot_gbps:.0f} GB/s), {rot_us:.1f} us per call issued from Python")
+
+    # ---------------------------------------------------------------- achievable HBM rate
+    # A plain device-to-device copy of 512 MiB (twice the infinity cache, so it streams from and
+    # to HBM): bytes read + written per second, the practical ceiling for the streaming kernels.
+    copy_gbps = None
+    if not args.no_copy_line:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(3)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        e0.record(stream)
+        for _ in range(10):
+            dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        copy_gbps = 2.0 * src.numel() * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        del src, dst
+        log(f"device copy of 512 MiB: {copy_gbps:.0f} GB/s (read + written)")
 
     # ---------------------------------------------------------------- cold caches
     # Between two calls on the same layer a model runs every other layer, whose rings (60 x 36 MB)
@@ -491,10 +514,13 @@ def main() -> int:
                       "calls_per_s": round(1e6 / call_us, 1)},
         "write": {"us": round(write_gpu_us, 2), "GBps": round(write_gbps, 1),
                   "frac_hbm_peak": round(write_gbps / HBM_PEAK_GBPS, 4), "bytes": WRITE_BYTES,
+                  "frac_of_copy": round(write_gbps / copy_gbps, 4) if copy_gbps else None,
                   "issued_us": round(write_us, 2)},
         "delta_rotate": {"us": round(rot_gpu_us, 2), "GBps": round(rot_gbps, 1),
                          "frac_hbm_peak": round(rot_gbps / HBM_PEAK_GBPS, 4), "bytes": ROTATE_BYTES,
+                         "frac_of_copy": round(rot_gbps / copy_gbps, 4) if copy_gbps else None,
                          "issued_us": round(rot_us, 2)},
+        "hbm_copy_GBps": round(copy_gbps, 1) if copy_gbps else None,
         "chunk": chunk,
         "cold_cache": cold,
         "write_sweep": sweep,
