@@ -127,8 +127,10 @@ struct Smem {
   float (&qs)[4];              // the head's query scale
 };
 
+// QK product, FP8 x FP8 -> fp32.  Zero scale operands select the unscaled encoding
+// (v_mfma_f32_16x16x128_f8f6f4): no operand scaling.
 __device__ inline v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
 __device__ inline v4f mfma_f16(const v8h& a, const v8h& b, const v4f& c) {
