@@ -244,17 +244,20 @@ __device__ inline void issue_v(const AttnArgs& a, Smem<D>& sm, int b, int64_t t,
 }
 
 // Wait until at most n of this thread's vector-memory operations are outstanding (they complete
-// in issue order).  n is one of the per-step copy counts (0 .. 2*kLoads + 2).
+// in issue order).  n is one of the copy counts of the tile schedule (0 .. 8: at most two K tiles
+// of kLoads + 1 copies and one V tile of kLoads copies, kLoads <= 2); any other count waits for
+// every operation.
 __device__ inline void wait_vm(int n) {
   switch (n) {   // s_waitcnt immediate: vmcnt in bits 3:0, expcnt and lgkmcnt left at their maximum
-    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
     case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
     case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
     case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
     case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
     case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
     case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+    case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
   }
 }
 
@@ -262,16 +265,6 @@ __device__ inline void wait_vm(int n) {
 // the compiler keeps memory accesses on their side of it.  Unlike __syncthreads it does not wait
 // for the asynchronous tile copies in flight (their completion is tracked with wait_vm).
 __device__ inline void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// Max over the 16 lanes of each row of a wavefront (every lane receives it): data-parallel
-// moves between lanes (DPP), no trip through LDS.
-__device__ inline uint32_t row_max16(uint32_t m) {
-  m = max(m, uint32_t(__builtin_amdgcn_update_dpp(int(m), int(m), 0xB1, 0xF, 0xF, false)));   // lane ^ 1
-  m = max(m, uint32_t(__builtin_amdgcn_update_dpp(int(m), int(m), 0x4E, 0xF, 0xF, false)));   // lane ^ 2
-  m = max(m, uint32_t(__builtin_amdgcn_update_dpp(int(m), int(m), 0x141, 0xF, 0xF, false)));  // 7 - lane (of 8)
-  m = max(m, uint32_t(__builtin_amdgcn_update_dpp(int(m), int(m), 0x140, 0xF, 0xF, false)));  // 15 - lane (of 16)
-  return m;
-}
 
 // Per-slot factors of the tile in K buffer b.  Wavefronts 0-3 (one per SIMD) take 32 slots
 // each, one per lane of their first half.  Split in two so that the LDS reads can be issued well
