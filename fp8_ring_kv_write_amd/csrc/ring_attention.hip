@@ -407,8 +407,9 @@ __device__ inline v8h p_operand(const PTile& p, int kb) {
 // One pipeline step of a wavefront:
 //   softmax of tile k   (raw scores s; factors in LDS buffer bk) -> probabilities pc
 //   PV of tile k-1      (probabilities pp; fp16 V in LDS buffer bp), interleaved with the softmax
-//   QK of tile k+1      (K in LDS buffer bn) -> raw scores, into s, block by block as the
-//                       softmax frees them
+//   QK of tile k+1      (K in LDS buffer bn) -> raw scores into the other score array (the
+//                       steps of a trip alternate the two, so no copy joins them), block by
+//                       block as the softmax frees the registers
 // The PV products do not depend on tile k, so the matrix cores work while the vector units
 // form tile k's probabilities.  A rescale found by tile k's max is applied to the accumulator
 // after the PV of tile k-1, whose probabilities were formed against the old max.
@@ -418,7 +419,7 @@ __device__ inline v8h p_operand(const PTile& p, int kb) {
 // P' * iv_j = 2^(score - m) to the row sum.  The running max m tracks max t.
 template <int D, class Bg>
 __device__ __forceinline__ void pipeline_step(const Smem<D>& sm, int bk, int bp, int bn, int g,
-                                              const LaneOffs& lo, const v8i& qop, v4f (&sc)[8],
+                                              const LaneOffs& lo, const v8i& qop, v4f (&sc)[8], v4f (&sco)[8],
                                               const PTile& pp, PTile& pc, RowState<D>& st, Bg&& bg) {
   constexpr int NDB = D / 16;
   const uint8_t* vt = sm.v16[bp];
@@ -504,11 +505,11 @@ __device__ __forceinline__ void pipeline_step(const Smem<D>& sm, int bk, int bp,
     bg(s8);
 #pragma unroll
     for (int i = (kLate + 1) / 2; i < kLate; ++i) pv(kEarly + s8 * kLate + i);
-    // QK(k+1) of score block s8: its raw scores replace the ones this block just consumed
+    // QK(k+1) of score block s8
     {
       const v8i ko = ko_n;
       if (s8 + 1 < 8) ko_n = k_operand<D>(kt, lo, s8 + 1, g);
-      sc[s8] = mfma_fp8(ko, qop, v4f{0.0f, 0.0f, 0.0f, 0.0f});
+      sco[s8] = mfma_fp8(ko, qop, v4f{0.0f, 0.0f, 0.0f, 0.0f});
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -618,7 +619,7 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) pa.w[i] = 0u;
     pb = pa;
-    v4f sc[8];
+    v4f sc[8], sc2[8];   // raw scores: the steps of a trip alternate between the two arrays
 
     // ---- prologue: K tile 0 resident and prepared, its raw scores in sc
     wait_vm((nt > 1 ? nk : 0) + nv);
@@ -638,8 +639,8 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
     if (nt > 1) { issue_v<D>(a, sm, 1, phys(k0 + 1), head, w, lane); n_prev += nv; }
 
     // ---- pipeline over the segment's tiles; two steps per trip so that the two probability
-    // tiles swap roles without register copies
-    auto step = [&](int j, const PTile& pprev, PTile& pcur) {
+    // tiles and the two score arrays swap roles without register copies
+    auto step = [&](int j, const PTile& pprev, PTile& pcur, v4f (&sci)[8], v4f (&sco)[8]) {
       const int bk = j % kBufs, bn = (j + 1) % kBufs;
       wait_vm(n_prev);   // this thread's copies issued two steps back have landed: K tile j+1
       lds_sync();        // and V tile j; fp16 V tile j-1 complete; K buffer of j+3 free
@@ -660,7 +661,7 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
       // read here, once: a read inside the blocks would wait for every operand read before it
       const bool vfull = __builtin_amdgcn_readfirstlane(sm.full[bk]) != 0;
       FactorIn fin;
-      pipeline_step<D>(sm, bk, (j + 1) & 1, bn, g, lo, qop, sc, pprev, pcur, st, [&](int s8) {
+      pipeline_step<D>(sm, bk, (j + 1) & 1, bn, g, lo, qop, sci, sco, pprev, pcur, st, [&](int s8) {
         // LDS reads a block ahead of the arithmetic that needs them
         if (s8 == 0) {
 #pragma unroll
@@ -683,12 +684,12 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
         st.acc[n % NDB] = mfma_f16(v_operand(vt, lo, n % NDB, n / NDB), p_operand(pt, n / NDB), st.acc[n % NDB]);
     };
     for (int j = 0;;) {
-      step(j, pa, pb);
+      step(j, pa, pb, sc, sc2);
       if (++j == nt) {
         final_pv(j - 1, pb);
         break;
       }
-      step(j, pb, pa);
+      step(j, pb, pa, sc2, sc);
       if (++j == nt) {
         final_pv(j - 1, pa);
         break;
