@@ -61,8 +61,8 @@ ATT_KERNEL = "attn_stream<128>"
 # (FETCH_SIZE, WRITE_SIZE) over this workload, each divided by the factor the same counter
 # reads for a torch copy of --calibrate-copy bytes.  Valid only for the kernel sources whose
 # hash is recorded; reported as null otherwise.
-ATT_TRAFFIC = {"sources": "ce1102ded303d7ed", "bytes": 129_400_000,
-               "read_bytes": 116_420_000, "write_bytes": 12_980_000}
+ATT_TRAFFIC = {"sources": "10736d8585d33874", "bytes": 130_110_000,
+               "read_bytes": 117_130_000, "write_bytes": 12_980_000}
 WRITE_BYTES = 2 * N * H * D * 2 + 2 * N * H * D + 2 * N * H * 4
 ROTATE_BYTES = 2 * (H * S * D + H * S * 4)
 
