@@ -597,9 +597,22 @@ def cpu_baseline(np, sched, k_new, v_new, q, start, pos0, scale):
         if el > 10.0 or reps >= 5:
             break
     log(f"cpu oracle: {el / reps:.2f} s per step on {threads} threads")
+    # the same step once more with the BLAS pool limited to one thread (one step, bounded)
+    single = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t1 = time.perf_counter()
+            oracle.ring_write(ring, kb, vb, start, pos0, table)
+            oracle.ring_attention(ring, head, filled, qb, pos0, table, scale)
+            single = time.perf_counter() - t1
+        log(f"cpu oracle: {single:.2f} s per step on 1 thread")
+    except Exception:  # pragma: no cover
+        pass
     return {"value": round(reps / el, 4), "unit": "calls/s", "cores": threads, "kind": "oracle",
             "sample": f"{reps} full steps (write 757 tokens + attention 757x5788, 24 heads x d128), "
-                      "numpy float64 attention"}
+                      "numpy float64 attention",
+            "single_thread_value": round(1.0 / single, 4) if single else None}
 
 
 if __name__ == "__main__":
