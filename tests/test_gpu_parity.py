@@ -320,6 +320,27 @@ def test_attention_mixed_write_scales(kv, torch, d):
     check_attention(*p.attend(q, sched[-1].pos0, 1 / math.sqrt(d)), label=f"mixed write scales d{d}")
 
 
+def test_large_ring_long_writes_and_rotation(kv, torch):
+    """A ring of 20,000 slots (157 tiles per head) filled by writes of 5,000 tokens (the last one
+    wraps): the write's partial-max lists (157 groups per head) and the delta rotation's (157
+    tiles) are longer than a wavefront and take the work-group reduction; ring bytes bit-exact
+    after the writes and after a rotation, attention over the whole ring before and after it."""
+    H, S, D, n = 2, 20000, 128, 5000
+    p = Pair(kv, torch, H, S, D)
+    for c in range(5):                     # slots 0, 5,000, ..., 20,000 -> 0: the fifth wraps
+        k = normal_bf16(tensor_seed("large_ring", c, 1), (n, H, D))
+        v = normal_bf16(tensor_seed("large_ring", c, 2), (n, H, D))
+        p.write(k, v, (n * c) % S, 2000 * c)   # positions 0 .. 12,999, inside the rotary table
+    assert (p.head, p.filled) == (5000, S)
+    p.assert_same("large ring")
+    q = normal_bf16(tensor_seed("large_ring", 9, 0), (200, H, D))
+    check_attention(*p.attend(q, 9000, 1 / math.sqrt(D)), label="large ring")
+    kv.kv_ring_delta_rotate(p.g, p.head, p.filled, -3000)
+    oracle.ring_delta_rotate(p.o, p.head, p.filled, -3000)
+    p.assert_same("large ring after delta -3000")
+    check_attention(*p.attend(q, 6000, 1 / math.sqrt(D)), label="large ring after rotation")
+
+
 def test_attention_empty_ring_and_no_queries(kv, torch):
     g = kv.Ring(2, 300, 128)
     tab_dev, _ = tables(kv, torch, 128)
