@@ -5,8 +5,8 @@
 //                                            the QK matrix-core product consumes them
 //                                            (k_code_offset)
 //   V codes  [heads][tiles][head_dim * 128]  each tile transposed (channel-major), 16-slot
-//                                            pieces in the order the PV product consumes them
-//                                            (v_code_offset)
+//                                            pieces in the order the attention's widening to
+//                                            fp16 reads them (v_code_offset)
 //   scales   [heads][slots] float32          dequantisation scale of the write that filled
 //                                            each slot (k_scale, v_scale)
 // tiles = ceil(slots / 128); slots past `slots` in the last tile are never valid.  With tiles in
@@ -44,8 +44,8 @@ __host__ __device__ inline int64_t k_code_offset(int64_t s, int c, int D) {
 
 // Byte offset, within one head's V codes, of slots s .. s+15 (s a multiple of 16) of channel d.
 // Unit ((db*2 + r) * 4 + g) * 16 + li of a tile holds tile slots 32g + 16r .. +15 of channel
-// 16*db + li: what lane (g, li) feeds to the PV product of channel block db as the r-th half
-// of its operand.
+// 16*db + li: lane (g, li) of the attention widens it into its fp16 PV operands of channel
+// block db for slot blocks 2r and 2r + 1.
 __host__ __device__ inline int64_t v_code_offset(int64_t s, int d, int D) {
   const int u = int(s % kTile);
   const int g = u >> 5, r = (u >> 4) & 1, db = d >> 4, li = d & 15;
