@@ -167,11 +167,29 @@ class Ring:
         return ctypes.byref(self._desc)
 
 
-def _ws(ws, need: int, device):
+# Workspaces of calls made without one: one buffer per (device, stream), kept for the life of
+# the process and grown by doubling when a call needs more, so calls do not allocate per shape
+# and no buffer is ever released while kernels queued on its stream may still use it (a buffer
+# outgrown is kept too).  Calls that share a stream are ordered by it, so they may share its
+# buffer; callers that must not allocate at all pass their own workspace.
+_WS_POOL: dict = {}
+_WS_RETIRED: list = []
+
+
+def _ws(ws, need: int, device, stream_handle: int):
     import torch
-    if ws is None:
-        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
-    return ws, int(ws.numel() * ws.element_size())
+    if ws is not None:
+        return ws, int(ws.numel() * ws.element_size())
+    dev = torch.device(device)
+    key = (dev.index if dev.index is not None else torch.cuda.current_device(), int(stream_handle))
+    cur = _WS_POOL.get(key)
+    if cur is None or cur.numel() < need:
+        size = max(need, 1 << 20, 2 * cur.numel() if cur is not None else 0)
+        if cur is not None:
+            _WS_RETIRED.append(cur)
+        cur = torch.empty(size, dtype=torch.uint8, device=dev)
+        _WS_POOL[key] = cur
+    return cur, int(cur.numel())
 
 
 def kv_ring_write(ring: Ring, k_new, v_new, start_slot: int, pos0: int, rope, workspace=None,
@@ -179,18 +197,20 @@ def kv_ring_write(ring: Ring, k_new, v_new, start_slot: int, pos0: int, rope, wo
     """k_new, v_new: bfloat16 [n, heads, head_dim] device tensors; rope: device float32 table."""
     n = int(k_new.shape[0])
     need = workspace_bytes(OP_WRITE, ring.heads, ring.slots, ring.head_dim, max(n, 1))
-    ws, wsb = _ws(workspace, need, ring.device)
+    st = _stream(stream, ring.device)
+    ws, wsb = _ws(workspace, need, ring.device, st)
     _check("kv_ring_write", lib.kv_ring_write(
         ring.desc, _ptr(k_new), _ptr(v_new), n, start_slot, pos0, _ptr(rope), int(rope.shape[0]),
-        _ptr(ws), wsb, _stream(stream, ring.device)))
+        _ptr(ws), wsb, st))
 
 
 def kv_ring_delta_rotate(ring: Ring, ring_head: int, filled: int, delta: int,
                          rope_base: float = 10000.0, workspace=None, stream=None) -> None:
     need = workspace_bytes(OP_DELTA_ROTATE, ring.heads, ring.slots, ring.head_dim, 0)
-    ws, wsb = _ws(workspace, need, ring.device)
+    st = _stream(stream, ring.device)
+    ws, wsb = _ws(workspace, need, ring.device, st)
     _check("kv_ring_delta_rotate", lib.kv_ring_delta_rotate(
-        ring.desc, ring_head, filled, delta, rope_base, _ptr(ws), wsb, _stream(stream, ring.device)))
+        ring.desc, ring_head, filled, delta, rope_base, _ptr(ws), wsb, st))
 
 
 def kv_ring_delta_rotate_3d(ring: Ring, ring_head: int, filled: int, delta, band_pairs=None,
@@ -199,10 +219,10 @@ def kv_ring_delta_rotate_3d(ring: Ring, ring_head: int, filled: int, delta, band
     d = np.ascontiguousarray(np.asarray(delta, dtype=np.int64).reshape(3))
     keep, bp = _bands_arg(band_pairs)
     need = workspace_bytes(OP_DELTA_ROTATE, ring.heads, ring.slots, ring.head_dim, 0)
-    ws, wsb = _ws(workspace, need, ring.device)
+    st = _stream(stream, ring.device)
+    ws, wsb = _ws(workspace, need, ring.device, st)
     _check("kv_ring_delta_rotate_3d", lib.kv_ring_delta_rotate_3d(
-        ring.desc, ring_head, filled, d.ctypes.data, bp, rope_base, _ptr(ws), wsb,
-        _stream(stream, ring.device)))
+        ring.desc, ring_head, filled, d.ctypes.data, bp, rope_base, _ptr(ws), wsb, st))
     del keep
 
 
@@ -217,10 +237,11 @@ def ring_attention(ring: Ring, ring_head: int, filled: int, q, q_pos0: int, rope
     if lse is None:
         lse = torch.empty((ring.heads, nq), dtype=torch.float32, device=q.device)
     need = workspace_bytes(OP_ATTENTION, ring.heads, ring.slots, ring.head_dim, max(nq, 1))
-    ws, wsb = _ws(workspace, need, ring.device)
+    st = _stream(stream, ring.device)
+    ws, wsb = _ws(workspace, need, ring.device, st)
     _check("ring_attention", lib.ring_attention(
         ring.desc, ring_head, filled, _ptr(q), nq, q_pos0, _ptr(rope), int(rope.shape[0]),
-        float(softmax_scale), _ptr(out), _ptr(lse), _ptr(ws), wsb, _stream(stream, ring.device)))
+        float(softmax_scale), _ptr(out), _ptr(lse), _ptr(ws), wsb, st))
     return out, lse
 
 
@@ -236,11 +257,12 @@ def kv_ring_write_attend(ring: Ring, k_new, v_new, start_slot: int, pos0: int, r
     if lse is None:
         lse = torch.empty((ring.heads, nq), dtype=torch.float32, device=q.device)
     need = workspace_bytes(OP_WRITE_ATTEND, ring.heads, ring.slots, ring.head_dim, max(n, nq, 1))
-    ws, wsb = _ws(workspace, need, ring.device)
+    st = _stream(stream, ring.device)
+    ws, wsb = _ws(workspace, need, ring.device, st)
     _check("kv_ring_write_attend", lib.kv_ring_write_attend(
         ring.desc, _ptr(k_new), _ptr(v_new), n, start_slot, pos0, ring_head, filled, _ptr(q), nq,
         q_pos0, _ptr(rope), int(rope.shape[0]), float(softmax_scale), _ptr(out), _ptr(lse), _ptr(ws),
-        wsb, _stream(stream, ring.device)))
+        wsb, st))
     return out, lse
 
 

@@ -97,7 +97,8 @@ def test_table_matches_angle_function_rounded_once():
 
 def test_ring_matches_linear_window_bruteforce():
     """The ring's valid slots, oldest first, hold exactly the last `filled` tokens of a plain
-    sliding window (a deque with maxlen S), for every S <= 20 and every write size."""
+    sliding window (a deque with maxlen S), for every S <= 20 and every write size, over
+    histories long enough to wrap several times."""
     for S in range(1, 21):
         for n in range(1, S + 1):
             window = collections.deque(maxlen=S)
@@ -111,6 +112,35 @@ def test_ring_matches_linear_window_bruteforce():
                 head, filled = advance(head, n, filled, S)
                 got = [slot_token[s] for s in valid_slots(head, filled, S)]
                 assert got == list(window), (S, n)
+
+
+def test_every_slot_count_start_and_write_size():
+    """Exhaustive over S <= 64, every start slot and every write size n <= S, from four prior
+    fill levels (empty, one token, half, full): a token-by-token simulation (each token goes to
+    the slot after the previous one, wrapping at S) gives the write's slots, and the valid slots
+    after the write are those holding the newest min(filled + n, S) tokens, oldest first."""
+    for S in range(1, 65):
+        for start in range(S):
+            for f0 in sorted({0, min(1, S), S // 2, S}):
+                # the f0 tokens before the write sit in the f0 slots just before `start`
+                owner = [-1] * S
+                for j in range(f0):
+                    owner[(start - f0 + j) % S] = j
+                for n in range(1, S + 1):
+                    sim, s = [], start
+                    for _ in range(n):
+                        sim.append(s)
+                        s = s + 1 if s + 1 < S else 0
+                    got = write_slots(start, n, S)
+                    assert list(got) == sim, (S, start, n)
+                    own = owner[:]
+                    for i, slot in enumerate(sim):
+                        own[slot] = f0 + i
+                    keep = min(f0 + n, S)
+                    newest = sorted((t, slot) for slot, t in enumerate(own) if t >= f0 + n - keep)
+                    head, filled = advance(start, n, f0, S)
+                    assert (head, filled) == (s, keep), (S, start, n, f0)
+                    assert list(valid_slots(head, filled, S)) == [slot for _, slot in newest], (S, start, n, f0)
 
 
 def test_tiny_schedule_golden():
