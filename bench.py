@@ -56,7 +56,7 @@ ROPE_POS = 16384
 FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 matrix-core peak
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E peak
 ATT_FLOP = 4.0 * N * S * D * H
-ATT_KERNEL = "attn_stream<128>"
+ATT_KERNEL = "attn_pp<128>"
 # HBM bytes per launch of the main attention kernel from two rocprofv3 --pmc passes
 # (FETCH_SIZE, WRITE_SIZE) over this workload, each divided by the factor the same counter
 # reads for a torch copy of --calibrate-copy bytes.  Valid only for the kernel sources whose

@@ -133,7 +133,7 @@ struct WriteArgs {
 struct QuantQArgs {
   const uint16_t* q;      // bfloat16 [nq][heads][D]
   const float* partial;   // [heads][groups]: the queries' absmax partials from pass 1
-  uint8_t* codes;         // [heads * qtiles][8][64][32]
+  uint8_t* codes;         // [heads * qtiles][8][64][32], qtiles even
   float* scale;           // [heads]
   int64_t pos0;
   int32_t nq, groups, qtiles;
@@ -384,7 +384,9 @@ QuantQArgs quant_q_args(const uint16_t* q, int32_t nq, int64_t q_pos0, const flo
   qa_.pos0 = q_pos0;
   qa_.nq = nq;
   qa_.groups = (nq + kChunk - 1) / kChunk;
-  qa_.qtiles = (nq + 127) / 128;
+  // an even number of 128-query tiles per head: the attention takes its rows 256 queries at a
+  // time (the padding queries of the last tile are stored as zero codes)
+  qa_.qtiles = 2 * ((nq + 255) / 256);
   qa_.blocks = 2 * qa_.qtiles;
   return qa_;
 }

@@ -8,36 +8,42 @@
 //      then quantize_pass (shared with the write): the queries rotated and encoded with their
 //      head's scale, stored in the order the QK product takes them.  kv_ring_write_attend runs
 //      both inside the write's own two launches;
-//   2. attn_stream: a persistent grid of one 8-wavefront work-group per compute unit.  The work
-//      is the set of units (row, tile), a row being 128 queries of one head and a tile 128 ring
+//   2. attn_pp: a persistent grid of one 8-wavefront work-group per compute unit.  The work is
+//      the set of units (row, tile), a row being 256 queries of one head and a tile 128 ring
 //      slots; each work-group takes a contiguous range of units of equal weight (a tile weighs
 //      one, the start of a row's segment kSegCost more), so a row may be split between
-//      work-groups.  A row held by one work-group is finished in place; the segments of
-//      a split row store their own output, normalised by their own sum, in half precision
-//      (a weighted mean of dequantised V rows: within 2^-11 relative), with their (max, sum).
-//      When rows are short (a ring still filling up) and fit the grid, each work-group takes
-//      one whole row instead, and no merge pass is needed.  Consecutive work-groups of one XCD
-//      get consecutive units, so the rows of one head share that XCD's L2;
+//      work-groups.  A row held by one work-group is finished in place; the segments of a split
+//      row store their own output, normalised by their own sum, in half precision (a weighted
+//      mean of dequantised V rows: within 2^-11 relative), with their (max, sum).  When rows
+//      are short (a ring still filling up) and fit the grid, each work-group takes one whole
+//      row instead, and no merge pass is needed.  Consecutive work-groups of one XCD get
+//      consecutive units, so the rows of one head share that XCD's L2;
 //   3. attn_combine: log-sum-exp merge of the split rows (skipped when no row is split).  Doing
-//      the merge in a kernel of its own avoids device-scope fences inside attn_stream, which on
+//      the merge in a kernel of its own avoids device-scope fences inside attn_pp, which on
 //      this multi-XCD part write back and invalidate L2.
 //
-// Per tile: K tile and transposed V tile are copied straight from HBM into LDS with
-// global_load_lds (16 bytes per lane; the ring stores each tile in the order the products read
-// it, so copies and operand reads are linear 1 KB wavefront accesses free of bank conflicts).
-// K has three LDS buffers; each K copy is issued at the end of the step two steps before the
-// one that reads it.  An FP8 V tile lands in one of two buffers two steps ahead and is widened
-// to fp16 (exact: every E4M3 value is an fp16 value) at the end of the step that forms its
-// probabilities, each thread widening the very units it copied, so no barrier separates the
-// landing from the widening.  Each wavefront owns 16 queries:
-//   S^T = K Q^T           8 MFMA 16x16x128 FP8 (fp32 accumulate)
+// Each wavefront owns 32 queries, as two groups of 16 that share every operand read from LDS:
+//   S^T = K Q^T           per group 8 MFMA 16x16x128 FP8 (fp32 accumulate)
 //   online softmax        log2 domain, lazily rescaled (the running max may lag the true max
 //                         by up to 2^4, so P <= 16); the running max is taken over the score
 //                         plus log2 of the slot's V scale, so P already carries that scale
-//   O^T += V^T P^T        32 MFMA 16x16x32 fp16 (fp32 accumulate): P rounded once to fp16,
-//                         V widened from E4M3
+//   O^T += V^T P^T        per group 32 MFMA 16x16x32 fp16 (fp32 accumulate): P rounded once
+//                         to fp16, V widened exactly from E4M3
 // Computing S^T rather than S leaves one query per lane with its keys in registers, which is
 // exactly the B-operand layout of the PV product: probabilities never leave their lane.
+//
+// Two-phase schedule.  The 8 wavefronts form two groups, wavefronts 0-3 and 4-7, one of each on
+// every SIMD.  A wavefront alternates a matrix phase M_i (PV of tile i-1, QK of tile i, widening
+// its share of V tile i to fp16, its share of the copies of tiles i+2) and a vector phase V_i
+// (the softmax of tile i).  The second group runs one phase behind the first, so on every SIMD
+// one wavefront issues matrix products while the other computes probabilities; every phase ends
+// at a work-group barrier.  K tiles (and their scale rows) go to three LDS buffers and FP8 V
+// tiles to two landing buffers, copied straight from HBM with global_load_lds (the ring stores
+// each tile in the order the products read it, so copies and operand reads are linear 1 KB
+// wavefront accesses free of bank conflicts).  Each thread widens exactly the V units its own
+// copy brought in, so its own wait for that copy suffices and the landing buffer is reused
+// right after.  Per-slot factors of tile i+1 and the zeroing of its invalid K bytes are done by
+// the second group during its matrix phase M_i.
 //
 // A tile whose 128 slots are all valid and come from one write (one K scale, one V scale) takes
 // the fast path: the max runs on raw scores, one FMA forms the exponent, and the V-scale factor
@@ -52,10 +58,11 @@ namespace kvring {
 
 namespace {
 
-constexpr int kWaves = 8;               // 2 wavefronts per SIMD
+constexpr int kWaves = 8;               // 2 wavefronts per SIMD, one of each group
 constexpr int kThreads = 64 * kWaves;   // 512
-constexpr int kRowQ = 16 * kWaves;      // 128 queries per row, 16 per wavefront
-constexpr int kBufs = 3;                // LDS buffers of K tiles (see attn_stream's schedule)
+constexpr int kGroupQ = 16;             // queries of one MFMA group
+constexpr int kRowQ = 2 * kGroupQ * kWaves;   // 256 queries per row, 32 per wavefront
+constexpr int kBufs = 3;                // LDS buffers of K tiles
 constexpr int kMaxGrid = 256;
 constexpr int kSegCost = 2;             // weight of a segment start in tiles (UnitSplit)
 constexpr int kCombineCost = 6;         // weight of the merge pass of split rows, in tiles
@@ -72,7 +79,7 @@ struct AttnArgs {
   const uint8_t* vc;
   const float* k_scale;
   const float* v_scale;
-  const uint8_t* q_codes;  // quantised queries: per row [8 wavefronts][64 lanes][32 bytes]
+  const uint8_t* q_codes;  // quantised queries: per 128-query tile [8][64 lanes][32 bytes]
   const float* q_scale;    // [heads]
   uint16_t* out;
   float* lse;
@@ -83,17 +90,17 @@ struct AttnArgs {
   int64_t cost;            // rows * (tv + seg_cost): the partition's total weight
   int32_t seg_cost;        // weight of a segment start, in tiles (see UnitSplit)
   int32_t heads, slots, ring_head, filled, nq;
-  int32_t qtiles, rows, tv, grid, max_seg;
+  int32_t qtiles, rows, tv, grid, max_seg;   // qtiles: rows per head
   int32_t first1, n1, first2;  // valid tiles: logical k < n1 -> first1 + k, else first2 + k - n1
   float score_scale;           // softmax_scale * log2(e)
 };
 
 // Partition of the units (row, tile) among the work-groups, by weight rather than by count: a
 // work-group whose range starts a row pays a second segment start (the end of one row's
-// segment, the quantised queries and first tiles of the next) -- measured at about two tiles of
-// work -- so every row start weighs seg_cost tiles on top of its tv tiles.  Unit u of row r at
-// tile k sits at weight position r * (tv + seg_cost) + seg_cost + k; virtual work-group v takes
-// the units whose position falls in [v * cost / grid, (v + 1) * cost / grid).
+// segment, the queries and first tiles of the next), so every row start weighs seg_cost tiles on
+// top of its tv tiles.  Unit u of row r at tile k sits at weight position
+// r * (tv + seg_cost) + seg_cost + k; virtual work-group v takes the units whose position falls
+// in [v * cost / grid, (v + 1) * cost / grid).
 struct UnitSplit {
   int64_t tv, c, cost;
   int grid;
@@ -123,7 +130,6 @@ struct Smem {
   float (&iv)[kBufs][kTile];   // per slot: 1 / v_scale (valid) or 0
   int (&uni)[kBufs][4];        // per 32 slots: all valid, one K scale and one V scale (1) or not
   int (&full)[kBufs];          // the tile's 128 slots are all valid (1) or not (0)
-  uint8_t (&q)[kRowQ * 128];   // the row's quantised queries (QK operands, 32 bytes per lane)
   float (&qs)[4];              // the head's query scale
 };
 
@@ -183,21 +189,10 @@ __device__ inline TileValid tile_valid(int64_t t, int head, int filled, int slot
 // 32g + 4bb + r: lane group g ends up holding slots 32g .. 32g+31 of its query across the 8
 // blocks, in order -- the B-operand layout of the PV product.
 
-// Per-lane byte offsets of a wavefront's share of one tile copy (tiles are stored in the order
-// the products consume them, so both K and V copies are linear: unit (j*8 + w)*64 + lane), and
-// the slot of the scale a lane copies (lanes 0..31; wavefronts 0-3: K scales, 4-7: V scales).
+// 16-byte copies per lane of one K or FP8 V tile (every wavefront copies its own units: unit
+// (j*8 + w)*64 + lane for j < kLoads).
 template <int D>
-struct CopyOffs {
-  static constexpr int kLoads = (kTile * D / 16) / kThreads;   // 16-byte copies per lane per tile
-  int su;
-};
-
-template <int D>
-__device__ inline CopyOffs<D> copy_offsets(int w, int lane) {
-  CopyOffs<D> o;
-  o.su = (w & 3) * 32 + lane;
-  return o;
-}
+constexpr int kLoads = (kTile * D / 16) / kThreads;
 
 // Asynchronous global -> LDS copy of 16 bytes per lane (4 for copy4): global address base + voff
 // (base uniform), LDS destination lds + 16 * lane (4 * lane).  Written as inline assembly so that
@@ -216,18 +211,18 @@ __device__ inline void copy4(const void* base, uint32_t voff, const void* lds) {
   asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "{m0}"(la) : "memory");
 }
 
-// Asynchronous copies of ring tile t into LDS: K tile and both scale rows into K buffer b
-// (kLoads + 1 copies per lane), or the transposed FP8 V tile into v8[b] (kLoads per lane).
+// This wavefront's share of the asynchronous copies of ring tile t: its K units and one scale
+// row segment into K buffer b (kLoads + 1 copies per lane; wavefronts 0-3 copy the K scales of
+// 32 slots each, 4-7 the V scales), or its FP8 V units into v8[b] (kLoads copies per lane).
 template <int D>
-__device__ inline void issue_k(const AttnArgs& a, Smem<D>& sm, const CopyOffs<D>& co, int b,
-                               int64_t t, int h, int w, int lane) {
+__device__ inline void issue_k(const AttnArgs& a, Smem<D>& sm, int b, int64_t t, int h, int w, int lane) {
   const uint8_t* kbase = a.kc + ((int64_t)h * a.tiles + t) * (kTile * D);   // uniform
 #pragma unroll
-  for (int j = 0; j < CopyOffs<D>::kLoads; ++j)
+  for (int j = 0; j < kLoads<D>; ++j)
     copy16(kbase, uint32_t(((j * kWaves + w) * 64 + lane) * 16), &sm.k[b][(j * kWaves + w) * 1024]);
   if (lane < 32) {
     // slot index clamped in bounds; padding slots are masked by the tile's validity
-    const int slot = min(int(t) * kTile + co.su, a.slots - 1);
+    const int slot = min(int(t) * kTile + (w & 3) * 32 + lane, a.slots - 1);
     const float* srow = ((w < 4) ? a.k_scale : a.v_scale) + (int64_t)h * a.slots;   // uniform
     float* dst = (w < 4) ? &sm.ks[b][(w & 3) * 32] : &sm.vs[b][(w & 3) * 32];
     copy4(srow, uint32_t(slot) * 4u, dst);
@@ -235,18 +230,17 @@ __device__ inline void issue_k(const AttnArgs& a, Smem<D>& sm, const CopyOffs<D>
 }
 
 template <int D>
-__device__ inline void issue_v(const AttnArgs& a, Smem<D>& sm, int b, int64_t t, int h, int w,
-                               int lane) {
+__device__ inline void issue_v(const AttnArgs& a, Smem<D>& sm, int b, int64_t t, int h, int w, int lane) {
   const uint8_t* vbase = a.vc + ((int64_t)h * a.tiles + t) * (D * kTile);   // uniform
 #pragma unroll
-  for (int j = 0; j < CopyOffs<D>::kLoads; ++j)
+  for (int j = 0; j < kLoads<D>; ++j)
     copy16(vbase, uint32_t(((j * kWaves + w) * 64 + lane) * 16), &sm.v8[b][(j * kWaves + w) * 1024]);
 }
 
-// Wait until at most n of this thread's vector-memory operations are outstanding (they complete
-// in issue order).  n is one of the copy counts of the tile schedule (0 .. 8: at most two K tiles
-// of kLoads + 1 copies and one V tile of kLoads copies, kLoads <= 2); any other count waits for
-// every operation.
+// Wait until at most n of this wavefront's vector-memory operations are outstanding (they
+// complete in issue order).  n is one of the copy counts of the schedule (0 .. 8: one K tile
+// share of kLoads + 1 copies and one V share of kLoads copies, kLoads <= 2); any other count
+// waits for every operation.
 __device__ inline void wait_vm(int n) {
   switch (n) {   // s_waitcnt immediate: vmcnt in bits 3:0, expcnt and lgkmcnt left at their maximum
     case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
@@ -264,95 +258,79 @@ __device__ inline void wait_vm(int n) {
 // Work-group barrier for LDS traffic only: this thread's LDS reads and writes are complete, and
 // the compiler keeps memory accesses on their side of it.  Unlike __syncthreads it does not wait
 // for the asynchronous tile copies in flight (their completion is tracked with wait_vm).
-__device__ inline void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// Per-slot factors of the tile in K buffer b.  Wavefronts 0-3 (one per SIMD) take 32 slots
-// each, one per lane of their first half.  Split in two so that the LDS reads can be issued well
-// before the arithmetic that needs them: factor_inputs, then tile_factors.
-struct FactorIn {
-  float ks, vs, ks0, vs0;
-};
-
-template <int D>
-__device__ inline FactorIn factor_inputs(const Smem<D>& sm, int b, int tid) {
-  FactorIn f{0.0f, 0.0f, 0.0f, 0.0f};
-  const int lane = tid & 63;
-  if (tid < 4 * 64 && lane < 32) {
-    const int u = (tid >> 6) * 32 + lane;
-    f.ks = sm.ks[b][u];
-    f.vs = sm.vs[b][u];
-    f.ks0 = sm.ks[b][0];
-    f.vs0 = sm.vs[b][0];
-  }
-  return f;
+__device__ inline void lds_sync() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
+// Per-slot factors of the tile in K buffer b, by the second group (wavefronts 4-7, one per SIMD,
+// 32 slots each, one per lane of their first half).
 template <int D>
-__device__ inline void tile_factors(Smem<D>& sm, int b, const TileValid& tvd, float c0, int tid,
-                                    const FactorIn& f) {
+__device__ inline void tile_factors(Smem<D>& sm, int b, const TileValid& tvd, float c0, int tid) {
   const int lane = tid & 63;
-  if (tid < 4 * 64 && lane < 32) {
-    const int u = (tid >> 6) * 32 + lane;
+  if (tid >= 4 * 64 && lane < 32) {
+    const int u = ((tid >> 6) & 3) * 32 + lane;
+    const float ks = sm.ks[b][u], vs = sm.vs[b][u], ks0 = sm.ks[b][0], vs0 = sm.vs[b][0];
     const bool ok = tvd.has(u);
-    sm.ck[b][u] = ok ? c0 * f.ks : 0.0f;
-    sm.nb[b][u] = ok ? __log2f(f.vs) : -INFINITY;
-    sm.iv[b][u] = ok ? __builtin_amdgcn_rcpf(f.vs) : 0.0f;
-    const bool same = ok && f.ks == f.ks0 && f.vs == f.vs0;
+    sm.ck[b][u] = ok ? c0 * ks : 0.0f;
+    sm.nb[b][u] = ok ? __log2f(vs) : -INFINITY;
+    sm.iv[b][u] = ok ? __builtin_amdgcn_rcpf(vs) : 0.0f;
+    const bool same = ok && ks == ks0 && vs == vs0;
     const bool all_same = __all(same);   // over this wavefront's 32 active lanes
     if (lane == 0) sm.uni[b][u >> 5] = all_same ? 1 : 0;
-    if (tid == 0) sm.full[b] = tvd.count() == kTile ? 1 : 0;
+    if (u == 0) sm.full[b] = tvd.count() == kTile ? 1 : 0;
   }
 }
 
 // Zeroed K bytes for the invalid slots of the tile in K buffer b (so that whatever they hold --
-// NaN codes included -- never reaches a product); tiles with invalid slots only.
+// NaN codes included -- never reaches a product); tiles with invalid slots only; by the second
+// group (256 threads).
 template <int D>
 __device__ inline void zero_invalid_k(Smem<D>& sm, int b, const TileValid& tvd, int tid) {
   constexpr int NCH = D / 16;
   uint8_t* kw = sm.k[b];
-  for (int c = tid; c < kTile * NCH; c += kThreads) {   // 16-byte units of the K tile
+  for (int c = tid - 4 * 64; c < kTile * NCH; c += 4 * 64) {   // 16-byte units of the K tile
     const int li = c & 15, bb = c / (16 * (D / 32)) / 2;
     if (!tvd.has(32 * (li >> 2) + 4 * bb + (li & 3))) *reinterpret_cast<uint4*>(kw + c * 16) = make_uint4(0, 0, 0, 0);
   }
 }
 
-// Widening of the FP8 V tile in v8[b] to fp16 in v16[b], in the PV product's operand order, with
-// the invalid slots' values zeroed when the tile is not full (a slot is valid exactly when its
-// factor iv, in K buffer bf, is non-zero: 1 / v_scale is finite and positive for every scale a
-// write can store).  FP8 unit ((db*2 + r)*4 + g)*16 + li holds slots 32g + 16r ..
-// +15 of channel 16db + li; its first 8 slots become piece (db, kb = 2r) and its last 8 piece
-// (db, 2r + 1), where piece (db, kb) of lane (g, li) -- slots 32g + 8kb .. +7 of channel
-// 16db + li, 8 fp16 values -- sits at byte ((db*4 + kb)*64 + g*16 + li) * 16.  Each thread widens
-// the units its own tile copy brought in (unit (j*8 + w)*64 + lane), so its own wait for that
-// copy suffices; the fp16 tile is read by other wavefronts only after the next barrier.  Unit
-// j of the thread's kLoads units is read by widen_load and converted and stored by widen_store.
+// Widening of this thread's FP8 V units of the tile in v8[b] to fp16 in v16[b], in the PV
+// product's operand order, with the invalid slots' values zeroed when the tile is not full (a
+// slot is valid exactly when its factor iv, in K buffer bf, is non-zero: 1 / v_scale is finite
+// and positive for every scale a write can store).  FP8 unit ((db*2 + r)*4 + g)*16 + li holds
+// slots 32g + 16r .. +15 of channel 16db + li; its first 8 slots become piece (db, kb = 2r) and
+// its last 8 piece (db, 2r + 1), where piece (db, kb) of lane (g, li) -- slots 32g + 8kb .. +7
+// of channel 16db + li, 8 fp16 values -- sits at byte ((db*4 + kb)*64 + g*16 + li) * 16.  Each
+// thread widens the units its own tile copy brought in (unit (j*8 + w)*64 + lane), so its own
+// wait for that copy suffices; the fp16 tile is read by other wavefronts only after a barrier.
 template <int D>
-__device__ inline uint4 widen_load(const Smem<D>& sm, int b, int j, int w, int lane) {
-  const int c = (j * kWaves + w) * 64 + lane;
-  return *reinterpret_cast<const uint4*>(&sm.v8[b][c * 16]);
-}
-
-template <int D>
-__device__ inline void widen_store(Smem<D>& sm, int b, int bf, int j, int w, int lane, const uint4& x,
-                                   bool full) {
-  const int c = (j * kWaves + w) * 64 + lane;
-  const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
-  uint32_t h[8];
+__device__ inline void widen(Smem<D>& sm, int b, int bf, int w, int lane, bool full) {
+  uint4 x[kLoads<D>];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    h[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(int(xw[i]), 1.0f, false));
-    h[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(int(xw[i]), 1.0f, true));
-  }
-  const int li = c & 15, g = (c >> 4) & 3, r = (c >> 6) & 1, db = c >> 7;
-  if (!full) {
-    const float* ivu = &sm.iv[bf][32 * g + 16 * r];
+  for (int j = 0; j < kLoads<D>; ++j) x[j] = *reinterpret_cast<const uint4*>(&sm.v8[b][((j * kWaves + w) * 64 + lane) * 16]);
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk)
-      if (ivu[kk] == 0.0f) h[kk >> 1] &= (kk & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+  for (int j = 0; j < kLoads<D>; ++j) {
+    const int c = (j * kWaves + w) * 64 + lane;
+    const uint32_t xw[4] = {x[j].x, x[j].y, x[j].z, x[j].w};
+    uint32_t h[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(int(xw[i]), 1.0f, false));
+      h[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(int(xw[i]), 1.0f, true));
+    }
+    const int li = c & 15, g = (c >> 4) & 3, r = (c >> 6) & 1, db = c >> 7;
+    if (!full) {
+      const float* ivu = &sm.iv[bf][32 * g + 16 * r];
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk)
+        if (ivu[kk] == 0.0f) h[kk >> 1] &= (kk & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+    }
+    const int o0 = ((db * 4 + 2 * r) * 64 + g * 16 + li) * 16;
+    *reinterpret_cast<uint4*>(&sm.v16[b][o0]) = make_uint4(h[0], h[1], h[2], h[3]);
+    *reinterpret_cast<uint4*>(&sm.v16[b][o0 + 1024]) = make_uint4(h[4], h[5], h[6], h[7]);
   }
-  const int o0 = ((db * 4 + 2 * r) * 64 + g * 16 + li) * 16;
-  *reinterpret_cast<uint4*>(&sm.v16[b][o0]) = make_uint4(h[0], h[1], h[2], h[3]);
-  *reinterpret_cast<uint4*>(&sm.v16[b][o0 + 1024]) = make_uint4(h[4], h[5], h[6], h[7]);
 }
 
 // Per-lane LDS byte offsets (within one buffer) of a lane's A operands: half r of score block bb
@@ -384,75 +362,81 @@ __device__ inline v8h v_operand(const uint8_t* vt, const LaneOffs& o, int db, in
   return *reinterpret_cast<const v8h*>(vt + o.v + (db * 4 + kb) * 1024);
 }
 
-// Running softmax state and output accumulator of one wavefront (16 queries; lane (g, li)
-// holds query li's channels 16*db + 4g .. +3 of every channel block db).
+// State of one query group (16 queries) of a wavefront: lane (g, li) holds query li's channels
+// 16*db + 4g .. +3 of every channel block db, its raw scores of tile slots 32g .. 32g+31
+// (sc[bb][r]: slot 32g + 4bb + r) and their probabilities as fp16 pairs (p[2bb + h]: slots
+// 32g + 4bb + 2h, +1; dwords 4kb .. 4kb+3 are the lane's B operand of PV slot block kb).
 template <int D>
-struct RowState {
+struct Group {
   v4f acc[D / 16];
+  v4f sc[8];
+  uint32_t p[16];
   float m;   // running max (log2 units), identical in the 4 lanes of a query
   float l;   // this lane's share of the running sum
 };
 
-// Probabilities of one tile as the B operands of the PV product, in fp16: lane (g, li) holds
-// query li's probabilities of slots 32g .. 32g+31, two per dword in slot order; dwords 4kb ..
-// 4kb+3 (slots 32g + 8kb .. +7) are its operand of slot block kb.
-struct PTile {
-  uint32_t w[16];
-};
-
-__device__ inline v8h p_operand(const PTile& p, int kb) {
-  return __builtin_bit_cast(v8h, v4u{p.w[4 * kb], p.w[4 * kb + 1], p.w[4 * kb + 2], p.w[4 * kb + 3]});
+__device__ inline v8h p_operand(const uint32_t (&p)[16], int kb) {
+  return __builtin_bit_cast(v8h, v4u{p[4 * kb], p[4 * kb + 1], p[4 * kb + 2], p[4 * kb + 3]});
 }
 
-// One pipeline step of a wavefront:
-//   softmax of tile k   (raw scores s; factors in LDS buffer bk) -> probabilities pc
-//   PV of tile k-1      (probabilities pp; fp16 V in LDS buffer bp), interleaved with the softmax
-//   QK of tile k+1      (K in LDS buffer bn) -> raw scores into the other score array (the
-//                       steps of a trip alternate the two, so no copy joins them), block by
-//                       block as the softmax frees the registers
-// The PV products do not depend on tile k, so the matrix cores work while the vector units
-// form tile k's probabilities.  A rescale found by tile k's max is applied to the accumulator
-// after the PV of tile k-1, whose probabilities were formed against the old max.
-//
+// Matrix part of phase M_i: PV of the previous tile (fp16 V in vt) and QK of this tile (K in kt,
+// or none).  Each operand read from LDS feeds both query groups; operands are read kPre products
+// ahead, and the scheduling barriers keep that distance (left to itself the compiler hoists every
+// read to the top and runs out of registers).
+template <int D>
+__device__ __forceinline__ void matrix_products(const uint8_t* vt, const uint8_t* kt, const LaneOffs& lo,
+                                                int g, const v8i (&qop)[2], Group<D>& ga, Group<D>& gb) {
+  constexpr int NDB = D / 16;
+  constexpr int NPV = NDB * 4;   // product n: channel block n % NDB, slot block n / NDB
+  constexpr int kPre = 4;
+  if (vt) {
+    v8h vo[kPre];
+#pragma unroll
+    for (int n = 0; n < kPre; ++n) vo[n] = v_operand(vt, lo, n % NDB, n / NDB);
+#pragma unroll
+    for (int n = 0; n < NPV; ++n) {
+      const v8h x = vo[n % kPre];
+      if (n + kPre < NPV) vo[n % kPre] = v_operand(vt, lo, (n + kPre) % NDB, (n + kPre) / NDB);
+      const int db = n % NDB, kb = n / NDB;
+      ga.acc[db] = mfma_f16(x, p_operand(ga.p, kb), ga.acc[db]);
+      gb.acc[db] = mfma_f16(x, p_operand(gb.p, kb), gb.acc[db]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  if (kt) {
+    v8i ko[2];
+    ko[0] = k_operand<D>(kt, lo, 0, g);
+    ko[1] = k_operand<D>(kt, lo, 1, g);
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb) {
+      const v8i x = ko[bb & 1];
+      if (bb + 2 < 8) ko[bb & 1] = k_operand<D>(kt, lo, bb + 2, g);
+      ga.sc[bb] = mfma_fp8(x, qop[0], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+      gb.sc[bb] = mfma_fp8(x, qop[1], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// Softmax of one query group over the tile whose factors are in K buffer bk.
 // Per score (slot j, query i):  t = raw * ck_j + nb_j, the log2-domain score plus log2 of the
 // slot's V scale; P' = 2^(t - m) goes to the PV product (with V decoded but not scaled) and
-// P' * iv_j = 2^(score - m) to the row sum.  The running max m tracks max t.
-template <int D, class Bg>
-__device__ __forceinline__ void pipeline_step(const Smem<D>& sm, int bk, int bp, int bn, int g,
-                                              const LaneOffs& lo, const v8i& qop, v4f (&sc)[8], v4f (&sco)[8],
-                                              const PTile& pp, PTile& pc, RowState<D>& st, Bg&& bg) {
+// P' * iv_j = 2^(score - m) to the row sum.  The running max m tracks max t.  A rescale found
+// by this tile's max is applied to the accumulator, which at this point holds the products of
+// every earlier tile (their probabilities were formed against the old max).
+template <int D>
+__device__ __forceinline__ void softmax_group(const Smem<D>& sm, int bk, int g, bool uniform, Group<D>& gr) {
   constexpr int NDB = D / 16;
-  const uint8_t* vt = sm.v16[bp];
-  const uint8_t* kt = sm.k[bn];
-  constexpr int kEarly = 8;   // PV products issued before the max (they do not depend on it)
-  static_assert((NDB * 4 - kEarly) % 8 == 0, "the other products spread evenly over 8 blocks");
-
-  // ---- PV(k-1), first products: product n takes channel block n % NDB and slot block n / NDB,
-  // so consecutive products accumulate into different blocks.  V operands are read from LDS
-  // two products ahead.
-  v8h vo_n = v_operand(vt, lo, 0, 0), vo_nn = v_operand(vt, lo, 1 % NDB, 1 / NDB);
-  auto pv = [&](int n) {
-    const v8h vo = vo_n;
-    vo_n = vo_nn;
-    if (n + 2 < NDB * 4) vo_nn = v_operand(vt, lo, (n + 2) % NDB, (n + 2) / NDB);
-    st.acc[n % NDB] = mfma_f16(vo, p_operand(pp, n / NDB), st.acc[n % NDB]);
-  };
-#pragma unroll
-  for (int n = 0; n < kEarly; ++n) pv(n);
-
-  // ---- tile k: scores with their factors, max, rescale decision.  A uniform tile (all slots
-  // valid, one K scale, one V scale) keeps its raw scores: t = raw * c + b for every slot.
-  const int4 un = *reinterpret_cast<const int4*>(&sm.uni[bk][0]);
-  const bool uniform = __builtin_amdgcn_readfirstlane(un.x & un.y & un.z & un.w) != 0;
-  float cf = 1.0f, bf = 0.0f, tmax;
+  float cf = 1.0f, bf = 0.0f, tmax, ivu = 0.0f;
   if (uniform) {
     cf = sm.ck[bk][0];
     bf = sm.nb[bk][0];
-    float rmax = sc[0][0];
+    ivu = sm.iv[bk][0];
+    float rmax = gr.sc[0][0];
 #pragma unroll
     for (int bb = 0; bb < 8; ++bb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) rmax = __builtin_fmaxf(rmax, sc[bb][r]);
+      for (int r = 0; r < 4; ++r) rmax = __builtin_fmaxf(rmax, gr.sc[bb][r]);
     tmax = max_over_groups(rmax) * cf + bf;
   } else {
     tmax = -INFINITY;
@@ -460,70 +444,52 @@ __device__ __forceinline__ void pipeline_step(const Smem<D>& sm, int bk, int bp,
     for (int bb = 0; bb < 8; ++bb) {
       const float4 ck = *reinterpret_cast<const float4*>(&sm.ck[bk][32 * g + 4 * bb]);
       const float4 nb = *reinterpret_cast<const float4*>(&sm.nb[bk][32 * g + 4 * bb]);
-      sc[bb][0] = __builtin_fmaf(sc[bb][0], ck.x, nb.x);
-      sc[bb][1] = __builtin_fmaf(sc[bb][1], ck.y, nb.y);
-      sc[bb][2] = __builtin_fmaf(sc[bb][2], ck.z, nb.z);
-      sc[bb][3] = __builtin_fmaf(sc[bb][3], ck.w, nb.w);
+      gr.sc[bb][0] = __builtin_fmaf(gr.sc[bb][0], ck.x, nb.x);
+      gr.sc[bb][1] = __builtin_fmaf(gr.sc[bb][1], ck.y, nb.y);
+      gr.sc[bb][2] = __builtin_fmaf(gr.sc[bb][2], ck.z, nb.z);
+      gr.sc[bb][3] = __builtin_fmaf(gr.sc[bb][3], ck.w, nb.w);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) tmax = __builtin_fmaxf(tmax, sc[bb][r]);
+      for (int r = 0; r < 4; ++r) tmax = __builtin_fmaxf(tmax, gr.sc[bb][r]);
     }
     tmax = max_over_groups(tmax);
   }
-  const bool need = __any(tmax > st.m + kTau);
+  const bool need = __any(tmax > gr.m + kTau);
   float alpha = 1.0f;
   if (need) {
-    const float m_new = __builtin_fmaxf(st.m, tmax);
-    alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(st.m - m_new);
-    st.m = m_new;
+    const float m_new = __builtin_fmaxf(gr.m, tmax);
+    alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(gr.m - m_new);
+    gr.m = m_new;
   }
-  const float bm = bf - (st.m == -INFINITY ? 0.0f : st.m);   // P' = 2^(s * cf + bm)
-
-  // ---- the rest of PV(k-1) interleaved with tile k's probabilities; the scheduling barriers
-  // keep the blocks in order so that few values are live.
+  const float bm = bf - (gr.m == -INFINITY ? 0.0f : gr.m);   // P' = 2^(s * cf + bm)
   float lsum = 0.0f;
-  constexpr int kLate = (NDB * 4 - kEarly) / 8;   // products per softmax block
-  v8i ko_n = k_operand<D>(kt, lo, 0, g);
-  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int s8 = 0; s8 < 8; ++s8) {
-#pragma unroll
-    for (int i = 0; i < (kLate + 1) / 2; ++i) pv(kEarly + s8 * kLate + i);
-    const float4 iv = *reinterpret_cast<const float4*>(&sm.iv[bk][32 * g + 4 * s8]);
-    const float ivr[4] = {iv.x, iv.y, iv.z, iv.w};
+  for (int bb = 0; bb < 8; ++bb) {
     float p[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[s8][r], cf, bm));
-      lsum = __builtin_fmaf(p[r], ivr[r], lsum);
+    for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(gr.sc[bb][r], cf, bm));
+    if (uniform) {
+      lsum += (p[0] + p[1]) + (p[2] + p[3]);
+    } else {
+      const float4 iv = *reinterpret_cast<const float4*>(&sm.iv[bk][32 * g + 4 * bb]);
+      lsum = __builtin_fmaf(p[0], iv.x, lsum);
+      lsum = __builtin_fmaf(p[1], iv.y, lsum);
+      lsum = __builtin_fmaf(p[2], iv.z, lsum);
+      lsum = __builtin_fmaf(p[3], iv.w, lsum);
     }
-    uint32_t h0 = pack_f16(p[0], p[1]), h1 = pack_f16(p[2], p[3]);
-    // pin the block's vector work here, between its products (otherwise it is sunk below the
-    // branches that follow, away from the products it should overlap)
-    asm volatile("" : "+v"(h0), "+v"(h1), "+v"(lsum));
-    pc.w[2 * s8] = h0;
-    pc.w[2 * s8 + 1] = h1;
-    bg(s8);
-#pragma unroll
-    for (int i = (kLate + 1) / 2; i < kLate; ++i) pv(kEarly + s8 * kLate + i);
-    // QK(k+1) of score block s8
-    {
-      const v8i ko = ko_n;
-      if (s8 + 1 < 8) ko_n = k_operand<D>(kt, lo, s8 + 1, g);
-      sco[s8] = mfma_fp8(ko, qop, v4f{0.0f, 0.0f, 0.0f, 0.0f});
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    gr.p[2 * bb] = pack_f16(p[0], p[1]);
+    gr.p[2 * bb + 1] = pack_f16(p[2], p[3]);
   }
-
+  if (uniform) lsum *= ivu;
   if (need) {
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) st.acc[db] *= alpha;
-    st.l *= alpha;
+    for (int db = 0; db < NDB; ++db) gr.acc[db] *= alpha;
+    gr.l *= alpha;
   }
-  st.l += lsum;
+  gr.l += lsum;
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
+__global__ __launch_bounds__(kThreads) void attn_pp(AttnArgs a) {
   constexpr int NDB = D / 16;
   __shared__ __align__(16) uint8_t s_k[kBufs][kTile * D];
   __shared__ __align__(16) uint8_t s_v8[2][D * kTile];
@@ -535,33 +501,28 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
   __shared__ __align__(16) float s_iv[kBufs][kTile];
   __shared__ __align__(16) int s_uni[kBufs][4];
   __shared__ int s_full[kBufs];
-  // the row's query codes: for head_dim 128 they land in K buffer 2 (a K tile is exactly their
-  // size), read before K tile 2 is copied there; 152 KB of LDS in all
-  __shared__ __align__(16) uint8_t s_qx[D == 128 ? 16 : kRowQ * 128];
   __shared__ __align__(16) float s_qs[4];
-  uint8_t (&s_q)[kRowQ * 128] =
-      *reinterpret_cast<uint8_t (*)[kRowQ * 128]>(D == 128 ? &s_k[2][0] : &s_qx[0]);
-  Smem<D> sm{s_k, s_v8, s_v16, s_ks, s_vs, s_ck, s_nb, s_iv, s_uni, s_full, s_q, s_qs};
+  Smem<D> sm{s_k, s_v8, s_v16, s_ks, s_vs, s_ck, s_nb, s_iv, s_uni, s_full, s_qs};
 
   const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);   // wavefront (uniform)
+  const int grp = w >> 2;   // 0: wavefronts 0-3 (phase ahead), 1: wavefronts 4-7
 
   // virtual work-group index: consecutive indices on one XCD (work-groups are dealt to the 8
   // XCDs round-robin), so that neighbouring units share an L2
   const int wg = blockIdx.x;
   const int v = (a.grid % 8 == 0) ? (wg % 8) * (a.grid / 8) + wg / 8 : wg;
   const UnitSplit split{a.tv, a.seg_cost, a.cost, a.grid};
-  auto owner = [&](int64_t u) -> int { return split.owner(u); };
   int64_t ub = split.begin(v);
   const int64_t ue = split.begin(v + 1);
   const int tid = int(threadIdx.x);
   const int lane = tid & 63, g = lane >> 4, li = lane & 15;
-  const CopyOffs<D> co = copy_offsets<D>(w, lane);
   const LaneOffs lo = lane_offsets<D>(lane);
+  constexpr int nk = kLoads<D> + 1, nv = kLoads<D>;
 
   // The first segment may start inside a row; every later one starts the next row at tile 0
   // (and is then the row's first segment).  The 64-bit divisions happen once per work-group.
   int row = int(ub / a.tv), k0 = int(ub % a.tv);
-  int seg = k0 > 0 ? v - owner((int64_t)row * a.tv) : 0;   // index of this segment in its row
+  int seg = k0 > 0 ? v - split.owner((int64_t)row * a.tv) : 0;   // index of this segment in its row
   while (ub < ue) {
     const int k1 = int(min<int64_t>(a.tv, k0 + (ue - ub)));
     const int nt = k1 - k0;
@@ -569,167 +530,139 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
     const bool row_split = nt < a.tv;   // the row has other segments (in other work-groups)
     auto phys = [&](int k) -> int64_t { return k < a.n1 ? a.first1 + k : a.first2 + (k - a.n1); };
 
-    // Copy schedule (j = tile index within the segment; step j forms tile j's probabilities,
-    // runs the PV product of tile j-1 and the QK product of tile j+1, then widens V tile j):
-    //   K tile j (+ scales) -> K buffer j % 3, issued at the end of step j-3, needed from step
-    //                          j-1 on;
-    //   FP8 V tile j        -> v8[j % 2], issued at the end of step j-2, widened at the end of
-    //                          step j into v16[j % 2] (read by step j+1).
-    // A step waits only for the copies issued two steps back, so each copy has a step to land.
-    // Issued after the step's products rather than before them, the copies queue in the memory
-    // pipeline while the matrix cores finish, instead of holding every wavefront at the start.
-    // A thread's V copy lands in the units that thread widens, so reusing v8[j % 2] for tile
-    // j+2 right after widening tile j needs no barrier.
-    // The row's quantised queries (16 KB, 32 bytes per lane) and the head's query scale are
-    // copied first, then K tiles 0 and 1 and V tile 0, so that one memory round trip covers all.
+    // ---- prologue: this wavefront's queries (group q of wavefront w: queries 32w + 16q ..
+    // +15 of the row, from 128-query tile 2qt + w/4 of the head, its wavefront slot (2w + q) % 8),
+    // the head's query scale, and tiles 0 and 1 (both groups' shares)
+    v8i qop[2];
     {
-      const uint8_t* qbase = a.q_codes + (int64_t)row * (kRowQ * 128);   // uniform
+      const int64_t qtile = (int64_t)head * (2 * a.qtiles) + 2 * qt + (w >> 2);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        copy16(qbase, uint32_t(((j * kWaves + w) * 64 + lane) * 16), &sm.q[(j * kWaves + w) * 1024]);
+      for (int q = 0; q < 2; ++q) {
+        const uint4* src = reinterpret_cast<const uint4*>(
+            a.q_codes + ((qtile * 8 + ((2 * w + q) & 7)) * 64 + lane) * 32);
+        const uint4 x0 = src[0], x1 = src[1];
+        qop[q] = v8i{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
+      }
       if (w == 0 && lane == 0) copy4(a.q_scale, uint32_t(head) * 4u, &sm.qs[0]);
     }
-    const int nk = CopyOffs<D>::kLoads + 1, nv = CopyOffs<D>::kLoads;
-    issue_k<D>(a, sm, co, 0, phys(k0), head, w, lane);
-    if (nt > 1) issue_k<D>(a, sm, co, 1, phys(k0 + 1), head, w, lane);
+    issue_k<D>(a, sm, 0, phys(k0), head, w, lane);
     issue_v<D>(a, sm, 0, phys(k0), head, w, lane);
-
-    // the PV of the first step reads "tile -1" from v16[1] with zero probabilities: zero it, so
-    // that no stale value (NaN included) meets them
-    {
-      uint4* vz = reinterpret_cast<uint4*>(sm.v16[1]);
-      for (int c = tid; c < 2 * D * kTile / 16; c += kThreads) vz[c] = make_uint4(0, 0, 0, 0);
+    if (nt > 1) {
+      issue_k<D>(a, sm, 1, phys(k0 + 1), head, w, lane);
+      issue_v<D>(a, sm, 1, phys(k0 + 1), head, w, lane);
     }
-    wait_vm((nt > 1 ? 2 * nk : nk) + nv);   // this thread's query copies have landed
+    wait_vm(0);
     lds_sync();
     const float c0 = a.score_scale * sm.qs[0];
-    v8i qop;
-    {
-      const uint4 x0 = *reinterpret_cast<const uint4*>(&sm.q[(w * 64 + lane) * 32]);
-      const uint4 x1 = *reinterpret_cast<const uint4*>(&sm.q[(w * 64 + lane) * 32 + 16]);
-      qop = v8i{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
-    }
-
-    RowState<D> st;
-    st.m = -INFINITY;
-    st.l = 0.0f;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) st.acc[db] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    PTile pa, pb;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) pa.w[i] = 0u;
-    pb = pa;
-    v4f sc[8], sc2[8];   // raw scores: the steps of a trip alternate between the two arrays
-
-    // ---- prologue: K tile 0 resident and prepared, its raw scores in sc
-    wait_vm((nt > 1 ? nk : 0) + nv);
-    lds_sync();
     {
       const TileValid tvd = tile_valid(phys(k0), a.ring_head, a.filled, a.slots);
-      tile_factors(sm, 0, tvd, c0, tid, factor_inputs(sm, 0, tid));
-      if (tvd.count() < kTile) zero_invalid_k(sm, 0, tvd, tid);
+      tile_factors(sm, 0, tvd, c0, tid);
+      if (grp == 1 && tvd.count() < kTile) zero_invalid_k(sm, 0, tvd, tid);
     }
-    lds_sync();   // also: every wavefront has read its queries out of K buffer 2
-#pragma unroll
-    for (int bb = 0; bb < 8; ++bb)
-      sc[bb] = mfma_fp8(k_operand<D>(sm.k[0], lo, bb, g), qop, v4f{0.0f, 0.0f, 0.0f, 0.0f});
-    // copies of step -1: K tile 2, V tile 1
-    int n_prev = 0;
-    if (nt > 2) { issue_k<D>(a, sm, co, 2, phys(k0 + 2), head, w, lane); n_prev += nk; }
-    if (nt > 1) { issue_v<D>(a, sm, 1, phys(k0 + 1), head, w, lane); n_prev += nv; }
+    lds_sync();
 
-    // ---- pipeline over the segment's tiles; two steps per trip so that the two probability
-    // tiles and the two score arrays swap roles without register copies
-    auto step = [&](int j, const PTile& pprev, PTile& pcur, v4f (&sci)[8], v4f (&sco)[8]) {
-      const int bk = j % kBufs, bn = (j + 1) % kBufs;
-      wait_vm(n_prev);   // this thread's copies issued two steps back have landed: K tile j+1
-      lds_sync();        // and V tile j; fp16 V tile j-1 complete; K buffer of j+3 free
-      n_prev = 0;
-      const bool next = j + 1 < nt;
-      const TileValid tvn = tile_valid(phys(k0 + (next ? j + 1 : j)), a.ring_head, a.filled, a.slots);
-      if (next && tvn.count() < kTile) {
-        zero_invalid_k(sm, bn, tvn, tid);
-        lds_sync();   // K bytes zeroed: barrier before the QK reads them
-      }
-      // Work spread over the softmax blocks, between their products: the factors of tile j+1
-      // (read from the next step on), widening V tile j (its units first, then this thread's
-      // copy of V tile j+2 into the same units), and the copy of K tile j+3 (its buffer is
-      // free all step).
-      constexpr int kWu = (D * kTile / 16) / kThreads;
-      const bool more_k = j + 3 < nt, more_v = j + 2 < nt;
-      uint4 vx[kWu];
-      // read here, once: a read inside the blocks would wait for every operand read before it
-      const bool vfull = __builtin_amdgcn_readfirstlane(sm.full[bk]) != 0;
-      FactorIn fin;
-      pipeline_step<D>(sm, bk, (j + 1) & 1, bn, g, lo, qop, sci, sco, pprev, pcur, st, [&](int s8) {
-        // LDS reads a block ahead of the arithmetic that needs them
-        if (s8 == 0) {
+    Group<D> ga, gb;
+    ga.m = gb.m = -INFINITY;
+    ga.l = gb.l = 0.0f;
 #pragma unroll
-          for (int u = 0; u < kWu; ++u) vx[u] = widen_load(sm, j & 1, u, w, lane);
-          if (next) fin = factor_inputs(sm, bn, tid);
-        }
-        if (s8 == 1 && next) tile_factors(sm, bn, tvn, c0, tid, fin);
-        if (s8 >= 2 && s8 < 2 + kWu) widen_store(sm, j & 1, bk, s8 - 2, w, lane, vx[s8 - 2], vfull);
-        if (s8 == 3 && more_k) issue_k<D>(a, sm, co, (j + 3) % kBufs, phys(k0 + j + 3), head, w, lane);
-        if (s8 == 5 && more_v) issue_v<D>(a, sm, j & 1, phys(k0 + j + 2), head, w, lane);
-      });
-      n_prev = (more_k ? nk : 0) + (more_v ? nv : 0);
+    for (int db = 0; db < NDB; ++db) ga.acc[db] = gb.acc[db] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ga.p[i] = gb.p[i] = 0u;
+
+    // ---- the two-phase pipeline.  Slot s of the work-group: the first group runs M_{s/2} (s
+    // even) or V_{s/2} (s odd), the second group one slot later; a barrier ends every slot.
+    //   M_i: PV(i-1); QK(i); widen this thread's units of V tile i into v16[i % 2]; copy this
+    //        wavefront's shares of tiles i+2 (V into v8[i % 2], the units just widened; K into
+    //        k[(i+2) % 3], free since the barrier after the second group's QK(i-1)); the second
+    //        group also prepares tile i+1 (its K copies landed by the previous slot's end);
+    //   V_i: softmax of tile i.
+    // Copy completion: at the end of M_i a wavefront waits for everything but the copies it has
+    // just issued, at the end of V_i for everything, so each copy has two slots to land.
+    // side work of M_i: widening, copies of tile i+2, (second group) preparation of tile i+1;
+    // returns the number of copies issued
+    auto side = [&](int i) -> int {
+      int issued = 0;
+      widen<D>(sm, i & 1, i % kBufs, w, lane, __builtin_amdgcn_readfirstlane(sm.full[i % kBufs]) != 0);
+      if (i + 2 < nt) {
+        issue_v<D>(a, sm, i & 1, phys(k0 + i + 2), head, w, lane);
+        issue_k<D>(a, sm, (i + 2) % kBufs, phys(k0 + i + 2), head, w, lane);
+        issued = nv + nk;
+      }
+      if (grp == 1 && i + 1 < nt) {
+        const int bn = (i + 1) % kBufs;
+        const TileValid tvd = tile_valid(phys(k0 + i + 1), a.ring_head, a.filled, a.slots);
+        tile_factors(sm, bn, tvd, c0, tid);
+        if (tvd.count() < kTile) zero_invalid_k(sm, bn, tvd, tid);
+      }
+      return issued;
     };
-    auto final_pv = [&](int jl, const PTile& pt) {   // PV of the last tile jl
+    auto vphase = [&](int i) {
+      const int bk = i % kBufs;
+      const int4 un = *reinterpret_cast<const int4*>(&sm.uni[bk][0]);
+      const bool uniform = __builtin_amdgcn_readfirstlane(un.x & un.y & un.z & un.w) != 0;
+      softmax_group<D>(sm, bk, g, uniform, ga);
+      softmax_group<D>(sm, bk, g, uniform, gb);
       wait_vm(0);
-      lds_sync();   // fp16 V tile jl complete
-      const uint8_t* vt = sm.v16[jl & 1];
-#pragma unroll
-      for (int n = 0; n < NDB * 4; ++n)
-        st.acc[n % NDB] = mfma_f16(v_operand(vt, lo, n % NDB, n / NDB), p_operand(pt, n / NDB), st.acc[n % NDB]);
+      lds_sync();
     };
-    for (int j = 0;;) {
-      step(j, pa, pb, sc, sc2);
-      if (++j == nt) {
-        final_pv(j - 1, pb);
-        break;
-      }
-      step(j, pb, pa, sc2, sc);
-      if (++j == nt) {
-        final_pv(j - 1, pa);
-        break;
-      }
+    if (grp == 1) lds_sync();   // the first group's M_0
+    {   // M_0: QK of tile 0 only
+      matrix_products<D>(nullptr, sm.k[0], lo, g, qop, ga, gb);
+      const int issued = side(0);
+      wait_vm(issued);
+      lds_sync();
+      vphase(0);
     }
+    for (int i = 1; i < nt; ++i) {   // M_i, V_i
+      matrix_products<D>(sm.v16[(i - 1) & 1], sm.k[i % kBufs], lo, g, qop, ga, gb);
+      const int issued = side(i);
+      wait_vm(issued);
+      lds_sync();
+      vphase(i);
+    }
+    // M_nt: PV of the last tile only
+    matrix_products<D>(sm.v16[(nt - 1) & 1], nullptr, lo, g, qop, ga, gb);
+    wait_vm(0);
+    lds_sync();
+    if (grp == 0) lds_sync();   // the second group's M_nt
 
     // ---- segment result: direct output, or partial for attn_combine
-    float lt = st.l;
-    lt += __shfl_xor(lt, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
-    if (row_split) {
-      const int64_t slot0 = ((int64_t)row * a.max_seg + seg) * kRowQ;
-      const int ql = w * 16 + li;
-      const float il = lt > 0.0f ? 1.0f / lt : 0.0f;
-      _Float16* po = a.part_o + (slot0 + ql) * D + 4 * g;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const v4f o = st.acc[db];
-        const v4h oh = {(_Float16)(o[0] * il), (_Float16)(o[1] * il), (_Float16)(o[2] * il),
-                        (_Float16)(o[3] * il)};
-        *reinterpret_cast<v4h*>(po + 16 * db) = oh;
-      }
-      if (g == 0) *reinterpret_cast<float2*>(a.part_ml + (slot0 + ql) * 2) = make_float2(st.m, lt);
-    } else {
-      const int i = qt * kRowQ + w * 16 + li;
-      if (i < a.nq) {
+    for (int q = 0; q < 2; ++q) {
+      Group<D>& gr = q == 0 ? ga : gb;
+      float lt = gr.l;
+      lt += __shfl_xor(lt, 16, 64);
+      lt += __shfl_xor(lt, 32, 64);
+      const int ql = 32 * w + 16 * q + li;   // query within the row
+      if (row_split) {
+        const int64_t slot0 = ((int64_t)row * a.max_seg + seg) * kRowQ;
         const float il = lt > 0.0f ? 1.0f / lt : 0.0f;
-        uint16_t* dst = a.out + ((int64_t)i * a.heads + head) * D + 4 * g;
+        _Float16* po = a.part_o + (slot0 + ql) * D + 4 * g;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const v4f o = st.acc[db];
-          const uint32_t lo = uint32_t(f32_to_bf16(o[0] * il)) | (uint32_t(f32_to_bf16(o[1] * il)) << 16);
-          const uint32_t hi = uint32_t(f32_to_bf16(o[2] * il)) | (uint32_t(f32_to_bf16(o[3] * il)) << 16);
-          *reinterpret_cast<uint2*>(dst + 16 * db) = make_uint2(lo, hi);
+          const v4f o = gr.acc[db];
+          const v4h oh = {(_Float16)(o[0] * il), (_Float16)(o[1] * il), (_Float16)(o[2] * il),
+                          (_Float16)(o[3] * il)};
+          *reinterpret_cast<v4h*>(po + 16 * db) = oh;
         }
-        if (g == 0)
-          a.lse[(int64_t)head * a.nq + i] = lt > 0.0f ? (st.m + __log2f(lt)) * kLn2 : -INFINITY;
+        if (g == 0) *reinterpret_cast<float2*>(a.part_ml + (slot0 + ql) * 2) = make_float2(gr.m, lt);
+      } else {
+        const int i = qt * kRowQ + ql;
+        if (i < a.nq) {
+          const float il = lt > 0.0f ? 1.0f / lt : 0.0f;
+          uint16_t* dst = a.out + ((int64_t)i * a.heads + head) * D + 4 * g;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const v4f o = gr.acc[db];
+            const uint32_t lo16 = uint32_t(f32_to_bf16(o[0] * il)) | (uint32_t(f32_to_bf16(o[1] * il)) << 16);
+            const uint32_t hi16 = uint32_t(f32_to_bf16(o[2] * il)) | (uint32_t(f32_to_bf16(o[3] * il)) << 16);
+            *reinterpret_cast<uint2*>(dst + 16 * db) = make_uint2(lo16, hi16);
+          }
+          if (g == 0)
+            a.lse[(int64_t)head * a.nq + i] = lt > 0.0f ? (gr.m + __log2f(lt)) * kLn2 : -INFINITY;
+        }
       }
     }
-    lds_sync();   // LDS buffers are reused by the next segment
     ub += nt;
     row += 1;
     k0 = 0;
@@ -738,9 +671,9 @@ __global__ __launch_bounds__(kThreads) void attn_stream(AttnArgs a) {
 }
 
 // Merge of split rows: thread = (query of a row, 8 channels); rows held by one work-group were
-// written directly by attn_stream and are skipped.  A row has at most 8 segments (make_plan);
-// every load of a thread is issued before any arithmetic (one memory round trip), and the
-// segments are merged in order.
+// written directly by attn_pp and are skipped.  A row has at most 8 segments (make_plan); every
+// load of a thread is issued before any arithmetic (one memory round trip), and the segments are
+// merged in order.
 typedef _Float16 v8hc __attribute__((ext_vector_type(8)));
 
 template <int D>
@@ -818,7 +751,7 @@ int device_cus() {
 Plan make_plan(int32_t heads, int32_t slots, int32_t nq, int32_t ring_head, int32_t filled, int grid_cap) {
   Plan p;
   const int64_t tiles = tile_count(slots);
-  p.qtiles = (nq + kRowQ - 1) / kRowQ;
+  p.qtiles = (nq + kRowQ - 1) / kRowQ;   // rows per head
   p.rows = p.qtiles * heads;
   // tiles holding valid slots: the valid interval [old, old + filled) mod slots as <= 2 runs
   p.first1 = p.n1 = p.first2 = 0;
@@ -869,7 +802,9 @@ Plan make_plan(int32_t heads, int32_t slots, int32_t nq, int32_t ring_head, int3
 }  // namespace
 
 namespace {
-hipEvent_t g_ev_before = nullptr, g_ev_after = nullptr;
+// Profiling hook (kv_ring_set_attention_events): per host thread, so that a setting made by one
+// thread never applies to calls issued by another.
+thread_local hipEvent_t g_ev_before = nullptr, g_ev_after = nullptr;
 }
 
 void set_attention_events(void* before, void* after) {
@@ -894,7 +829,7 @@ WsLayout ws_layout(int32_t heads, int32_t slots, int32_t head_dim, int32_t nq) {
   l.part_o = l.q_partial + up4((int64_t)heads * ((nq + 31) / 32));
   l.part_ml = l.part_o + (int64_t)p.rows * 8 * kRowQ * head_dim / 2;   // half precision
   l.q_codes = l.part_ml + (int64_t)p.rows * 8 * kRowQ * 2;
-  l.q_scale = l.q_codes + (int64_t)p.rows * (kRowQ * 128) / 4;
+  l.q_scale = l.q_codes + (int64_t)p.rows * (kRowQ * 128) / 4;   // 128 bytes per query
   l.total = l.q_scale + up4(heads);
   return l;
 }
@@ -958,7 +893,14 @@ hipError_t launch_attention(const kv_ring_desc& r, int32_t ring_head, int32_t fi
     e = launch_q_prep(q, nq, r.heads, r.head_dim, q_pos0, rope, aw.q_partial, aw.q_codes, aw.q_scale, stream);
     if (e != hipSuccess) return e;
   }
-  if (g_ev_before && g_ev_after) {
+  // the profiling events are recorded only outside stream capture (a captured record would
+  // become a node of the caller's graph)
+  bool events = g_ev_before && g_ev_after;
+  if (events) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    events = hipStreamIsCapturing(stream, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone;
+  }
+  if (events) {
     e = hipEventRecord(g_ev_before, stream);
     if (e != hipSuccess) return e;
   }
@@ -972,11 +914,11 @@ hipError_t launch_attention(const kv_ring_desc& r, int32_t ring_head, int32_t fi
     a.grid = p.rows < kMaxGrid ? p.rows : kMaxGrid;
   }
   if (r.head_dim == 128)
-    hipLaunchKernelGGL(attn_stream<128>, dim3(a.grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(attn_pp<128>, dim3(a.grid), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(attn_stream<64>, dim3(a.grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(attn_pp<64>, dim3(a.grid), dim3(kThreads), 0, stream, a);
   e = hipGetLastError();
-  if (e == hipSuccess && g_ev_before && g_ev_after) e = hipEventRecord(g_ev_after, stream);
+  if (e == hipSuccess && events) e = hipEventRecord(g_ev_after, stream);
   if (e != hipSuccess) return e;
   bool split = false;   // does any row span more than one work-group?
   for (int row = 0; row < p.rows && !split; ++row) {
