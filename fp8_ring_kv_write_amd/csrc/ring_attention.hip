@@ -67,6 +67,7 @@ constexpr int kMaxGrid = 256;
 constexpr int kSegCost = 2;             // weight of a segment start in tiles (UnitSplit)
 constexpr int kCombineCost = 6;         // weight of the merge pass of split rows, in tiles
 constexpr float kTau = 4.0f;            // lazy rescale threshold, log2 units
+constexpr float kPmax = 4096.0f;        // bound on a lane's probability sum in the fast path
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));   // split rows' partial outputs
@@ -129,7 +130,6 @@ struct Smem {
   float (&nb)[kBufs][kTile];   // per slot: log2(v_scale) (valid) or -inf
   float (&iv)[kBufs][kTile];   // per slot: 1 / v_scale (valid) or 0
   int (&uni)[kBufs][4];        // per 32 slots: all valid, one K scale and one V scale (1) or not
-  int (&full)[kBufs];          // the tile's 128 slots are all valid (1) or not (0)
   float (&qs)[4];              // the head's query scale
 };
 
@@ -265,21 +265,39 @@ __device__ inline void lds_sync() {
 }
 
 // Per-slot factors of the tile in K buffer b, by the second group (wavefronts 4-7, one per SIMD,
-// 32 slots each, one per lane of their first half).
+// 32 slots each, one per lane of their first half).  Split in two so that the LDS reads can be
+// issued well before the arithmetic that needs them: factor_inputs, then tile_factors.
+struct FactorIn {
+  float ks, vs, ks0, vs0;
+};
+
 template <int D>
-__device__ inline void tile_factors(Smem<D>& sm, int b, const TileValid& tvd, float c0, int tid) {
+__device__ inline FactorIn factor_inputs(const Smem<D>& sm, int b, int tid) {
+  FactorIn f{0.0f, 0.0f, 0.0f, 0.0f};
   const int lane = tid & 63;
   if (tid >= 4 * 64 && lane < 32) {
     const int u = ((tid >> 6) & 3) * 32 + lane;
-    const float ks = sm.ks[b][u], vs = sm.vs[b][u], ks0 = sm.ks[b][0], vs0 = sm.vs[b][0];
+    f.ks = sm.ks[b][u];
+    f.vs = sm.vs[b][u];
+    f.ks0 = sm.ks[b][0];
+    f.vs0 = sm.vs[b][0];
+  }
+  return f;
+}
+
+template <int D>
+__device__ inline void tile_factors(Smem<D>& sm, int b, const TileValid& tvd, float c0, int tid,
+                                    const FactorIn& f) {
+  const int lane = tid & 63;
+  if (tid >= 4 * 64 && lane < 32) {
+    const int u = ((tid >> 6) & 3) * 32 + lane;
     const bool ok = tvd.has(u);
-    sm.ck[b][u] = ok ? c0 * ks : 0.0f;
-    sm.nb[b][u] = ok ? __log2f(vs) : -INFINITY;
-    sm.iv[b][u] = ok ? __builtin_amdgcn_rcpf(vs) : 0.0f;
-    const bool same = ok && ks == ks0 && vs == vs0;
+    sm.ck[b][u] = ok ? c0 * f.ks : 0.0f;
+    sm.nb[b][u] = ok ? __log2f(f.vs) : -INFINITY;
+    sm.iv[b][u] = ok ? __builtin_amdgcn_rcpf(f.vs) : 0.0f;
+    const bool same = ok && f.ks == f.ks0 && f.vs == f.vs0;
     const bool all_same = __all(same);   // over this wavefront's 32 active lanes
     if (lane == 0) sm.uni[b][u >> 5] = all_same ? 1 : 0;
-    if (u == 0) sm.full[b] = tvd.count() == kTile ? 1 : 0;
   }
 }
 
@@ -296,7 +314,7 @@ __device__ inline void zero_invalid_k(Smem<D>& sm, int b, const TileValid& tvd, 
   }
 }
 
-// Widening of this thread's FP8 V units of the tile in v8[b] to fp16 in v16[b], in the PV
+// Widening of this thread's FP8 V units (loaded into x) of the tile in v8[b] to fp16 in v16[b], in the PV
 // product's operand order, with the invalid slots' values zeroed when the tile is not full (a
 // slot is valid exactly when its factor iv, in K buffer bf, is non-zero: 1 / v_scale is finite
 // and positive for every scale a write can store).  FP8 unit ((db*2 + r)*4 + g)*16 + li holds
@@ -306,10 +324,8 @@ __device__ inline void zero_invalid_k(Smem<D>& sm, int b, const TileValid& tvd, 
 // thread widens the units its own tile copy brought in (unit (j*8 + w)*64 + lane), so its own
 // wait for that copy suffices; the fp16 tile is read by other wavefronts only after a barrier.
 template <int D>
-__device__ inline void widen(Smem<D>& sm, int b, int bf, int w, int lane, bool full) {
-  uint4 x[kLoads<D>];
-#pragma unroll
-  for (int j = 0; j < kLoads<D>; ++j) x[j] = *reinterpret_cast<const uint4*>(&sm.v8[b][((j * kWaves + w) * 64 + lane) * 16]);
+__device__ inline void widen_store(Smem<D>& sm, int b, int bf, int w, int lane, const uint4 (&x)[kLoads<D>],
+                                   bool full) {
 #pragma unroll
   for (int j = 0; j < kLoads<D>; ++j) {
     const int c = (j * kWaves + w) * 64 + lane;
@@ -373,117 +389,171 @@ struct Group {
   uint32_t p[16];
   float m;   // running max (log2 units), identical in the 4 lanes of a query
   float l;   // this lane's share of the running sum
+  bool started;   // every lane's running max is finite (wavefront-uniform)
 };
 
 __device__ inline v8h p_operand(const uint32_t (&p)[16], int kb) {
   return __builtin_bit_cast(v8h, v4u{p[4 * kb], p[4 * kb + 1], p[4 * kb + 2], p[4 * kb + 3]});
 }
 
-// Matrix part of phase M_i: PV of the previous tile (fp16 V in vt) and QK of this tile (K in kt,
-// or none).  Each operand read from LDS feeds both query groups; operands are read kPre products
-// ahead, and the scheduling barriers keep that distance (left to itself the compiler hoists every
-// read to the top and runs out of registers).
+// Matrix part of phase M_i: PV of the previous tile (fp16 V in vt) and QK of this tile (K in kt).
+// Each operand read from LDS feeds both query groups.  PV product n takes channel block n % NDB and
+// slot block n / NDB; its V operand is read kPre products ahead (PvPipe), the K operands of QK
+// kPreK blocks ahead, and the scheduling
+// barriers keep that distance (left to itself the compiler hoists every read to the top and runs
+// out of registers).  The products run in ranges (pv_run<N0, N1>), so that the phase's side work
+// can be placed between them and overlap them.
+constexpr int kPre = 8;    // V operands in flight (PV)
+constexpr int kPreK = 4;   // K operands in flight (QK)
+
 template <int D>
-__device__ __forceinline__ void matrix_products(const uint8_t* vt, const uint8_t* kt, const LaneOffs& lo,
-                                                int g, const v8i (&qop)[2], Group<D>& ga, Group<D>& gb) {
+struct PvPipe {
+  v8h vo[kPre];
+};
+
+template <int D>
+__device__ __forceinline__ void pv_start(PvPipe<D>& pp, const uint8_t* vt, const LaneOffs& lo) {
   constexpr int NDB = D / 16;
-  constexpr int NPV = NDB * 4;   // product n: channel block n % NDB, slot block n / NDB
-  constexpr int kPre = 4;
-  if (vt) {
-    v8h vo[kPre];
 #pragma unroll
-    for (int n = 0; n < kPre; ++n) vo[n] = v_operand(vt, lo, n % NDB, n / NDB);
+  for (int n = 0; n < kPre; ++n) pp.vo[n] = v_operand(vt, lo, n % NDB, n / NDB);
+}
+
+template <int N0, int N1, int D>
+__device__ __forceinline__ void pv_run(PvPipe<D>& pp, const uint8_t* vt, const LaneOffs& lo, Group<D>& ga,
+                                       Group<D>& gb) {
+  constexpr int NDB = D / 16;
+  constexpr int NPV = NDB * 4;
 #pragma unroll
-    for (int n = 0; n < NPV; ++n) {
-      const v8h x = vo[n % kPre];
-      if (n + kPre < NPV) vo[n % kPre] = v_operand(vt, lo, (n + kPre) % NDB, (n + kPre) / NDB);
-      const int db = n % NDB, kb = n / NDB;
-      ga.acc[db] = mfma_f16(x, p_operand(ga.p, kb), ga.acc[db]);
-      gb.acc[db] = mfma_f16(x, p_operand(gb.p, kb), gb.acc[db]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-  if (kt) {
-    v8i ko[2];
-    ko[0] = k_operand<D>(kt, lo, 0, g);
-    ko[1] = k_operand<D>(kt, lo, 1, g);
-#pragma unroll
-    for (int bb = 0; bb < 8; ++bb) {
-      const v8i x = ko[bb & 1];
-      if (bb + 2 < 8) ko[bb & 1] = k_operand<D>(kt, lo, bb + 2, g);
-      ga.sc[bb] = mfma_fp8(x, qop[0], v4f{0.0f, 0.0f, 0.0f, 0.0f});
-      gb.sc[bb] = mfma_fp8(x, qop[1], v4f{0.0f, 0.0f, 0.0f, 0.0f});
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  for (int n = N0; n < N1; ++n) {
+    const v8h x = pp.vo[n % kPre];
+    if (n + kPre < NPV) pp.vo[n % kPre] = v_operand(vt, lo, (n + kPre) % NDB, (n + kPre) / NDB);
+    const int db = n % NDB, kb = n / NDB;
+    ga.acc[db] = mfma_f16(x, p_operand(ga.p, kb), ga.acc[db]);
+    gb.acc[db] = mfma_f16(x, p_operand(gb.p, kb), gb.acc[db]);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Softmax of one query group over the tile whose factors are in K buffer bk.
-// Per score (slot j, query i):  t = raw * ck_j + nb_j, the log2-domain score plus log2 of the
-// slot's V scale; P' = 2^(t - m) goes to the PV product (with V decoded but not scaled) and
-// P' * iv_j = 2^(score - m) to the row sum.  The running max m tracks max t.  A rescale found
-// by this tile's max is applied to the accumulator, which at this point holds the products of
-// every earlier tile (their probabilities were formed against the old max).
 template <int D>
-__device__ __forceinline__ void softmax_group(const Smem<D>& sm, int bk, int g, bool uniform, Group<D>& gr) {
+__device__ __forceinline__ void qk_run(const uint8_t* kt, const LaneOffs& lo, int g, const v8i (&qop)[2],
+                                       Group<D>& ga, Group<D>& gb) {
+  v8i ko[kPreK];
+#pragma unroll
+  for (int bb = 0; bb < kPreK; ++bb) ko[bb] = k_operand<D>(kt, lo, bb, g);
+#pragma unroll
+  for (int bb = 0; bb < 8; ++bb) {
+    const v8i x = ko[bb % kPreK];
+    if (bb + kPreK < 8) ko[bb % kPreK] = k_operand<D>(kt, lo, bb + kPreK, g);
+    ga.sc[bb] = mfma_fp8(x, qop[0], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+    gb.sc[bb] = mfma_fp8(x, qop[1], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Marks a rarely taken branch: an instruction with side effects cannot be executed
+// speculatively, so the compiler keeps the branch instead of flattening both paths into one
+// sequence that runs every time.
+__device__ inline void rare_branch() { asm volatile(""); }
+
+// Raises the group's running max to the tile's maximum score t = raw * cf + bf (cf > 0) when it
+// exceeds the running max by more than kTau (lazy rescaling), rescaling the accumulator and the
+// running sum, which at this point hold the contributions of every earlier tile.
+template <int D>
+__device__ __forceinline__ void raise_max(Group<D>& gr, float tmax) {
   constexpr int NDB = D / 16;
-  float cf = 1.0f, bf = 0.0f, tmax, ivu = 0.0f;
-  if (uniform) {
-    cf = sm.ck[bk][0];
-    bf = sm.nb[bk][0];
-    ivu = sm.iv[bk][0];
-    float rmax = gr.sc[0][0];
-#pragma unroll
-    for (int bb = 0; bb < 8; ++bb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) rmax = __builtin_fmaxf(rmax, gr.sc[bb][r]);
-    tmax = max_over_groups(rmax) * cf + bf;
-  } else {
-    tmax = -INFINITY;
-#pragma unroll
-    for (int bb = 0; bb < 8; ++bb) {
-      const float4 ck = *reinterpret_cast<const float4*>(&sm.ck[bk][32 * g + 4 * bb]);
-      const float4 nb = *reinterpret_cast<const float4*>(&sm.nb[bk][32 * g + 4 * bb]);
-      gr.sc[bb][0] = __builtin_fmaf(gr.sc[bb][0], ck.x, nb.x);
-      gr.sc[bb][1] = __builtin_fmaf(gr.sc[bb][1], ck.y, nb.y);
-      gr.sc[bb][2] = __builtin_fmaf(gr.sc[bb][2], ck.z, nb.z);
-      gr.sc[bb][3] = __builtin_fmaf(gr.sc[bb][3], ck.w, nb.w);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) tmax = __builtin_fmaxf(tmax, gr.sc[bb][r]);
-    }
-    tmax = max_over_groups(tmax);
-  }
-  const bool need = __any(tmax > gr.m + kTau);
-  float alpha = 1.0f;
-  if (need) {
+  if (__any(tmax > gr.m + kTau)) {
+    rare_branch();
     const float m_new = __builtin_fmaxf(gr.m, tmax);
-    alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(gr.m - m_new);
+    const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(gr.m - m_new);
     gr.m = m_new;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) gr.acc[db] *= alpha;
+    gr.l *= alpha;
   }
-  const float bm = bf - (gr.m == -INFINITY ? 0.0f : gr.m);   // P' = 2^(s * cf + bm)
-  float lsum = 0.0f;
+  gr.started = __all(gr.m != -INFINITY);
+}
+
+// Probabilities of a uniform tile: P' = 2^(raw * cf + bm) into the group's fp16 operand tile;
+// returns this lane's sum of the fp16 values (the dot product with ones keeps it in fp32).
+template <int D>
+__device__ __forceinline__ float uniform_probs(Group<D>& gr, float cf, float bm) {
+  const v2h one = {(_Float16)1.0f, (_Float16)1.0f};
+  float s2 = 0.0f;
 #pragma unroll
   for (int bb = 0; bb < 8; ++bb) {
     float p[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(gr.sc[bb][r], cf, bm));
-    if (uniform) {
-      lsum += (p[0] + p[1]) + (p[2] + p[3]);
-    } else {
-      const float4 iv = *reinterpret_cast<const float4*>(&sm.iv[bk][32 * g + 4 * bb]);
-      lsum = __builtin_fmaf(p[0], iv.x, lsum);
-      lsum = __builtin_fmaf(p[1], iv.y, lsum);
-      lsum = __builtin_fmaf(p[2], iv.z, lsum);
-      lsum = __builtin_fmaf(p[3], iv.w, lsum);
-    }
     gr.p[2 * bb] = pack_f16(p[0], p[1]);
     gr.p[2 * bb + 1] = pack_f16(p[2], p[3]);
+    s2 = __builtin_amdgcn_fdot2(__builtin_bit_cast(v2h, gr.p[2 * bb]), one, s2, false);
+    s2 = __builtin_amdgcn_fdot2(__builtin_bit_cast(v2h, gr.p[2 * bb + 1]), one, s2, false);
   }
-  if (uniform) lsum *= ivu;
-  if (need) {
+  return s2;
+}
+
+// Softmax of one query group over the tile whose factors are in K buffer bk.
+// Per score (slot j, query i):  t = raw * ck_j + nb_j, the log2-domain score plus log2 of the
+// slot's V scale; P' = 2^(t - m) goes to the PV product (with V decoded but not scaled) and
+// P' * iv_j = 2^(score - m) to the row sum.  The running max m tracks max t, lazily.
+// Uniform tile (one ck, nb, iv for all 128 slots): the probabilities are formed against the
+// running max as it stands, without a max over the tile first.  Their sum bounds every one of
+// them: while no lane's sum exceeds kPmax (an fp16 overflow makes it infinite), each P' <= kPmax,
+// far from the fp16 range limit; otherwise the tile's max has moved up, the running max is
+// raised to it and the probabilities are formed again.  The first tile of a segment raises the
+// running max first.  Other tiles take per-slot factors and a max over the tile.
+template <int D>
+__device__ __forceinline__ void softmax_group(const Smem<D>& sm, int bk, int g, bool uniform, Group<D>& gr) {
+  if (uniform) {
+    const float cf = sm.ck[bk][0], bf = sm.nb[bk][0], ivu = sm.iv[bk][0];
+    auto tile_max = [&]() __attribute__((always_inline)) {
+      float rmax = gr.sc[0][0];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) gr.acc[db] *= alpha;
-    gr.l *= alpha;
+      for (int bb = 0; bb < 8; ++bb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rmax = __builtin_fmaxf(rmax, gr.sc[bb][r]);
+      return max_over_groups(rmax) * cf + bf;
+    };
+    if (!gr.started) {
+      rare_branch();
+      raise_max(gr, tile_max());
+    }
+    float s2 = uniform_probs(gr, cf, bf - gr.m);
+    if (!__all(s2 <= kPmax)) {
+      rare_branch();
+      raise_max(gr, tile_max());
+      s2 = uniform_probs(gr, cf, bf - gr.m);
+    }
+    gr.l = __builtin_fmaf(s2, ivu, gr.l);
+    return;
+  }
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int bb = 0; bb < 8; ++bb) {
+    const float4 ck = *reinterpret_cast<const float4*>(&sm.ck[bk][32 * g + 4 * bb]);
+    const float4 nb = *reinterpret_cast<const float4*>(&sm.nb[bk][32 * g + 4 * bb]);
+    gr.sc[bb][0] = __builtin_fmaf(gr.sc[bb][0], ck.x, nb.x);
+    gr.sc[bb][1] = __builtin_fmaf(gr.sc[bb][1], ck.y, nb.y);
+    gr.sc[bb][2] = __builtin_fmaf(gr.sc[bb][2], ck.z, nb.z);
+    gr.sc[bb][3] = __builtin_fmaf(gr.sc[bb][3], ck.w, nb.w);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) tmax = __builtin_fmaxf(tmax, gr.sc[bb][r]);
+  }
+  raise_max(gr, max_over_groups(tmax));
+  const float bm = -(gr.m == -INFINITY ? 0.0f : gr.m);   // P' = 2^(t + bm)
+  float lsum = 0.0f;
+#pragma unroll
+  for (int bb = 0; bb < 8; ++bb) {
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(gr.sc[bb][r] + bm);
+    const float4 iv = *reinterpret_cast<const float4*>(&sm.iv[bk][32 * g + 4 * bb]);
+    lsum = __builtin_fmaf(p[0], iv.x, lsum);
+    lsum = __builtin_fmaf(p[1], iv.y, lsum);
+    lsum = __builtin_fmaf(p[2], iv.z, lsum);
+    lsum = __builtin_fmaf(p[3], iv.w, lsum);
+    gr.p[2 * bb] = pack_f16(p[0], p[1]);
+    gr.p[2 * bb + 1] = pack_f16(p[2], p[3]);
   }
   gr.l += lsum;
 }
@@ -500,9 +570,8 @@ __global__ __launch_bounds__(kThreads) void attn_pp(AttnArgs a) {
   __shared__ __align__(16) float s_nb[kBufs][kTile];
   __shared__ __align__(16) float s_iv[kBufs][kTile];
   __shared__ __align__(16) int s_uni[kBufs][4];
-  __shared__ int s_full[kBufs];
   __shared__ __align__(16) float s_qs[4];
-  Smem<D> sm{s_k, s_v8, s_v16, s_ks, s_vs, s_ck, s_nb, s_iv, s_uni, s_full, s_qs};
+  Smem<D> sm{s_k, s_v8, s_v16, s_ks, s_vs, s_ck, s_nb, s_iv, s_uni, s_qs};
 
   const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);   // wavefront (uniform)
   const int grp = w >> 2;   // 0: wavefronts 0-3 (phase ahead), 1: wavefronts 4-7
@@ -528,7 +597,7 @@ __global__ __launch_bounds__(kThreads) void attn_pp(AttnArgs a) {
     const int nt = k1 - k0;
     const int head = row / a.qtiles, qt = row % a.qtiles;
     const bool row_split = nt < a.tv;   // the row has other segments (in other work-groups)
-    auto phys = [&](int k) -> int64_t { return k < a.n1 ? a.first1 + k : a.first2 + (k - a.n1); };
+    auto phys = [&](int k) __attribute__((always_inline)) -> int64_t { return k < a.n1 ? a.first1 + k : a.first2 + (k - a.n1); };
 
     // ---- prologue: this wavefront's queries (group q of wavefront w: queries 32w + 16q ..
     // +15 of the row, from 128-query tile 2qt + w/4 of the head, its wavefront slot (2w + q) % 8),
@@ -556,7 +625,7 @@ __global__ __launch_bounds__(kThreads) void attn_pp(AttnArgs a) {
     const float c0 = a.score_scale * sm.qs[0];
     {
       const TileValid tvd = tile_valid(phys(k0), a.ring_head, a.filled, a.slots);
-      tile_factors(sm, 0, tvd, c0, tid);
+      tile_factors(sm, 0, tvd, c0, tid, factor_inputs(sm, 0, tid));
       if (grp == 1 && tvd.count() < kTile) zero_invalid_k(sm, 0, tvd, tid);
     }
     lds_sync();
@@ -564,6 +633,7 @@ __global__ __launch_bounds__(kThreads) void attn_pp(AttnArgs a) {
     Group<D> ga, gb;
     ga.m = gb.m = -INFINITY;
     ga.l = gb.l = 0.0f;
+    ga.started = gb.started = false;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) ga.acc[db] = gb.acc[db] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -578,25 +648,37 @@ __global__ __launch_bounds__(kThreads) void attn_pp(AttnArgs a) {
     //   V_i: softmax of tile i.
     // Copy completion: at the end of M_i a wavefront waits for everything but the copies it has
     // just issued, at the end of V_i for everything, so each copy has two slots to land.
-    // side work of M_i: widening, copies of tile i+2, (second group) preparation of tile i+1;
-    // returns the number of copies issued
-    auto side = [&](int i) -> int {
-      int issued = 0;
-      widen<D>(sm, i & 1, i % kBufs, w, lane, __builtin_amdgcn_readfirstlane(sm.full[i % kBufs]) != 0);
-      if (i + 2 < nt) {
-        issue_v<D>(a, sm, i & 1, phys(k0 + i + 2), head, w, lane);
-        issue_k<D>(a, sm, (i + 2) % kBufs, phys(k0 + i + 2), head, w, lane);
-        issued = nv + nk;
-      }
-      if (grp == 1 && i + 1 < nt) {
-        const int bn = (i + 1) % kBufs;
-        const TileValid tvd = tile_valid(phys(k0 + i + 1), a.ring_head, a.filled, a.slots);
-        tile_factors(sm, bn, tvd, c0, tid);
-        if (tvd.count() < kTile) zero_invalid_k(sm, bn, tvd, tid);
-      }
-      return issued;
+    // Side work of M_i, in pieces placed between the phase's products.  Loads first, at the start
+    // of the phase and ahead of the product operands (LDS reads return in order): this thread's
+    // FP8 units of V tile i and, in the second group, the scale rows of tile i+1.  Then, a few
+    // products later, the widening of those units to fp16 and the second group's preparation of
+    // tile i+1 (factors, zeroed K bytes), and last the copies of tile i+2 (so that no wait before
+    // them can cover a copy just issued).  side_copies returns the number of copies issued.
+    uint4 vx[kLoads<D>];
+    FactorIn fin{0.0f, 0.0f, 0.0f, 0.0f};
+    auto side_loads = [&](int i) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < kLoads<D>; ++j) vx[j] = *reinterpret_cast<const uint4*>(&sm.v8[i & 1][((j * kWaves + w) * 64 + lane) * 16]);
+      if (grp == 1 && i + 1 < nt) fin = factor_inputs(sm, (i + 1) % kBufs, tid);
     };
-    auto vphase = [&](int i) {
+    auto side_widen = [&](int i) __attribute__((always_inline)) {
+      const bool vfull = tile_valid(phys(k0 + i), a.ring_head, a.filled, a.slots).count() == kTile;
+      widen_store<D>(sm, i & 1, i % kBufs, w, lane, vx, vfull);
+    };
+    auto side_prep = [&](int i) __attribute__((always_inline)) {
+      if (grp != 1 || i + 1 >= nt) return;
+      const int bn = (i + 1) % kBufs;
+      const TileValid tvd = tile_valid(phys(k0 + i + 1), a.ring_head, a.filled, a.slots);
+      tile_factors(sm, bn, tvd, c0, tid, fin);
+      if (tvd.count() < kTile) zero_invalid_k(sm, bn, tvd, tid);
+    };
+    auto side_copies = [&](int i) __attribute__((always_inline)) -> int {
+      if (i + 2 >= nt) return 0;
+      issue_v<D>(a, sm, i & 1, phys(k0 + i + 2), head, w, lane);
+      issue_k<D>(a, sm, (i + 2) % kBufs, phys(k0 + i + 2), head, w, lane);
+      return nv + nk;
+    };
+    auto vphase = [&](int i) __attribute__((always_inline)) {
       const int bk = i % kBufs;
       const int4 un = *reinterpret_cast<const int4*>(&sm.uni[bk][0]);
       const bool uniform = __builtin_amdgcn_readfirstlane(un.x & un.y & un.z & un.w) != 0;
@@ -606,24 +688,48 @@ __global__ __launch_bounds__(kThreads) void attn_pp(AttnArgs a) {
       lds_sync();
     };
     if (grp == 1) lds_sync();   // the first group's M_0
-    {   // M_0: QK of tile 0 only
-      matrix_products<D>(nullptr, sm.k[0], lo, g, qop, ga, gb);
-      const int issued = side(0);
+    {   // M_0: QK of tile 0, then its side work
+      __builtin_amdgcn_s_setprio(1);
+      side_loads(0);
+      qk_run<D>(sm.k[0], lo, g, qop, ga, gb);
+      __builtin_amdgcn_s_setprio(0);
+      side_widen(0);
+      side_prep(0);
+      const int issued = side_copies(0);
       wait_vm(issued);
       lds_sync();
       vphase(0);
     }
+    constexpr int NPV = NDB * 4;
     for (int i = 1; i < nt; ++i) {   // M_i, V_i
-      matrix_products<D>(sm.v16[(i - 1) & 1], sm.k[i % kBufs], lo, g, qop, ga, gb);
-      const int issued = side(i);
+      const uint8_t* vt = sm.v16[(i - 1) & 1];
+      __builtin_amdgcn_s_setprio(1);   // the matrix products issue ahead of the other group's softmax
+      side_loads(i);
+      PvPipe<D> pp;
+      pv_start<D>(pp, vt, lo);
+      pv_run<0, 4, D>(pp, vt, lo, ga, gb);
+      side_widen(i);
+      pv_run<4, 8, D>(pp, vt, lo, ga, gb);
+      side_prep(i);
+      pv_run<8, 12, D>(pp, vt, lo, ga, gb);
+      const int issued = side_copies(i);
+      pv_run<12, NPV, D>(pp, vt, lo, ga, gb);
+      qk_run<D>(sm.k[i % kBufs], lo, g, qop, ga, gb);
+      __builtin_amdgcn_s_setprio(0);
       wait_vm(issued);
       lds_sync();
       vphase(i);
     }
-    // M_nt: PV of the last tile only
-    matrix_products<D>(sm.v16[(nt - 1) & 1], nullptr, lo, g, qop, ga, gb);
-    wait_vm(0);
-    lds_sync();
+    {   // M_nt: PV of the last tile only
+      const uint8_t* vt = sm.v16[(nt - 1) & 1];
+      PvPipe<D> pp;
+      __builtin_amdgcn_s_setprio(1);
+      pv_start<D>(pp, vt, lo);
+      pv_run<0, NPV, D>(pp, vt, lo, ga, gb);
+      __builtin_amdgcn_s_setprio(0);
+      wait_vm(0);
+      lds_sync();
+    }
     if (grp == 0) lds_sync();   // the second group's M_nt
 
     // ---- segment result: direct output, or partial for attn_combine
