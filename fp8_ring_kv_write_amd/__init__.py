@@ -22,6 +22,7 @@ from ._lib import (  # noqa: F401
     rope_table_3d,
     workspace_bytes,
     kv_ring_write,
+    kv_ring_write_static,
     kv_ring_delta_rotate,
     kv_ring_delta_rotate_3d,
     ring_attention,

@@ -50,6 +50,7 @@ def _load() -> ctypes.CDLL:
         "kv_ring_rope_table": (ctypes.c_int, [vp, i64, i32, f64]),
         "kv_ring_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
         "kv_ring_write": (ctypes.c_int, [dp, vp, vp, i32, i32, i64, vp, i64, vp, sz, vp]),
+        "kv_ring_write_static": (ctypes.c_int, [dp, vp, vp, i32, i32, i64, vp, i64, vp]),
         "kv_ring_delta_rotate": (ctypes.c_int, [dp, i32, i32, i64, f64, vp, sz, vp]),
         "kv_ring_rope_table_3d": (ctypes.c_int, [vp, vp, i64, i32, vp, f64]),
         "kv_ring_delta_rotate_3d": (ctypes.c_int, [dp, i32, i32, vp, vp, f64, vp, sz, vp]),
@@ -202,6 +203,14 @@ def kv_ring_write(ring: Ring, k_new, v_new, start_slot: int, pos0: int, rope, wo
     _check("kv_ring_write", lib.kv_ring_write(
         ring.desc, _ptr(k_new), _ptr(v_new), n, start_slot, pos0, _ptr(rope), int(rope.shape[0]),
         _ptr(ws), wsb, st))
+
+
+def kv_ring_write_static(ring: Ring, k_new, v_new, start_slot: int, pos0: int, rope, stream=None) -> None:
+    """kv_ring_write with the library's static scratch instead of a workspace (allocates nothing)."""
+    n = int(k_new.shape[0])
+    _check("kv_ring_write_static", lib.kv_ring_write_static(
+        ring.desc, _ptr(k_new), _ptr(v_new), n, start_slot, pos0, _ptr(rope), int(rope.shape[0]),
+        _stream(stream, ring.device)))
 
 
 def kv_ring_delta_rotate(ring: Ring, ring_head: int, filled: int, delta: int,

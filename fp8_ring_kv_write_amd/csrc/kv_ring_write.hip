@@ -17,6 +17,7 @@
 // unit is compiled with -ffp-contract=off) so the codes match the CPU oracle bit for bit.
 
 #include <cstring>
+#include <mutex>
 
 #include "kvring_common.hpp"
 #include "kvring_internal.hpp"
@@ -458,4 +459,37 @@ hipError_t launch_write_and_q_prep(const kv_ring_desc& r, const uint16_t* k_new,
                               r.head_dim, stream);
 }
 
+// ---- the write without a caller workspace (kv_ring_write_static) ---------------------------------
+//
+// Its scratch (the per-(tensor, head, group) partial maxima of pass 1, read by pass 2) lives in a
+// file-scope device array, one copy per GPU, held until the process ends.  Host code must not pass
+// the array's name to a kernel (in host code it is a host-side stand-in); its device address is
+// looked up once per device, with that device current, and kept.  Every call writes every partial
+// it reads before reading it, so the array needs no clearing between calls; calls that overlap on
+// one GPU share it and race.
+
+namespace {
+__device__ __align__(256) float g_write_scratch[kWriteStaticScratchFloats];
+
+std::mutex g_scratch_mutex;
+float* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t write_static_scratch(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(g_write_scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<float*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace kvring
+

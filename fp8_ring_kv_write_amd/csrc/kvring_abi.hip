@@ -162,6 +162,24 @@ int kv_ring_write(const kv_ring_desc* ring, const void* k_new, const void* v_new
                                         static_cast<hipStream_t>(stream)));
 }
 
+int kv_ring_write_static(const kv_ring_desc* ring, const void* k_new, const void* v_new, int32_t n,
+                         int32_t start_slot, int64_t pos0, const float* rope_table, int64_t rope_n_pos,
+                         void* stream) {
+  int st = check_ring(ring);
+  if (st) return st;
+  if (!k_new || !v_new || !rope_table) return KV_RING_ERR_NULL;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(rope_table, 16)) return KV_RING_ERR_ALIGN;
+  if (n < 1 || n > ring->slots || start_slot < 0 || start_slot >= ring->slots) return KV_RING_ERR_RANGE;
+  if (pos0 < 0 || rope_n_pos < 1 || pos0 > rope_n_pos - n) return KV_RING_ERR_POSITION;
+  if (kvring::write_workspace_floats(ring->heads, n) > kvring::kWriteStaticScratchFloats)
+    return KV_RING_ERR_SCRATCH;
+  float* scratch = nullptr;
+  if (kvring::write_static_scratch(&scratch) != hipSuccess) return KV_RING_ERR_LAUNCH;
+  return status_of(kvring::launch_write(*ring, static_cast<const uint16_t*>(k_new),
+                                        static_cast<const uint16_t*>(v_new), n, start_slot, pos0,
+                                        rope_table, scratch, static_cast<hipStream_t>(stream)));
+}
+
 int kv_ring_delta_rotate(const kv_ring_desc* ring, int32_t ring_head, int32_t filled, int64_t delta,
                          double rope_base, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_delta_rotate(ring, ring_head, filled, rope_base, workspace, workspace_bytes);
@@ -343,6 +361,7 @@ const char* kv_ring_status_string(int status) {
     case KV_RING_ERR_POSITION: return "a position falls outside the rotary table";
     case KV_RING_ERR_WORKSPACE: return "workspace missing or too small";
     case KV_RING_ERR_LAUNCH: return "a kernel launch failed";
+    case KV_RING_ERR_SCRATCH: return "the call needs more than the library's static scratch";
     default: return "unknown status";
   }
 }

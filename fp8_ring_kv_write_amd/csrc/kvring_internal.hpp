@@ -15,6 +15,12 @@ int64_t write_workspace_floats(int32_t heads, int32_t n);
 int64_t rotate_workspace_floats(int32_t heads, int32_t slots);
 int64_t attention_workspace_floats(int32_t heads, int32_t slots, int32_t head_dim, int32_t nq);
 
+// kv_ring_write_static: the write's scratch in a static device array of this many floats per GPU.
+constexpr int64_t kWriteStaticScratchFloats = 262144;   // 1 MiB
+constexpr int kMaxDevices = 64;
+// Device address of this device's copy of that array (looked up once per device).
+hipError_t write_static_scratch(float** out);
+
 hipError_t launch_write(const kv_ring_desc& r, const uint16_t* k_new, const uint16_t* v_new,
                         int32_t n, int32_t start_slot, int64_t pos0, const float* rope,
                         float* ws, hipStream_t stream);

@@ -53,7 +53,8 @@ enum {
   KV_RING_ERR_RANGE = -4,      /* n, start_slot, ring_head, filled or nq out of range  */
   KV_RING_ERR_POSITION = -5,   /* a position falls outside the rotary table            */
   KV_RING_ERR_WORKSPACE = -6,  /* workspace NULL or smaller than required              */
-  KV_RING_ERR_LAUNCH = -7      /* a kernel launch failed (HIP error)                   */
+  KV_RING_ERR_LAUNCH = -7,     /* a kernel launch failed (HIP error)                   */
+  KV_RING_ERR_SCRATCH = -8     /* kv_ring_write_static: heads * ceil(n/32) > 131072    */
 };
 
 enum {
@@ -147,6 +148,20 @@ size_t kv_ring_workspace_bytes(int32_t op, int32_t heads, int32_t slots, int32_t
 int kv_ring_write(const kv_ring_desc *ring, const void *k_new, const void *v_new, int32_t n,
                   int32_t start_slot, int64_t pos0, const float *rope_table, int64_t rope_n_pos,
                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kv_ring_write without a workspace, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation): the same kernels,
+ * arguments (less the workspace), results and errors as kv_ring_write; its scratch is a static
+ * device array of the library, 1 MiB per GPU, held until the process ends.
+ * Limit: heads * ceil(n / 32) <= 131072 (e.g. 24 heads and up to 174,752 tokens), else
+ * KV_RING_ERR_SCRATCH and nothing is launched.  The call allocates nothing.  All calls on one GPU
+ * share its scratch: calls that may overlap on one GPU (different streams, or different host
+ * threads without ordering) race and must not be made.
+ */
+int kv_ring_write_static(const kv_ring_desc *ring, const void *k_new, const void *v_new, int32_t n,
+                         int32_t start_slot, int64_t pos0, const float *rope_table,
+                         int64_t rope_n_pos, void *stream);
 
 /*
  * Delta rotation when positions reset (abstract: a delta rotation of the cache instead of

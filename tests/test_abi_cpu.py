@@ -88,7 +88,7 @@ def test_sizes(kv):
 
 def test_status_strings(kv):
     assert kv.status_string(0) == "ok"
-    for s in range(-7, 0):
+    for s in range(-8, 0):
         assert kv.status_string(s) != "unknown status"
 
 
@@ -115,6 +115,13 @@ def test_argument_errors_are_reported_before_any_launch(kv):
     assert L.kv_ring_write(d(good), F, F, 16, 0, -1, F, 128, F, ws, None) == -5
     assert L.kv_ring_write(d(good), F, F, 16, 0, 0, F, 128, None, ws, None) == -6
     assert L.kv_ring_write(d(good), F, F, 16, 0, 0, F, 128, F, ws - 4, None) == -6
+    # write with the static scratch: the same checks, and calls beyond the scratch rejected
+    assert L.kv_ring_write_static(None, F, F, 16, 0, 0, F, 128, None) == -1
+    assert L.kv_ring_write_static(d(good), F + 2, F, 16, 0, 0, F, 128, None) == -2
+    assert L.kv_ring_write_static(d(good), F, F, 65, 0, 0, F, 128, None) == -4
+    assert L.kv_ring_write_static(d(good), F, F, 16, 0, 120, F, 128, None) == -5
+    big = _Desc(F, F, F, F, 8192, 1024, 64)   # 8192 heads x ceil(544 / 32) = 139,264 > 131,072
+    assert L.kv_ring_write_static(d(big), F, F, 544, 0, 0, F, 1024, None) == -8
     # delta rotate
     wr = kv.workspace_bytes(kv.OP_DELTA_ROTATE, 2, 64, 64, 0)
     assert L.kv_ring_delta_rotate(d(good), 64, 10, 5, 10000.0, F, wr, None) == -4
