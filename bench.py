@@ -14,9 +14,13 @@ Also reported (one JSON line on stdout; progress on stderr):
               stream around each launch (53.84 GFLOP algorithmic per call: 4 * 757 * 5788 *
               128 * 24), as a fraction of the FP8 matrix-core peak -> the `roofline` object;
   write       kv_ring_write per call (14.10 MB algorithmic: bf16 K and V read, FP8 codes and
-              per-slot scales written) as a fraction of HBM peak;
+              per-slot scales written) as a fraction of HBM peak, from its cold-cache GPU time
+              (the warm graph-replay time beside it as cache-resident throughput);
   delta_rotate kv_ring_delta_rotate of one full ring (36.67 MB algorithmic: K codes and
-              scales read and written);
+              scales read and written), the same way;
+  launch_floor_us  GPU time of one dependent launch of a near-empty kernel (graph replays);
+  reset_60_layers  the position-reset workload with outliers: 60 rings of Student-t K/V with
+              x20 outlier channels, each rotated by -4,000 then attended (2.2 GB, cold);
   chunk       240 (write + attention) calls over 60 rings, 4 passes, as one chunk;
   cold_cache  write, delta rotation and step timed one call at a time after a 512 MB buffer is
               rewritten (the infinity cache no longer holds the ring, as between two calls of
@@ -61,8 +65,8 @@ ATT_KERNEL = "attn_pp<128>"
 # (FETCH_SIZE, WRITE_SIZE) over this workload, each divided by the factor the same counter
 # reads for a torch copy of --calibrate-copy bytes.  Valid only for the kernel sources whose
 # hash is recorded; reported as null otherwise.
-ATT_TRAFFIC = {"sources": "10736d8585d33874", "bytes": 130_110_000,
-               "read_bytes": 117_130_000, "write_bytes": 12_980_000}
+ATT_TRAFFIC = {"sources": "ebf5bb7581dc77ff", "bytes": 99_040_000,
+               "read_bytes": 76_910_000, "write_bytes": 22_130_000}
 WRITE_BYTES = 2 * N * H * D * 2 + 2 * N * H * D + 2 * N * H * 4
 ROTATE_BYTES = 2 * (H * S * D + H * S * 4)
 
@@ -80,6 +84,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-read-time", action="store_true", help="skip the read-time baseline")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timings")
+    ap.add_argument("--no-reset", action="store_true",
+                    help="skip the position-reset workload (60 outlier rings rotated, then attended)")
     ap.add_argument("--no-graph", action="store_true",
                     help="time repeated calls as issued from Python only (no graph replays; for profilers)")
     ap.add_argument("--no-sweep", action="store_true", help="skip the write-size and fill-up sweeps")
@@ -213,6 +219,13 @@ def main() -> int:
     for b, a in evs:        # torch creates the HIP event on its first record(); the library then
         b.record(stream)    # re-records the same events around the attention kernel
         a.record(stream)
+    # the GPU's clock ramps up under sustained load: run calls for about half a second first
+    t_w = time.perf_counter()
+    while time.perf_counter() - t_w < 0.5:
+        for _ in range(20):
+            kv.ring_attention(ring, head, filled, q, pos0, tab, scale, out=out, lse=lse, workspace=ws_a,
+                              stream=stream)
+        torch.cuda.synchronize()
     for b, a in evs[:5]:
         kv.set_attention_events(b, a)
         kv.ring_attention(ring, head, filled, q, pos0, tab, scale, out=out, lse=lse, workspace=ws_a, stream=stream)
@@ -278,35 +291,63 @@ def main() -> int:
     # ---------------------------------------------------------------- cold caches
     # Between two calls on the same layer a model runs every other layer, whose rings (60 x 36 MB)
     # push this one out of the 256 MB infinity cache.  Here a 512 MB buffer is rewritten before
-    # each timed call to the same effect; each call is then timed alone with events around it.
+    # each call to the same effect.  GPU time per call: a captured graph of (rewrite, call) x 20
+    # replayed, minus a graph of the 20 rewrites alone (no host work between the calls).  The HBM
+    # fractions of the write and the rotation are taken from these times; the warm replays above
+    # (inputs and ring resident in the caches) are reported as cache-resident throughput only.
     cold = None
+    flush = None
     if not args.no_cold:
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        # rewritten by an elementwise kernel (no memset, which a captured graph should not hold)
+        flush = torch.zeros(128 << 20, dtype=torch.float32, device=dev)
         cold_reps = 20
 
-        def timed_cold(fn):
-            tot = 0.0
-            for i in range(cold_reps):
-                flush.fill_(i & 0xFF)
-                b, a = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                b.record(stream)
-                fn(i)
-                a.record(stream)
+        def graph_ms(body, reps):
+            body(0)
+            torch.cuda.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                for i in range(reps):
+                    body(i)
+            gr.replay()
+            torch.cuda.synchronize()
+            best = None
+            for _ in range(3):
+                e0.record(stream)
+                gr.replay()
+                e1.record(stream)
                 torch.cuda.synchronize()
-                tot += b.elapsed_time(a)
-            return 1000.0 * tot / cold_reps
+                t = e0.elapsed_time(e1)
+                best = t if best is None else min(best, t)
+            del gr
+            return best
 
-        c_write = timed_cold(lambda i: kv.kv_ring_write(ring, k_new, v_new, start, pos0, tab, workspace=ws_w,
-                                                        stream=stream))
+        flush_ms = graph_ms(lambda i: flush.add_(1.0), cold_reps)
+
+        def timed_cold(fn):
+            def body(i):
+                flush.add_(1.0)
+                fn(i)
+            return 1000.0 * max(graph_ms(body, cold_reps) - flush_ms, 0.0) / cold_reps
+
+        c_write = timed_cold(lambda i: kv.kv_ring_write(ring, k_new, v_new, start, pos0, tab, workspace=ws_w))
         c_rot = timed_cold(lambda i: kv.kv_ring_delta_rotate(ring, head, filled, -4000 if i % 2 == 0 else 4000,
-                                                             workspace=ws_r, stream=stream))
-        c_step = timed_cold(lambda i: step())
+                                                             workspace=ws_r))
+        c_step = timed_cold(lambda i: kv.kv_ring_write_attend(ring, k_new, v_new, start, pos0, head, filled, q, pos0,
+                                                               tab, scale, out=out, lse=lse, workspace=ws_f))
         cold = {"write_us": round(c_write, 2), "write_GBps": round(WRITE_BYTES / (c_write * 1e-6) / 1e9, 1),
                 "delta_rotate_us": round(c_rot, 2),
                 "delta_rotate_GBps": round(ROTATE_BYTES / (c_rot * 1e-6) / 1e9, 1),
-                "step_us": round(c_step, 2), "calls": cold_reps}
+                "step_us": round(c_step, 2), "calls": cold_reps,
+                "method": "graph of (512 MB rewrite, call) x 20 minus graph of the rewrites"}
         log(f"cold caches: write {c_write:.1f} us, delta rotate {c_rot:.1f} us, step {c_step:.1f} us")
-        del flush
+
+    # ---------------------------------------------------------------- the floor of one launch
+    # GPU time per launch of a kernel that does almost nothing (a one-element add), replayed from a
+    # captured graph like the calls above: the fixed cost every dependent launch pays on this part
+    tiny = torch.zeros(1, dtype=torch.float32, device=dev)
+    launch_floor_us = graph_us(lambda i: tiny.add_(1.0), 50)
+    log(f"launch floor {launch_floor_us:.2f} us per dependent launch")
 
     # ---------------------------------------------------------------- write sizes
     # the write is latency-bound at 757 tokens: its time over the token count
@@ -483,6 +524,77 @@ def main() -> int:
         log(f"chunk of 240 calls: {chunk_ms:.2f} ms eager, {graph_ms} ms as one graph")
         del inputs, rings
 
+    # ---------------------------------------------------------------- position reset, 60 layers
+    # The position-reset workload with outliers: 60 layers' rings hold Student-t (nu = 3) keys and
+    # values with 1% of (head, channel) pairs x20, positions 6,212 .. 11,999 (8 writes of 757, the
+    # last wrapping); each ring is rotated by delta = -4,000, then 757 queries (N(0,1), positions
+    # 7,243 .. 7,999) attend over it.  2.2 GB of rings: every call finds its ring outside the
+    # infinity cache (one ring's contents are built once and copied to the other 59).  Timed as
+    # the full sequence (60 x (rotate, attend)), then the 60 rotations alone and the 60 attention
+    # calls alone; the delta alternates between -4,000 and +4,000 from one repetition to the next
+    # so that positions stay inside the rotary table.
+    reset = None
+    if not args.no_reset:
+        from workloads import outlier_channels, student_t_outlier_bf16
+        layers = 60
+        outl = outlier_channels(tensor_seed("reset", 0, 3), H, D)
+        base = kv.Ring(H, S, D, dev)
+        rsched = steady_ring_schedule(S, N, 8, 5944)
+        for c, w in enumerate(rsched):
+            kv.kv_ring_write(base, to_dev(student_t_outlier_bf16(tensor_seed("reset_l0", c, 1), (N, H, D), outl)),
+                             to_dev(student_t_outlier_bf16(tensor_seed("reset_l0", c, 2), (N, H, D), outl)),
+                             w.start_slot, w.pos0, tab)
+        r_head = (rsched[-1].start_slot + N) % S
+        rq = to_dev(normal_bf16(tensor_seed("reset_l0", 99, 0), (N, H, D)))
+        rings_r = [base]
+        for _ in range(layers - 1):
+            r = kv.Ring(H, S, D, dev)
+            r.k.copy_(base.k), r.v.copy_(base.v), r.k_scale.copy_(base.k_scale), r.v_scale.copy_(base.v_scale)
+            rings_r.append(r)
+        shift = [0]   # the rings' current position offset (0 or -4,000)
+        p_last = rsched[-1].pos0
+
+        def reset_pass(rot=True, att=True):
+            d = -4000 if shift[0] == 0 else 4000
+            for r in rings_r:
+                if rot:
+                    kv.kv_ring_delta_rotate(r, r_head, S, d, workspace=ws_r, stream=stream)
+                if att:   # queries at the positions the rings hold after this pass's rotation
+                    kv.ring_attention(r, r_head, S, rq, p_last + shift[0] + (d if rot else 0), tab, scale,
+                                      out=out, lse=lse, workspace=ws_a, stream=stream)
+            if rot:
+                shift[0] += d
+
+        def timed(rot, att, reps):
+            best = None
+            for _ in range(reps):
+                e0.record(stream)
+                reset_pass(rot, att)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                t = e0.elapsed_time(e1)
+                best = t if best is None else min(best, t)
+            return best
+
+        reset_pass(True, True)   # warm-up, then back to the original positions
+        reset_pass(True, False)
+        torch.cuda.synchronize()
+        full_ms = timed(True, True, reps=1)
+        rot_ms = timed(True, False, reps=2)
+        att_ms = timed(False, True, reps=2)
+        reset = {"layers": layers, "ms": round(full_ms, 3),
+                 "per_layer_us": round(1000.0 * full_ms / layers, 2),
+                 "delta_rotate_us": round(1000.0 * rot_ms / layers, 2),
+                 "delta_rotate_GBps": round(ROTATE_BYTES * layers / (rot_ms * 1e-3) / 1e9, 1),
+                 "delta_rotate_frac_hbm_peak": round(ROTATE_BYTES * layers / (rot_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                 "attention_call_us": round(1000.0 * att_ms / layers, 2),
+                 "attention_calls_per_s": round(layers / (att_ms * 1e-3), 1),
+                 "data": "Student-t(3) K/V, 1% of (head, channel) pairs x20, N(0,1) queries"}
+        log(f"position reset over {layers} rings: {full_ms:.2f} ms ({1000 * full_ms / layers:.1f} us per layer); "
+            f"rotations {1000 * rot_ms / layers:.1f} us each ({reset['delta_rotate_GBps']:.0f} GB/s), "
+            f"attention {1000 * att_ms / layers:.1f} us per call")
+        del rings_r, base
+
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -512,14 +624,11 @@ def main() -> int:
         "attention": {"kernel_us": round(att_us, 2), "call_us": round(call_us, 2),
                       "tflops": round(att_tflops, 1), "frac_fp8_peak": round(att_tflops / FP8_PEAK_TFLOPS, 4),
                       "calls_per_s": round(1e6 / call_us, 1)},
-        "write": {"us": round(write_gpu_us, 2), "GBps": round(write_gbps, 1),
-                  "frac_hbm_peak": round(write_gbps / HBM_PEAK_GBPS, 4), "bytes": WRITE_BYTES,
-                  "frac_of_copy": round(write_gbps / copy_gbps, 4) if copy_gbps else None,
-                  "issued_us": round(write_us, 2)},
-        "delta_rotate": {"us": round(rot_gpu_us, 2), "GBps": round(rot_gbps, 1),
-                         "frac_hbm_peak": round(rot_gbps / HBM_PEAK_GBPS, 4), "bytes": ROTATE_BYTES,
-                         "frac_of_copy": round(rot_gbps / copy_gbps, 4) if copy_gbps else None,
-                         "issued_us": round(rot_us, 2)},
+        "write": hbm_entry(write_gpu_us, write_us, WRITE_BYTES, cold["write_us"] if cold else None, copy_gbps),
+        "delta_rotate": hbm_entry(rot_gpu_us, rot_us, ROTATE_BYTES, cold["delta_rotate_us"] if cold else None,
+                                  copy_gbps),
+        "launch_floor_us": round(launch_floor_us, 2),
+        "reset_60_layers": reset,
         "hbm_copy_GBps": round(copy_gbps, 1) if copy_gbps else None,
         "chunk": chunk,
         "cold_cache": cold,
@@ -539,6 +648,19 @@ def main() -> int:
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def hbm_entry(warm_us, issued_us, nbytes, cold_us, copy_gbps):
+    """An HBM-bound call: the fraction of HBM peak from its cold-cache GPU time (inputs and outputs
+    outside the caches, as in a 60-layer model), with the warm graph-replay time beside it as
+    cache-resident throughput."""
+    e = {"bytes": nbytes, "cache_resident_us": round(warm_us, 2),
+         "cache_resident_GBps": round(nbytes / (warm_us * 1e-6) / 1e9, 1), "issued_us": round(issued_us, 2)}
+    if cold_us:
+        gbps = nbytes / (cold_us * 1e-6) / 1e9
+        e.update({"us": round(cold_us, 2), "GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                  "frac_of_copy": round(gbps / copy_gbps, 4) if copy_gbps else None})
+    return e
 
 
 def kernel_sources_hash(read=None) -> str:
