@@ -478,7 +478,7 @@ __device__ __forceinline__ void raise_max(Group<D>& gr, float tmax) {
 template <int D>
 __device__ __forceinline__ float uniform_probs(Group<D>& gr, float cf, float bm) {
   const v2h one = {(_Float16)1.0f, (_Float16)1.0f};
-  float s2 = 0.0f;
+  float s0 = 0.0f, s1 = 0.0f;   // two chains of dependent steps
 #pragma unroll
   for (int bb = 0; bb < 8; ++bb) {
     float p[4];
@@ -486,10 +486,10 @@ __device__ __forceinline__ float uniform_probs(Group<D>& gr, float cf, float bm)
     for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(gr.sc[bb][r], cf, bm));
     gr.p[2 * bb] = pack_f16(p[0], p[1]);
     gr.p[2 * bb + 1] = pack_f16(p[2], p[3]);
-    s2 = __builtin_amdgcn_fdot2(__builtin_bit_cast(v2h, gr.p[2 * bb]), one, s2, false);
-    s2 = __builtin_amdgcn_fdot2(__builtin_bit_cast(v2h, gr.p[2 * bb + 1]), one, s2, false);
+    s0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(v2h, gr.p[2 * bb]), one, s0, false);
+    s1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(v2h, gr.p[2 * bb + 1]), one, s1, false);
   }
-  return s2;
+  return s0 + s1;
 }
 
 // Softmax of one query group over the tile whose factors are in K buffer bk.
@@ -503,9 +503,8 @@ __device__ __forceinline__ float uniform_probs(Group<D>& gr, float cf, float bm)
 // raised to it and the probabilities are formed again.  The first tile of a segment raises the
 // running max first.  Other tiles take per-slot factors and a max over the tile.
 template <int D>
-__device__ __forceinline__ void softmax_group(const Smem<D>& sm, int bk, int g, bool uniform, Group<D>& gr) {
+__device__ __forceinline__ void softmax_group(const Smem<D>& sm, int bk, int g, bool uniform, float cf, float bf, float ivu, Group<D>& gr) {
   if (uniform) {
-    const float cf = sm.ck[bk][0], bf = sm.nb[bk][0], ivu = sm.iv[bk][0];
     auto tile_max = [&]() __attribute__((always_inline)) {
       float rmax = gr.sc[0][0];
 #pragma unroll
@@ -678,12 +677,10 @@ __global__ __launch_bounds__(kThreads) void attn_pp(AttnArgs a) {
       issue_k<D>(a, sm, (i + 2) % kBufs, phys(k0 + i + 2), head, w, lane);
       return nv + nk;
     };
-    auto vphase = [&](int i) __attribute__((always_inline)) {
+    auto vphase = [&](int i, bool uniform, float cf, float bf, float ivu) __attribute__((always_inline)) {
       const int bk = i % kBufs;
-      const int4 un = *reinterpret_cast<const int4*>(&sm.uni[bk][0]);
-      const bool uniform = __builtin_amdgcn_readfirstlane(un.x & un.y & un.z & un.w) != 0;
-      softmax_group<D>(sm, bk, g, uniform, ga);
-      softmax_group<D>(sm, bk, g, uniform, gb);
+      softmax_group<D>(sm, bk, g, uniform, cf, bf, ivu, ga);
+      softmax_group<D>(sm, bk, g, uniform, cf, bf, ivu, gb);
       wait_vm(0);
       lds_sync();
     };
@@ -691,14 +688,20 @@ __global__ __launch_bounds__(kThreads) void attn_pp(AttnArgs a) {
     {   // M_0: QK of tile 0, then its side work
       __builtin_amdgcn_s_setprio(1);
       side_loads(0);
+      const int4 un = *reinterpret_cast<const int4*>(&sm.uni[0][0]);
+      const float cf0 = sm.ck[0][0], bf0 = sm.nb[0][0], iv0 = sm.iv[0][0];
       qk_run<D>(sm.k[0], lo, g, qop, ga, gb);
       __builtin_amdgcn_s_setprio(0);
+      const bool uniform = __builtin_amdgcn_readfirstlane(un.x & un.y & un.z & un.w) != 0;
+      const float cf = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(cf0)));
+      const float bf = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(bf0)));
+      const float ivu = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(iv0)));
       side_widen(0);
       side_prep(0);
       const int issued = side_copies(0);
       wait_vm(issued);
       lds_sync();
-      vphase(0);
+      vphase(0, uniform, cf, bf, ivu);
     }
     constexpr int NPV = NDB * 4;
     for (int i = 1; i < nt; ++i) {   // M_i, V_i
@@ -714,11 +717,17 @@ __global__ __launch_bounds__(kThreads) void attn_pp(AttnArgs a) {
       pv_run<8, 12, D>(pp, vt, lo, ga, gb);
       const int issued = side_copies(i);
       pv_run<12, NPV, D>(pp, vt, lo, ga, gb);
+      const int4 un = *reinterpret_cast<const int4*>(&sm.uni[i % kBufs][0]);
+      const float cf0 = sm.ck[i % kBufs][0], bf0 = sm.nb[i % kBufs][0], iv0 = sm.iv[i % kBufs][0];
       qk_run<D>(sm.k[i % kBufs], lo, g, qop, ga, gb);
       __builtin_amdgcn_s_setprio(0);
+      const bool uniform = __builtin_amdgcn_readfirstlane(un.x & un.y & un.z & un.w) != 0;
+      const float cf = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(cf0)));
+      const float bf = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(bf0)));
+      const float ivu = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(iv0)));
       wait_vm(issued);
       lds_sync();
-      vphase(i);
+      vphase(i, uniform, cf, bf, ivu);
     }
     {   // M_nt: PV of the last tile only
       const uint8_t* vt = sm.v16[(nt - 1) & 1];
