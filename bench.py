@@ -133,9 +133,9 @@ def main() -> int:
     v_new = to_dev(normal_bf16(tensor_seed("single_call", 100, 2), (N, H, D)))
     q = to_dev(normal_bf16(tensor_seed("single_call", 99, 0), (N, H, D)))
     scale = 1.0 / math.sqrt(D)
-    ws_w = torch.empty(kv.workspace_bytes(kv.OP_WRITE, H, S, D, N), dtype=torch.uint8, device=dev)
-    ws_a = torch.empty(kv.workspace_bytes(kv.OP_ATTENTION, H, S, D, N), dtype=torch.uint8, device=dev)
-    ws_r = torch.empty(kv.workspace_bytes(kv.OP_DELTA_ROTATE, H, S, D, 0), dtype=torch.uint8, device=dev)
+    ws_w = torch.zeros(kv.workspace_bytes(kv.OP_WRITE, H, S, D, N), dtype=torch.uint8, device=dev)
+    ws_a = torch.zeros(kv.workspace_bytes(kv.OP_ATTENTION, H, S, D, N), dtype=torch.uint8, device=dev)
+    ws_r = torch.zeros(kv.workspace_bytes(kv.OP_DELTA_ROTATE, H, S, D, 0), dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
     lse = torch.empty((H, N), dtype=torch.float32, device=dev)
 
@@ -147,7 +147,7 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    ws_f = torch.empty(kv.workspace_bytes(kv.OP_WRITE_ATTEND, H, S, D, N), dtype=torch.uint8, device=dev)
+    ws_f = torch.zeros(kv.workspace_bytes(kv.OP_WRITE_ATTEND, H, S, D, N), dtype=torch.uint8, device=dev)
 
     def step():
         kv.kv_ring_write_attend(ring, k_new, v_new, start, pos0, head, filled, q, pos0, tab, scale,
@@ -357,7 +357,7 @@ def main() -> int:
         for n_tok in (32, 128, 757, 1514, 2894, 5788):
             kk = to_dev(normal_bf16(tensor_seed("sweep", n_tok, 1), (n_tok, H, D)))
             vv = to_dev(normal_bf16(tensor_seed("sweep", n_tok, 2), (n_tok, H, D)))
-            wsn = torch.empty(kv.workspace_bytes(kv.OP_WRITE, H, S, D, n_tok), dtype=torch.uint8, device=dev)
+            wsn = torch.zeros(kv.workspace_bytes(kv.OP_WRITE, H, S, D, n_tok), dtype=torch.uint8, device=dev)
             us = graph_us(lambda i: kv.kv_ring_write(ring, kk, vv, 0, 0, tab, workspace=wsn), 20)
             nbytes = n_tok * H * D * (2 * 2 + 2) + 2 * n_tok * H * 4
             sweep.append({"tokens": n_tok, "us": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)})
@@ -431,7 +431,7 @@ def main() -> int:
         win = [[to_dev(normal_bf16(tensor_seed("read_time", 0, t), (S, H, D))) for t in (1, 2)],
                [torch.empty((S, H, D), dtype=torch.bfloat16, device=dev) for _ in range(2)]]
         rt_ring = kv.Ring(H, S, D, dev)
-        ws_rt = torch.empty(kv.workspace_bytes(kv.OP_WRITE, H, S, D, S), dtype=torch.uint8, device=dev)
+        ws_rt = torch.zeros(kv.workspace_bytes(kv.OP_WRITE, H, S, D, S), dtype=torch.uint8, device=dev)
         w_pos0 = pos0 + N - S          # the window ends with the new tokens
 
         def rt_maintain(i):

@@ -31,5 +31,6 @@ from ._lib import (  # noqa: F401
     kv_window_advance,
     set_attention_events,
     status_string,
+    sync_status,
     lib,
 )

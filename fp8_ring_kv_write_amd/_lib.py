@@ -57,6 +57,7 @@ def _load() -> ctypes.CDLL:
         "ring_attention": (ctypes.c_int, [dp, i32, i32, vp, i32, i64, vp, i64, f32, vp, vp, vp, sz, vp]),
         "kv_ring_fp8_encode": (ctypes.c_int, [vp, vp, i64, vp]),
         "kv_ring_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "kv_ring_sync_status": (ctypes.c_int, [vp, vp]),
         "kv_ring_set_attention_events": (ctypes.c_int, [vp, vp]),
         "kv_window_advance": (ctypes.c_int, [vp, vp, vp, i32, i32, i64, vp]),
         "kv_ring_write_attend": (ctypes.c_int, [dp, vp, vp, i32, i32, i64, i32, i32, vp, i32, i64, vp,
@@ -188,9 +189,32 @@ def _ws(ws, need: int, device, stream_handle: int):
         size = max(need, 1 << 20, 2 * cur.numel() if cur is not None else 0)
         if cur is not None:
             _WS_RETIRED.append(cur)
-        cur = torch.empty(size, dtype=torch.uint8, device=dev)
+        # zero-filled: every workspace starts with synchronisation records that must be zero
+        # before their first use (every call then leaves them ready for the next)
+        cur = torch.zeros(size, dtype=torch.uint8, device=dev)
         _WS_POOL[key] = cur
     return cur, int(cur.numel())
+
+
+def sync_status(workspace=None, device=None, stream=None) -> int:
+    """0 unless a synchronisation wait of the calls made with `workspace` (default: every
+    workspace the binding has pooled for `device`) exceeded its bound (then -9, the outputs of
+    those calls are not to be trusted).  Waits for the device first."""
+    import torch
+    dev = torch.device(device if device is not None else "cuda")
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    torch.cuda.synchronize(idx)
+    st = _stream(stream, torch.device("cuda", idx))
+    if workspace is not None:
+        bufs = [workspace]
+    else:
+        bufs = [b for (d, _), b in _WS_POOL.items() if d == idx]
+        bufs += [b for b in _WS_RETIRED if b.device.index == idx]
+    for b in bufs:
+        r = int(lib.kv_ring_sync_status(_ptr(b), st))
+        if r:
+            return r
+    return 0
 
 
 def kv_ring_write(ring: Ring, k_new, v_new, start_slot: int, pos0: int, rope, workspace=None,

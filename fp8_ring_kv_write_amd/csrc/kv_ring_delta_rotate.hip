@@ -5,11 +5,10 @@
 //
 // Keys are dequantised (decode * slot scale, float32), rotated by the delta table (float32,
 // every operation rounded), and requantised with one new per-head scale over all valid
-// slots.  Two passes over the K codes (the second mostly from L2 / infinity cache), no
-// atomics: pass 1 writes per-(head, tile) absmax partials, pass 2 reduces them and rewrites
-// codes and scales.  A work-group takes one 128-slot tile of one head, each thread 4 (head_dim
-// 128) or 2 (64) 16-byte units of 16 channels with all of its loads in flight at once.  V is
-// untouched.
+// slots.  One launch, one read of the K codes: a work-group takes one 128-slot tile of one head
+// (each thread 4 (head_dim 128) or 2 (64) 16-byte units of 16 channels, all of its loads in
+// flight at once), rotates it in registers, meets the head's other work-groups (head_sync) for
+// the new absmax, and rewrites its codes and scales.  V is untouched.
 
 #include "kvring_common.hpp"
 #include "kvring_internal.hpp"
@@ -88,53 +87,38 @@ __device__ inline void load_units(const uint8_t* tile, const float* srow, int t,
   }
 }
 
-// grid = (tiles, heads): max |rotated key| over the valid slots of one tile of one head.
-template <int D>
-__global__ __launch_bounds__(kThreads) void rotate_absmax_partials(
-    const uint8_t* __restrict__ kc, const float* __restrict__ k_scale, RotGeom g, DeltaTable tab,
-    float* __restrict__ partial) {
-  __shared__ float red[4];
-  const int t = blockIdx.x, h = blockIdx.y;
-  Units<D> x;
-  load_units<D>(kc + ((int64_t)h * g.tiles + t) * kTile * D, k_scale + (int64_t)h * g.slots, t, g, x);
-  float m = 0.0f;
-#pragma unroll
-  for (int j = 0; j < kUnitsPerThread<D>; ++j) {
-    if (!x.ok[j]) continue;
-    float v[16];
-    dequant_rotate<16>(x.w[j], x.scale[j], tab, 8 * x.q[j], v);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[e]));
-  }
-  m = block_max_256(m, red);
-  if (threadIdx.x == 0) partial[(int64_t)h * g.tiles + t] = m;
-}
-
-// grid = (tiles, heads): requantise one tile of one head with the head's new scale.
+// grid = (tiles, heads), tiles varying fastest (a head's work-groups are consecutive, as
+// head_sync requires): one tile of one head, rotated, requantised with the head's new scale.
 template <int D>
 __global__ __launch_bounds__(kThreads) void rotate_requantize(
-    uint8_t* __restrict__ kc, float* __restrict__ k_scale, RotGeom g, DeltaTable tab,
-    const float* __restrict__ partial) {
-  __shared__ float red[4];
+    uint8_t* __restrict__ kc, float* __restrict__ k_scale, RotGeom g, DeltaTable tab, void* sync) {
+  __shared__ float sl[10];
   const int t = blockIdx.x, h = blockIdx.y;
   uint8_t* tile = kc + ((int64_t)h * g.tiles + t) * kTile * D;
   float* srow = k_scale + (int64_t)h * g.slots;
   Units<D> x;
   load_units<D>(tile, srow, t, g, x);
-  // the head's new absmax from the per-tile partials (rings of up to 64 tiles: each wavefront
-  // reduces them itself)
-  const float a = list_max(partial + (int64_t)h * g.tiles, int(g.tiles), red);
-  __syncthreads();   // every thread's reads of the old slot scales precede the writes below
+  float v[kUnitsPerThread<D>][16];
+  float m = 0.0f, unused = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kUnitsPerThread<D>; ++j) {
+    dequant_rotate<16>(x.w[j], x.scale[j], tab, 8 * x.q[j], v[j]);
+    if (!x.ok[j]) continue;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[j][e]));
+  }
+  // the head's new absmax; every thread's reads of the old slot scales (above) precede its
+  // barrier, and so the writes below
+  head_sync(sync_record(sync, 0, h), sync_error_word(sync), int(g.tiles), false, m, unused, sl);
   float scale, inv;
-  scale_from_absmax(a, scale, inv);
+  scale_from_absmax(m, scale, inv);
 #pragma unroll
   for (int j = 0; j < kUnitsPerThread<D>; ++j) {
     if (!x.ok[j]) continue;
-    float v[16];
-    dequant_rotate<16>(x.w[j], x.scale[j], tab, 8 * x.q[j], v);
     uint32_t o[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = e4m3x4(v[4 * e] * inv, v[4 * e + 1] * inv, v[4 * e + 2] * inv, v[4 * e + 3] * inv);
+    for (int e = 0; e < 4; ++e)
+      o[e] = e4m3x4(v[j][4 * e] * inv, v[j][4 * e + 1] * inv, v[j][4 * e + 2] * inv, v[j][4 * e + 3] * inv);
     const int p = j * kThreads + int(threadIdx.x);
     *reinterpret_cast<uint4*>(tile + p * 16) = make_uint4(o[0], o[1], o[2], o[3]);
     if (x.q[j] == 0) srow[x.slot[j]] = scale;
@@ -143,9 +127,7 @@ __global__ __launch_bounds__(kThreads) void rotate_requantize(
 
 }  // namespace
 
-int64_t rotate_workspace_floats(int32_t heads, int32_t slots) {
-  return (int64_t)heads * ((slots + kChunk - 1) / kChunk);
-}
+int64_t rotate_workspace_floats(int32_t, int32_t) { return kSyncBytes / 4; }
 
 hipError_t launch_delta_rotate(const kv_ring_desc& r, int32_t ring_head, int32_t filled,
                                const DeltaTable& tab, float* ws, hipStream_t stream) {
@@ -159,19 +141,9 @@ hipError_t launch_delta_rotate(const kv_ring_desc& r, int32_t ring_head, int32_t
   g.tiles = tile_count(r.slots);
   dim3 grid(g.tiles, r.heads);
   if (r.head_dim == 128)
-    hipLaunchKernelGGL(rotate_absmax_partials<128>, grid, dim3(kThreads), 0, stream, r.k,
-                       r.k_scale, g, tab, ws);
+    hipLaunchKernelGGL(rotate_requantize<128>, grid, dim3(kThreads), 0, stream, r.k, r.k_scale, g, tab, ws);
   else
-    hipLaunchKernelGGL(rotate_absmax_partials<64>, grid, dim3(kThreads), 0, stream, r.k,
-                       r.k_scale, g, tab, ws);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (r.head_dim == 128)
-    hipLaunchKernelGGL(rotate_requantize<128>, grid, dim3(kThreads), 0, stream, r.k, r.k_scale, g,
-                       tab, ws);
-  else
-    hipLaunchKernelGGL(rotate_requantize<64>, grid, dim3(kThreads), 0, stream, r.k, r.k_scale, g,
-                       tab, ws);
+    hipLaunchKernelGGL(rotate_requantize<64>, grid, dim3(kThreads), 0, stream, r.k, r.k_scale, g, tab, ws);
   return hipGetLastError();
 }
 

@@ -2,16 +2,13 @@
 // (Runway Characters abstract: RoPE and FP8 quantisation applied once per write into a ring
 // cache; cpdf.ai blog, section "Como rodar 57B em tempo real com batch size 1").
 //
-// Two bandwidth-bound passes, no atomics:
-//   1. rope_absmax_partials: each work-group takes 32 tokens x 1 head, rotates K, and writes
-//      the max |K'| and max |V| of its rows to a per-(tensor, head, group) partial;
-//   2. quantize_pass: each write work-group takes one aligned 32-slot chunk of the ring x 1
-//      head, reduces the head's partials to the write's absmax, rotates and quantises again,
-//      and stores K and V codes into the tile layout (V transposed).
-// The attention's queries take the same two passes (their absmax partials, then rotation and
-// quantisation in the QK product's operand order), in the same launches when the attention
-// follows a write (kv_ring_write_attend).
-// The second read of the bf16 inputs is served mostly from the L2 / infinity cache.
+// One bandwidth-bound launch, one read of the inputs: each write work-group takes one aligned
+// 32-slot chunk of the ring x 1 head, loads its tokens, rotates K, and meets the head's other
+// work-groups (head_sync) for the write's absmax of K' and V; then it encodes what it holds in
+// registers and stores K and V codes into the tile layout (V transposed).  The attention's
+// queries are prepared the same way (rotation, the head's absmax, quantisation in the QK
+// product's operand order), in the same launch when the attention follows a write
+// (kv_ring_write_attend).
 //
 // Arithmetic is float32 with every product and sum rounded separately (the translation
 // unit is compiled with -ffp-contract=off) so the codes match the CPU oracle bit for bit.
@@ -44,26 +41,6 @@ __device__ inline void load_bf16(const uint16_t* p, float (&x)[CPT]) {
   }
 }
 
-// Rotate CPT channels (CPT/2 interleaved pairs) with the table row of this position.
-// `tab` points at the (cos, sin) of the first pair; 16-byte aligned.
-template <int CPT>
-__device__ inline void rope_pairs(float (&x)[CPT], const float* tab) {
-  const float4* t4 = reinterpret_cast<const float4*>(tab);
-#pragma unroll
-  for (int j = 0; j < CPT / 4; ++j) {
-    float4 t = t4[j];  // cos0 sin0 cos1 sin1 for pairs 2j, 2j+1
-    float cs[2][2] = {{t.x, t.y}, {t.z, t.w}};
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int p = 2 * j + e;
-      const float xe = x[2 * p], xo = x[2 * p + 1];
-      const float c = cs[e][0], s = cs[e][1];
-      x[2 * p] = xe * c - xo * s;
-      x[2 * p + 1] = xe * s + xo * c;
-    }
-  }
-}
-
 template <int CPT>
 __device__ inline float absmax(const float (&x)[CPT]) {
   float m = 0.0f;
@@ -72,46 +49,9 @@ __device__ inline float absmax(const float (&x)[CPT]) {
   return m;
 }
 
-// Pass 1: per (tensor, head, 32-token group) max |x|, rotated tensors (K, Q) after RoPE at their
-// positions.  One launch can serve up to three tensors (K and V of a write, and the queries of
-// the attention that follows it): grid = (max groups, heads, jobs); job z writes its partials
-// [heads][groups of job z] at its own base pointer.
-struct AbsmaxJob {
-  const uint16_t* x;   // bfloat16 [n][heads][D]
-  float* partial;      // [heads][groups]
-  int64_t pos0;        // position of token 0 (rotated jobs)
-  int32_t n, groups, rotate;
-};
-struct AbsmaxJobs {
-  AbsmaxJob job[3];
-};
-
-template <int D>
-__global__ __launch_bounds__(kThreads) void rope_absmax_partials(AbsmaxJobs jobs, int32_t heads,
-                                                                 const float* __restrict__ rope) {
-  constexpr int CPT = D / 8;
-  __shared__ float red[4];
-  const AbsmaxJob& jb = jobs.job[blockIdx.z];
-  const int grp = blockIdx.x, h = blockIdx.y;
-  if (grp >= jb.groups) return;   // uniform per work-group: this job has fewer tokens
-  const int i = grp * kChunk + (threadIdx.x >> 3);
-  const int cg = threadIdx.x & 7;
-  float m = 0.0f;
-  if (i < jb.n) {
-    const uint16_t* src = jb.x + ((int64_t)i * heads + h) * D + cg * CPT;
-    float x[CPT];
-    load_bf16<CPT>(src, x);
-    if (jb.rotate) rope_pairs<CPT>(x, rope + ((jb.pos0 + i) * (D / 2) + cg * (CPT / 2)) * 2);
-    m = absmax<CPT>(x);
-  }
-  m = block_max_256(m, red);
-  if (threadIdx.x == 0) jb.partial[(int64_t)h * jb.groups + grp] = m;
-}
-
 struct WriteGeom {
   int32_t n, start, slots, heads;
   int32_t chunk_a0, n_chunks_a;  // first chunk of the run [start, min(start+n, slots))
-  int32_t n_partial_groups;      // partial groups per (tensor, head) from pass 1
   int64_t tiles;
   int64_t pos0;
 };
@@ -119,7 +59,7 @@ struct WriteGeom {
 struct WriteArgs {
   const uint16_t* k_new;
   const uint16_t* v_new;
-  const float* partial;   // pass-1 partials [2][heads][groups]
+  void* sync;             // the workspace: its per-head records, slot 0
   uint8_t* kc;
   uint8_t* vc;
   float* k_scale;
@@ -133,32 +73,29 @@ struct WriteArgs {
 // (per 128-query row: wavefront w, lane 16g + li -> query 16w + li, channels 32g .. 32g+31).
 struct QuantQArgs {
   const uint16_t* q;      // bfloat16 [nq][heads][D]
-  const float* partial;   // [heads][groups]: the queries' absmax partials from pass 1
+  void* sync;             // the workspace: its per-head records, slot 1
   uint8_t* codes;         // [heads * qtiles][8][64][32], qtiles even
   float* scale;           // [heads]
   int64_t pos0;
-  int32_t nq, groups, qtiles;
+  int32_t nq, qtiles;
   int32_t blocks;         // 2 * qtiles (a work-group takes 64 queries of a row); 0: none
 };
 
-// Pass 2 of the write: one aligned 32-slot chunk of the ring x one head.
+// The write's work-group: one aligned 32-slot chunk of the ring x one head.
 template <int D>
 __device__ inline void write_chunk(const WriteArgs& wa, const float* __restrict__ rope, int blk, int h) {
   constexpr int CPT = D / 8;
-  __shared__ float red[2][4];
+  __shared__ float sl[10];
   __shared__ __align__(16) uint8_t vlds[kChunk][D];
   const WriteGeom& g = wa.g;
   const uint16_t* __restrict__ k_new = wa.k_new;
   const uint16_t* __restrict__ v_new = wa.v_new;
-  const float* __restrict__ partial = wa.partial;
   uint8_t* __restrict__ kc = wa.kc;
   uint8_t* __restrict__ vc = wa.vc;
   float* __restrict__ k_scale = wa.k_scale;
   float* __restrict__ v_scale = wa.v_scale;
   const int chunk = blk < g.n_chunks_a ? g.chunk_a0 + blk : blk - g.n_chunks_a;
 
-  // this thread's inputs first (they do not depend on the scales), so that their latency
-  // overlaps the reduction of the partials
   const int t = threadIdx.x >> 3, cg = threadIdx.x & 7;
   const int slot = chunk * kChunk + t;
   int i = slot - g.start;
@@ -175,27 +112,31 @@ __device__ inline void write_chunk(const WriteArgs& wa, const float* __restrict_
     for (int j = 0; j < CPT / 4; ++j) tab[j] = t4[j];
   }
 
-  // the write's per-head absmax of K' and V from the pass-1 partials (up to 2,048 tokens each
-  // wavefront reduces the partial lists itself, with no barrier)
-  const float ak = list_max(partial + (int64_t)h * g.n_partial_groups, g.n_partial_groups, red[0]);
-  const float av = list_max(partial + ((int64_t)g.heads + h) * g.n_partial_groups, g.n_partial_groups, red[1]);
-  float sk, ik, sv, iv;
-  scale_from_absmax(ak, sk, ik);
-  scale_from_absmax(av, sv, iv);
-
+  // RoPE of K (pairs 2j, 2j+1 of this thread's channels), then the write's per-head absmax of
+  // K' and V over every work-group of the head
+  float mk = 0.0f, mv = 0.0f;
   if (mine) {
-    float (&x)[CPT] = xk;
 #pragma unroll
-    for (int j = 0; j < CPT / 4; ++j) {   // RoPE: pairs 2j, 2j+1 of this thread's channels
+    for (int j = 0; j < CPT / 4; ++j) {
       const float cs[2][2] = {{tab[j].x, tab[j].y}, {tab[j].z, tab[j].w}};
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int p = 2 * j + e;
-        const float xe = x[2 * p], xo = x[2 * p + 1];
-        x[2 * p] = xe * cs[e][0] - xo * cs[e][1];
-        x[2 * p + 1] = xe * cs[e][1] + xo * cs[e][0];
+        const float xe = xk[2 * p], xo = xk[2 * p + 1];
+        xk[2 * p] = xe * cs[e][0] - xo * cs[e][1];
+        xk[2 * p + 1] = xe * cs[e][1] + xo * cs[e][0];
       }
     }
+    mk = absmax<CPT>(xk);
+    mv = absmax<CPT>(xv);
+  }
+  head_sync(sync_record(wa.sync, 0, h), sync_error_word(wa.sync), wa.blocks, true, mk, mv, sl);
+  float sk, ik, sv, iv;
+  scale_from_absmax(mk, sk, ik);
+  scale_from_absmax(mv, sv, iv);
+
+  if (mine) {
+    float (&x)[CPT] = xk;
     uint32_t w[CPT / 4];
 #pragma unroll
     for (int j = 0; j < CPT / 4; ++j)
@@ -254,14 +195,14 @@ __device__ inline void write_chunk(const WriteArgs& wa, const float* __restrict_
 template <int D>
 __device__ inline void quantize_q_half(const QuantQArgs& qa_, const float* __restrict__ rope, int blk,
                                        int h, int heads) {
-  __shared__ float red[4];
+  __shared__ float sl[10];
   const int qt = blk >> 1, w = 4 * (blk & 1) + (int(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
   const int i = qt * 128 + w * 16 + li;
   const bool live = i < qa_.nq && (D == 128 || g < 2);
   uint4 raw[4];
   float4 tab[8];
-  if (live) {   // inputs first: their latency overlaps the reduction below
+  if (live) {
     const uint4* src = reinterpret_cast<const uint4*>(qa_.q + ((int64_t)i * heads + h) * D + 32 * g);
     const float4* t4 = reinterpret_cast<const float4*>(rope + ((qa_.pos0 + i) * (D / 2) + 16 * g) * 2);
 #pragma unroll
@@ -269,34 +210,41 @@ __device__ inline void quantize_q_half(const QuantQArgs& qa_, const float* __res
 #pragma unroll
     for (int j = 0; j < 8; ++j) tab[j] = t4[j];
   }
-  const float a = list_max(qa_.partial + (int64_t)h * qa_.groups, qa_.groups, red);
+  // rotation (8 channels, 4 pairs, per step), then the head's absmax over every query
+  float y[32];
+  float m = 0.0f, unused = 0.0f;
+  if (live) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t bw[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+      const float4 t0 = tab[2 * j], t1 = tab[2 * j + 1];
+      const float cs[4][2] = {{t0.x, t0.y}, {t0.z, t0.w}, {t1.x, t1.y}, {t1.z, t1.w}};
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float xe = __uint_as_float(bw[p] << 16), xo = __uint_as_float(bw[p] & 0xFFFF0000u);
+        y[8 * j + 2 * p] = xe * cs[p][0] - xo * cs[p][1];
+        y[8 * j + 2 * p + 1] = xe * cs[p][1] + xo * cs[p][0];
+      }
+    }
+    m = absmax<32>(y);
+  }
+  head_sync(sync_record(qa_.sync, 1, h), sync_error_word(qa_.sync), qa_.blocks, false, m, unused, sl);
   float scale, inv;
-  scale_from_absmax(a, scale, inv);
+  scale_from_absmax(m, scale, inv);
   if (blk == 0 && threadIdx.x == 0) qa_.scale[h] = scale;
   uint32_t wd[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (live) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {   // 8 channels (4 pairs) per step
-      const uint32_t bw[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
-      const float4 t0 = tab[2 * j], t1 = tab[2 * j + 1];
-      const float cs[4][2] = {{t0.x, t0.y}, {t0.z, t0.w}, {t1.x, t1.y}, {t1.z, t1.w}};
-      float y[8];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const float xe = __uint_as_float(bw[p] << 16), xo = __uint_as_float(bw[p] & 0xFFFF0000u);
-        y[2 * p] = (xe * cs[p][0] - xo * cs[p][1]) * inv;
-        y[2 * p + 1] = (xe * cs[p][1] + xo * cs[p][0]) * inv;
-      }
-      wd[2 * j] = e4m3x4(y[0], y[1], y[2], y[3]);
-      wd[2 * j + 1] = e4m3x4(y[4], y[5], y[6], y[7]);
-    }
+    for (int j = 0; j < 8; ++j)
+      wd[j] = e4m3x4(y[4 * j] * inv, y[4 * j + 1] * inv, y[4 * j + 2] * inv, y[4 * j + 3] * inv);
   }
   uint4* dst = reinterpret_cast<uint4*>(qa_.codes + ((((int64_t)h * qa_.qtiles + qt) * 8 + w) * 64 + lane) * 32);
   dst[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
   dst[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
 }
 
-// Pass 2: grid = (write blocks + query blocks, heads); each work-group does one or the other.
+// grid = (write blocks + query blocks, heads); each work-group does one or the other.  A head's
+// work-groups have consecutive indices (x varies fastest), as head_sync requires.
 template <int D>
 __global__ __launch_bounds__(kThreads) void quantize_pass(WriteArgs wa, QuantQArgs qa_,
                                                           const float* __restrict__ rope, int32_t heads) {
@@ -309,34 +257,9 @@ __global__ __launch_bounds__(kThreads) void quantize_pass(WriteArgs wa, QuantQAr
 
 }  // namespace
 
-int64_t write_workspace_floats(int32_t heads, int32_t n) {
-  return 2LL * heads * ((n + kChunk - 1) / kChunk);
-}
+int64_t write_workspace_floats(int32_t, int32_t) { return kSyncBytes / 4; }
 
 namespace {
-
-hipError_t launch_absmax(const AbsmaxJobs& jobs, int njobs, int32_t heads, int32_t head_dim,
-                         const float* rope, hipStream_t stream) {
-  int gx = 1;
-  for (int j = 0; j < njobs; ++j) gx = jobs.job[j].groups > gx ? jobs.job[j].groups : gx;
-  dim3 g1(gx, heads, njobs);
-  if (head_dim == 128)
-    hipLaunchKernelGGL(rope_absmax_partials<128>, g1, dim3(kThreads), 0, stream, jobs, heads, rope);
-  else
-    hipLaunchKernelGGL(rope_absmax_partials<64>, g1, dim3(kThreads), 0, stream, jobs, heads, rope);
-  return hipGetLastError();
-}
-
-AbsmaxJob absmax_job(const uint16_t* x, int32_t n, bool rotate, int64_t pos0, float* partial) {
-  AbsmaxJob j;
-  j.x = x;
-  j.partial = partial;
-  j.pos0 = pos0;
-  j.n = n;
-  j.groups = (n + kChunk - 1) / kChunk;
-  j.rotate = rotate ? 1 : 0;
-  return j;
-}
 
 }  // namespace
 
@@ -347,7 +270,7 @@ WriteArgs write_args(const kv_ring_desc& r, const uint16_t* k_new, const uint16_
   WriteArgs wa;
   wa.k_new = k_new;
   wa.v_new = v_new;
-  wa.partial = ws;
+  wa.sync = ws;
   wa.kc = r.k;
   wa.vc = r.v;
   wa.k_scale = r.k_scale;
@@ -359,7 +282,6 @@ WriteArgs write_args(const kv_ring_desc& r, const uint16_t* k_new, const uint16_
   g.heads = r.heads;
   g.tiles = tile_count(r.slots);
   g.pos0 = pos0;
-  g.n_partial_groups = (n + kChunk - 1) / kChunk;
   const int end_a = start_slot + n < r.slots ? start_slot + n : r.slots;
   g.chunk_a0 = start_slot / kChunk;
   g.n_chunks_a = (end_a - 1) / kChunk - g.chunk_a0 + 1;
@@ -375,16 +297,15 @@ WriteArgs write_args(const kv_ring_desc& r, const uint16_t* k_new, const uint16_
   return wa;
 }
 
-QuantQArgs quant_q_args(const uint16_t* q, int32_t nq, int64_t q_pos0, const float* q_partial,
-                        uint8_t* codes, float* scale) {
+QuantQArgs quant_q_args(const uint16_t* q, int32_t nq, int64_t q_pos0, void* sync, uint8_t* codes,
+                        float* scale) {
   QuantQArgs qa_;
   qa_.q = q;
-  qa_.partial = q_partial;
+  qa_.sync = sync;
   qa_.codes = codes;
   qa_.scale = scale;
   qa_.pos0 = q_pos0;
   qa_.nq = nq;
-  qa_.groups = (nq + kChunk - 1) / kChunk;
   // an even number of 128-query tiles per head: the attention takes its rows 256 queries at a
   // time (the padding queries of the last tile are stored as zero codes)
   qa_.qtiles = 2 * ((nq + 255) / 256);
@@ -419,56 +340,38 @@ QuantQArgs no_queries() {
 hipError_t launch_write(const kv_ring_desc& r, const uint16_t* k_new, const uint16_t* v_new,
                         int32_t n, int32_t start_slot, int64_t pos0, const float* rope,
                         float* ws, hipStream_t stream) {
-  const int ngroups = (n + kChunk - 1) / kChunk;
-  AbsmaxJobs jobs;
-  jobs.job[0] = absmax_job(k_new, n, true, pos0, ws);
-  jobs.job[1] = absmax_job(v_new, n, false, 0, ws + (int64_t)r.heads * ngroups);
-  jobs.job[2] = jobs.job[1];
-  hipError_t e = launch_absmax(jobs, 2, r.heads, r.head_dim, rope, stream);
-  if (e != hipSuccess) return e;
   return launch_quantize_pass(write_args(r, k_new, v_new, n, start_slot, pos0, ws), no_queries(), rope,
                               r.heads, r.head_dim, stream);
 }
 
 hipError_t launch_q_prep(const uint16_t* q, int32_t nq, int32_t heads, int32_t head_dim,
-                         int64_t q_pos0, const float* rope, float* q_partial, uint8_t* codes,
+                         int64_t q_pos0, const float* rope, void* sync, uint8_t* codes,
                          float* scale, hipStream_t stream) {
-  AbsmaxJobs jobs;
-  jobs.job[0] = absmax_job(q, nq, true, q_pos0, q_partial);
-  jobs.job[1] = jobs.job[2] = jobs.job[0];
-  hipError_t e = launch_absmax(jobs, 1, heads, head_dim, rope, stream);
-  if (e != hipSuccess) return e;
-  return launch_quantize_pass(no_write(), quant_q_args(q, nq, q_pos0, q_partial, codes, scale), rope,
+  return launch_quantize_pass(no_write(), quant_q_args(q, nq, q_pos0, sync, codes, scale), rope,
                               heads, head_dim, stream);
 }
 
 hipError_t launch_write_and_q_prep(const kv_ring_desc& r, const uint16_t* k_new,
                                    const uint16_t* v_new, int32_t n, int32_t start_slot,
                                    int64_t pos0, const uint16_t* q, int32_t nq, int64_t q_pos0,
-                                   const float* rope, float* ws, float* q_partial, uint8_t* codes,
-                                   float* scale, hipStream_t stream) {
-  const int ngroups = (n + kChunk - 1) / kChunk;
-  AbsmaxJobs jobs;
-  jobs.job[0] = absmax_job(k_new, n, true, pos0, ws);
-  jobs.job[1] = absmax_job(v_new, n, false, 0, ws + (int64_t)r.heads * ngroups);
-  jobs.job[2] = absmax_job(q, nq, true, q_pos0, q_partial);
-  hipError_t e = launch_absmax(jobs, 3, r.heads, r.head_dim, rope, stream);
-  if (e != hipSuccess) return e;
+                                   const float* rope, float* ws, uint8_t* codes, float* scale,
+                                   hipStream_t stream) {
   return launch_quantize_pass(write_args(r, k_new, v_new, n, start_slot, pos0, ws),
-                              quant_q_args(q, nq, q_pos0, q_partial, codes, scale), rope, r.heads,
+                              quant_q_args(q, nq, q_pos0, ws, codes, scale), rope, r.heads,
                               r.head_dim, stream);
 }
 
 // ---- the write without a caller workspace (kv_ring_write_static) ---------------------------------
 //
-// Its scratch (the per-(tensor, head, group) partial maxima of pass 1, read by pass 2) lives in a
-// file-scope device array, one copy per GPU, held until the process ends.  Host code must not pass
-// the array's name to a kernel (in host code it is a host-side stand-in); its device address is
-// looked up once per device, with that device current, and kept.  Every call writes every partial
-// it reads before reading it, so the array needs no clearing between calls; calls that overlap on
-// one GPU share it and race.
+// Its scratch (the per-head synchronisation records of head_sync) lives in a file-scope device
+// array, one copy per GPU, held until the process ends.  Host code must not pass the array's name
+// to a kernel (in host code it is a host-side stand-in); its device address is looked up once per
+// device, with that device current, and kept.  The array starts at zero when the code object is
+// loaded and every call leaves its records ready for the next, so it needs no clearing between
+// calls; calls that overlap on one GPU share it and race.
 
 namespace {
+static_assert(kSyncBytes <= kWriteStaticScratchFloats * 4, "the static scratch holds the records");
 __device__ __align__(256) float g_write_scratch[kWriteStaticScratchFloats];
 
 std::mutex g_scratch_mutex;

@@ -24,7 +24,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 int check_ring(const kv_ring_desc* r) {
   if (!r) return KV_RING_ERR_NULL;
   if (!r->k || !r->v || !r->k_scale || !r->v_scale) return KV_RING_ERR_NULL;
-  if (r->heads < 1 || r->heads > 65535 || r->slots < 1 || r->slots > (1 << 20)) return KV_RING_ERR_SHAPE;
+  if (r->heads < 1 || r->heads > kvring::kMaxHeads || r->slots < 1 || r->slots > (1 << 20)) return KV_RING_ERR_SHAPE;
   if (r->head_dim != 64 && r->head_dim != 128) return KV_RING_ERR_SHAPE;
   if (!aligned(r->k, 16) || !aligned(r->v, 16) || !aligned(r->k_scale, 4) || !aligned(r->v_scale, 4))
     return KV_RING_ERR_ALIGN;
@@ -40,12 +40,6 @@ int check_workspace(void* ws, size_t have, size_t need) {
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? KV_RING_OK : KV_RING_ERR_LAUNCH; }
-
-// Floats of the fused call's workspace taken by its write part (the attention part follows,
-// 16-byte aligned); m = max(new tokens, queries).
-int64_t write_attend_split(int32_t heads, int32_t m) {
-  return (kvring::write_workspace_floats(heads, m) + 3) / 4 * 4;
-}
 
 double rope_theta(int32_t i, int32_t head_dim, double base) {
   return std::pow(base, -(2.0 * i) / (double)head_dim);
@@ -124,7 +118,7 @@ int kv_ring_rope_table(float* host_out, int64_t n_pos, int32_t head_dim, double 
 }
 
 size_t kv_ring_workspace_bytes(int32_t op, int32_t heads, int32_t slots, int32_t head_dim, int32_t n) {
-  if (heads < 1 || slots < 1 || (head_dim != 64 && head_dim != 128)) return 0;
+  if (heads < 1 || heads > kvring::kMaxHeads || slots < 1 || (head_dim != 64 && head_dim != 128)) return 0;
   switch (op) {
     case KV_RING_OP_WRITE:
       if (n < 1) return 0;
@@ -135,10 +129,9 @@ size_t kv_ring_workspace_bytes(int32_t op, int32_t heads, int32_t slots, int32_t
       if (n < 0) return 0;
       if (n == 0) return 16;
       return sizeof(float) * (size_t)kvring::attention_workspace_floats(heads, slots, head_dim, n);
-    case KV_RING_OP_WRITE_ATTEND:   // n = max(new tokens, queries)
-      if (n < 1) return 0;
-      return sizeof(float) * (size_t)(write_attend_split(heads, n) +
-                                      kvring::attention_workspace_floats(heads, slots, head_dim, n));
+    case KV_RING_OP_WRITE_ATTEND:   // n = max(new tokens, queries); the write shares the
+      if (n < 1) return 0;          // attention's synchronisation records
+      return sizeof(float) * (size_t)kvring::attention_workspace_floats(heads, slots, head_dim, n);
     default:
       return 0;
   }
@@ -301,21 +294,31 @@ int kv_ring_write_attend(const kv_ring_desc* ring, const void* k_new, const void
                        kv_ring_workspace_bytes(KV_RING_OP_WRITE_ATTEND, ring->heads, ring->slots, ring->head_dim, m));
   if (st) return st;
   float* ws = static_cast<float*>(workspace);
-  float* ws_att = ws + write_attend_split(ring->heads, m);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const auto* kn = static_cast<const uint16_t*>(k_new);
   const auto* vn = static_cast<const uint16_t*>(v_new);
   if (nq == 0)
     return status_of(kvring::launch_write(*ring, kn, vn, n, start_slot, pos0, rope_table, ws, s));
   const kvring::AttnWorkspace aw =
-      kvring::attention_workspace(ws_att, ring->heads, ring->slots, ring->head_dim, nq);
+      kvring::attention_workspace(ws, ring->heads, ring->slots, ring->head_dim, nq);
   hipError_t e = kvring::launch_write_and_q_prep(*ring, kn, vn, n, start_slot, pos0,
                                                  static_cast<const uint16_t*>(q), nq, q_pos0,
-                                                 rope_table, ws, aw.q_partial, aw.q_codes, aw.q_scale, s);
+                                                 rope_table, ws, aw.q_codes, aw.q_scale, s);
   if (e != hipSuccess) return KV_RING_ERR_LAUNCH;
   return status_of(kvring::launch_attention(*ring, ring_head, filled, static_cast<const uint16_t*>(q), nq,
                                             q_pos0, rope_table, softmax_scale, static_cast<uint16_t*>(out),
-                                            lse, ws_att, true, s));
+                                            lse, ws, true, s));
+}
+
+int kv_ring_sync_status(const void* workspace, void* stream) {
+  if (!workspace) return KV_RING_ERR_NULL;
+  if (!aligned(workspace, 16)) return KV_RING_ERR_ALIGN;
+  int word = 0;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int* src = kvring::sync_error_word(const_cast<void*>(workspace));
+  if (hipMemcpyAsync(&word, src, sizeof(word), hipMemcpyDeviceToHost, s) != hipSuccess) return KV_RING_ERR_LAUNCH;
+  if (hipStreamSynchronize(s) != hipSuccess) return KV_RING_ERR_LAUNCH;
+  return word == 0 ? KV_RING_OK : KV_RING_ERR_SYNC;
 }
 
 int kv_ring_fp8_encode(const float* x, uint8_t* out, int64_t n, void* stream) {
@@ -362,6 +365,7 @@ const char* kv_ring_status_string(int status) {
     case KV_RING_ERR_WORKSPACE: return "workspace missing or too small";
     case KV_RING_ERR_LAUNCH: return "a kernel launch failed";
     case KV_RING_ERR_SCRATCH: return "the call needs more than the library's static scratch";
+    case KV_RING_ERR_SYNC: return "a synchronisation wait exceeded its bound";
     default: return "unknown status";
   }
 }

@@ -133,6 +133,99 @@ __device__ inline float list_max(const float* __restrict__ p, int n, float* red)
   return block_max_256(m, red);
 }
 
+// ---- per-head synchronisation inside one launch ------------------------------------------------
+//
+// An encoding needs the absmax over every element of its head before it can encode any of them.
+// The work-groups of one head meet at a record in device memory.  Each reads the record's
+// generation g (its parity p selects one of two sets of maxima), adds its partial maxima to set p
+// (float bits; every value is >= 0, so unsigned order is float order) and then counts itself in.
+// The last one in zeroes set 1 - p and the count for the next launch and bumps the generation;
+// the others wait for the generation to change.  Then every work-group reads set p.  A record is
+// therefore ready for the next launch as soon as this one's work-groups are all in, with no
+// clearing step (graph replays included); a zero-filled record is ready for the first.
+//
+// Ordering without fences: every operation on a record is an atomic at the device's coherence
+// point (agent scope).  Each step depends on the value the previous one returned (the maxima's
+// addresses on g, the count-in on the returned old maxima, the generation bump on the count), so
+// a work-group's maxima are in before its count, and every count before the bump that releases
+// the waiters.  (Acquire and release orderings would add cache write-backs and invalidations to
+// every poll, with no other data to publish.)
+//
+// The wait cannot deadlock: work-groups start in index order on each XCD and a head's are
+// consecutive, so the lowest unfinished head always has all of its work-groups started or able to
+// start; a head never has more work-groups than fit on one XCD at once.  The wait is bounded all
+// the same: past kSpinLimit polls a work-group sets the error word, stops waiting and carries on
+// (its output is then not to be trusted), so every launch ends.
+//
+// Every workspace starts with the records: slot 0 (writes, rotations) and slot 1 (queries) of
+// kMaxHeads records each, then the error word; an operation's own data follows kSyncBytes.  A
+// record's count, generation and four maxima each have a 128-byte line to themselves, so that
+// the atomics on one do not queue behind those on another.
+constexpr int kMaxHeads = 512;
+constexpr int kSyncLine = 128;
+constexpr int kSyncRecordBytes = 6 * kSyncLine;
+constexpr int64_t kSyncRecordsBytes = 2LL * kMaxHeads * kSyncRecordBytes;
+constexpr int64_t kSyncBytes = kSyncRecordsBytes + 256;
+constexpr int kSpinLimit = 1 << 20;
+
+__host__ __device__ inline char* sync_record(void* ws, int slot, int head) {
+  return reinterpret_cast<char*>(ws) + ((int64_t)slot * kMaxHeads + head) * kSyncRecordBytes;
+}
+__host__ __device__ inline int* sync_error_word(void* ws) {
+  return reinterpret_cast<int*>(reinterpret_cast<char*>(ws) + kSyncRecordsBytes);
+}
+
+// Called by every thread of a 256-thread work-group (uniformly): v0, v1 are this thread's partial
+// maxima (v1 only with two = true); on return they hold the head's maxima over all `expected`
+// work-groups.  `lds` is LDS scratch of >= 10 floats used by this call only.
+__device__ inline void head_sync(char* rec, int* err, int expected, bool two, float& v0, float& v1,
+                                 float* lds) {
+  v0 = wave_max(v0);
+  if (two) v1 = wave_max(v1);
+  if ((threadIdx.x & 63) == 0) {
+    lds[threadIdx.x >> 6] = v0;
+    lds[4 + (threadIdx.x >> 6)] = two ? v1 : 0.0f;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int* count = reinterpret_cast<int*>(rec);
+    unsigned* gen = reinterpret_cast<unsigned*>(rec + kSyncLine);
+    auto maxima = [rec](unsigned p, int k) __attribute__((always_inline)) {
+      return reinterpret_cast<unsigned*>(rec + (2 + 2 * p + k) * kSyncLine);
+    };
+    const float m0 = __builtin_fmaxf(__builtin_fmaxf(lds[0], lds[1]), __builtin_fmaxf(lds[2], lds[3]));
+    const float m1 = __builtin_fmaxf(__builtin_fmaxf(lds[4], lds[5]), __builtin_fmaxf(lds[6], lds[7]));
+    const unsigned g = __hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned p = g & 1u;
+    unsigned o = __hip_atomic_fetch_max(maxima(p, 0), __float_as_uint(m0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (two) o |= __hip_atomic_fetch_max(maxima(p, 1), __float_as_uint(m1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // o is never 0xFFFFFFFF (finite or +inf bit patterns), so the increment is 1; it depends on
+    // the returned old maxima, which orders it after them
+    const int one = (o != 0xFFFFFFFFu) ? 1 : 2;
+    const int before = __hip_atomic_fetch_add(count, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (before == expected - 1) {   // the last one in: ready the next launch, release the others
+      __hip_atomic_store(maxima(p ^ 1u, 0), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(maxima(p ^ 1u, 1), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(count, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(gen, g + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      int polls = 0;
+      while (__hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g) {
+        if (++polls > kSpinLimit) {
+          __hip_atomic_fetch_or(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    lds[8] = __uint_as_float(__hip_atomic_load(maxima(p, 0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    lds[9] = two ? __uint_as_float(__hip_atomic_load(maxima(p, 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) : 0.0f;
+  }
+  __syncthreads();
+  v0 = lds[8];
+  v1 = lds[9];
+}
+
 // Whether `slot` holds a token of the ring whose valid interval is the `filled` slots just
 // before `head` (oldest first).
 __device__ inline bool slot_valid(int slot, int head, int filled, int slots) {

@@ -15,8 +15,9 @@ int64_t write_workspace_floats(int32_t heads, int32_t n);
 int64_t rotate_workspace_floats(int32_t heads, int32_t slots);
 int64_t attention_workspace_floats(int32_t heads, int32_t slots, int32_t head_dim, int32_t nq);
 
-// kv_ring_write_static: the write's scratch in a static device array of this many floats per GPU.
-constexpr int64_t kWriteStaticScratchFloats = 262144;   // 1 MiB
+// kv_ring_write_static: the write's scratch (its synchronisation records) in a static device
+// array of this many floats per GPU.
+constexpr int64_t kWriteStaticScratchFloats = 196672;   // 768 KiB + 256 bytes
 constexpr int kMaxDevices = 64;
 // Device address of this device's copy of that array (looked up once per device).
 hipError_t write_static_scratch(float** out);
@@ -32,10 +33,12 @@ struct DeltaTable {  // cos/sin of delta * theta_i for i < head_dim/2, float32
 hipError_t launch_delta_rotate(const kv_ring_desc& r, int32_t ring_head, int32_t filled,
                                const DeltaTable& tab, float* ws, hipStream_t stream);
 
-// The attention's workspace: the queries' absmax partials, the split rows' partial results, and
-// the queries quantised for the QK product with their per-head scales.
+// Every workspace starts with the per-head synchronisation records (kSyncBytes, see head_sync):
+// the write, the rotation and the query preparation meet there, and each call leaves them ready
+// for the next.
+// The attention's workspace follows them with the split rows' partial results and the queries
+// quantised for the QK product with their per-head scales.
 struct AttnWorkspace {
-  float* q_partial;   // [heads][ceil(nq/32)]
   float* part_o;      // [rows][8][128][head_dim] halves (the split rows' normalised outputs)
   float* part_ml;     // [rows][8][128][2]
   uint8_t* q_codes;   // [heads * ceil(nq/128)][8][64][32]
@@ -45,23 +48,23 @@ AttnWorkspace attention_workspace(float* ws, int32_t heads, int32_t slots, int32
                                   int32_t nq);
 
 // With q_ready an earlier launch on the stream has written the quantised queries (and scales)
-// into the workspace; otherwise the attention prepares them first (two launches).
+// into the workspace; otherwise the attention prepares them first (one more launch).
 hipError_t launch_attention(const kv_ring_desc& r, int32_t ring_head, int32_t filled,
                             const uint16_t* q, int32_t nq, int64_t q_pos0, const float* rope,
                             float softmax_scale, uint16_t* out, float* lse, float* ws,
                             bool q_ready, hipStream_t stream);
 
-// Query preparation: absmax partials, then rotation and quantisation (two launches).
+// Query preparation: rotation, the per-head absmax and quantisation (one launch; sync is the
+// workspace, whose records of slot 1 it uses).
 hipError_t launch_q_prep(const uint16_t* q, int32_t nq, int32_t heads, int32_t head_dim,
-                         int64_t q_pos0, const float* rope, float* q_partial, uint8_t* codes,
+                         int64_t q_pos0, const float* rope, void* sync, uint8_t* codes,
                          float* scale, hipStream_t stream);
 
-// Write followed by the query preparation, sharing both launches: pass 1 for K, V and the
-// queries, then pass 2 (the write's quantisation and the queries').
+// Write followed by the query preparation, in one launch (records of slots 0 and 1 of ws).
 hipError_t launch_write_and_q_prep(const kv_ring_desc& r, const uint16_t* k_new,
                                    const uint16_t* v_new, int32_t n, int32_t start_slot,
                                    int64_t pos0, const uint16_t* q, int32_t nq, int64_t q_pos0,
-                                   const float* rope, float* ws, float* q_partial, uint8_t* codes,
+                                   const float* rope, float* ws, uint8_t* codes,
                                    float* scale, hipStream_t stream);
 
 void set_attention_events(void* before, void* after);

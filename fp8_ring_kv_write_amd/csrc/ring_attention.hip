@@ -929,19 +929,19 @@ void set_attention_events(void* before, void* after) {
 
 namespace {
 
-// Workspace layout (floats, each part 16-byte aligned): query absmax partials | split rows'
-// partial outputs | their (m, l) | quantised queries | query scales.  Sized for the largest plan
+// Workspace layout (floats, each part 16-byte aligned): the per-head synchronisation records
+// (kSyncBytes, head_sync; the query preparation takes slot 1) | split rows' partial outputs |
+// their (m, l) | quantised queries | query scales.  Sized for the largest plan
 // any (ring_head, filled) and any grid <= 256 can produce (<= 8 segments per row).
 struct WsLayout {
-  int64_t q_partial, part_o, part_ml, q_codes, q_scale, total;
+  int64_t part_o, part_ml, q_codes, q_scale, total;
 };
 
 WsLayout ws_layout(int32_t heads, int32_t slots, int32_t head_dim, int32_t nq) {
   auto up4 = [](int64_t x) { return (x + 3) / 4 * 4; };
   const Plan p = make_plan(heads, slots, nq, 0, slots, kMaxGrid);
   WsLayout l;
-  l.q_partial = 0;
-  l.part_o = l.q_partial + up4((int64_t)heads * ((nq + 31) / 32));
+  l.part_o = kSyncBytes / 4;
   l.part_ml = l.part_o + (int64_t)p.rows * 8 * kRowQ * head_dim / 2;   // half precision
   l.q_codes = l.part_ml + (int64_t)p.rows * 8 * kRowQ * 2;
   l.q_scale = l.q_codes + (int64_t)p.rows * (kRowQ * 128) / 4;   // 128 bytes per query
@@ -959,7 +959,6 @@ AttnWorkspace attention_workspace(float* ws, int32_t heads, int32_t slots, int32
                                   int32_t nq) {
   const WsLayout l = ws_layout(heads, slots, head_dim, nq);
   AttnWorkspace w;
-  w.q_partial = ws + l.q_partial;
   w.part_o = ws + l.part_o;
   w.part_ml = ws + l.part_ml;
   w.q_codes = reinterpret_cast<uint8_t*>(ws + l.q_codes);
@@ -1005,7 +1004,7 @@ hipError_t launch_attention(const kv_ring_desc& r, int32_t ring_head, int32_t fi
 
   hipError_t e = hipSuccess;
   if (!q_ready) {   // else an earlier launch on this stream wrote them
-    e = launch_q_prep(q, nq, r.heads, r.head_dim, q_pos0, rope, aw.q_partial, aw.q_codes, aw.q_scale, stream);
+    e = launch_q_prep(q, nq, r.heads, r.head_dim, q_pos0, rope, ws, aw.q_codes, aw.q_scale, stream);
     if (e != hipSuccess) return e;
   }
   // the profiling events are recorded only outside stream capture (a captured record would

@@ -33,7 +33,14 @@
  *   - the return value is KV_RING_OK (0) or a negative status; arguments are checked before
  *     anything is enqueued, and on an argument error nothing is launched and nothing written;
  *   - no call allocates memory: scratch space is the caller's `workspace`, sized by
- *     kv_ring_workspace_bytes; the workspace must not be shared by calls that may overlap.
+ *     kv_ring_workspace_bytes; the workspace must not be shared by calls that may overlap;
+ *   - every workspace starts with the per-head synchronisation records through which the
+ *     work-groups of one launch agree on a head's absmax (kv_ring_workspace_bytes counts them):
+ *     the caller zero-fills a workspace once, before its first use, and every call leaves the
+ *     records ready for the next (graph replays included), so one workspace serves every
+ *     operation and every ring shape in turn.  A record wait that exceeds its bound (no such
+ *     wait arises in correct use) sets a word of the workspace instead of hanging;
+ *     kv_ring_sync_status reads it.
  */
 #ifndef KVRING_H
 #define KVRING_H
@@ -54,7 +61,8 @@ enum {
   KV_RING_ERR_POSITION = -5,   /* a position falls outside the rotary table            */
   KV_RING_ERR_WORKSPACE = -6,  /* workspace NULL or smaller than required              */
   KV_RING_ERR_LAUNCH = -7,     /* a kernel launch failed (HIP error)                   */
-  KV_RING_ERR_SCRATCH = -8     /* kv_ring_write_static: heads * ceil(n/32) > 131072    */
+  KV_RING_ERR_SCRATCH = -8,    /* kv_ring_write_static: the call does not fit its scratch */
+  KV_RING_ERR_SYNC = -9        /* kv_ring_sync_status: a record wait exceeded its bound */
 };
 
 enum {
@@ -78,7 +86,7 @@ enum {
  *   k_scale  float32 [heads][slots], the dequantisation scale of the write that filled a slot;
  *   v_scale  float32 [heads][slots].
  * Byte b of unit n of tile t of head h is at byte ((h*T + t)*128*head_dim + 16n + b).
- * Limits: 1 <= heads <= 65535, 1 <= slots <= 1048576, head_dim in {64, 128}.
+ * Limits: 1 <= heads <= 512, 1 <= slots <= 1048576, head_dim in {64, 128}.
  * Bytes of the last tile for slots past `slots` are padding and never read as data.
  */
 typedef struct kv_ring_desc {
@@ -129,9 +137,16 @@ int kv_ring_rope_table_3d(float *host_out, const int32_t *positions, int64_t n, 
 
 /* Workspace bytes for `op` (KV_RING_OP_*) with n = new tokens (write), unused (delta
  * rotate), nq = queries (attention) or the larger of the two (write + attention).  Returns 0
- * for an unknown op or invalid shape. */
+ * for an unknown op or invalid shape.  Every workspace starts with the same synchronisation
+ * records (786,688 bytes), zero-filled by the caller before first use. */
 size_t kv_ring_workspace_bytes(int32_t op, int32_t heads, int32_t slots, int32_t head_dim,
                                int32_t n);
+
+/* Whether any record wait of the calls made with `workspace` (device memory) has exceeded its
+ * bound: copies one word of it to the host, waiting for `stream` first.  KV_RING_OK, or
+ * KV_RING_ERR_SYNC (the outputs of those calls are then not to be trusted), KV_RING_ERR_NULL,
+ * KV_RING_ERR_ALIGN (workspace not 16-byte aligned), KV_RING_ERR_LAUNCH (a HIP error). */
+int kv_ring_sync_status(const void *workspace, void *stream);
 
 /*
  * Write n new tokens into the ring (abstract: RoPE and FP8 quantisation applied once per
@@ -152,12 +167,14 @@ int kv_ring_write(const kv_ring_desc *ring, const void *k_new, const void *v_new
 /*
  * kv_ring_write without a workspace, for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid allocation): the same kernels,
- * arguments (less the workspace), results and errors as kv_ring_write; its scratch is a static
- * device array of the library, 1 MiB per GPU, held until the process ends.
- * Limit: heads * ceil(n / 32) <= 131072 (e.g. 24 heads and up to 174,752 tokens), else
- * KV_RING_ERR_SCRATCH and nothing is launched.  The call allocates nothing.  All calls on one GPU
- * share its scratch: calls that may overlap on one GPU (different streams, or different host
- * threads without ordering) race and must not be made.
+ * arguments (less the workspace), results and errors as kv_ring_write; its scratch (the
+ * per-head synchronisation records) is a static device array of the library, 768 KiB per GPU,
+ * zero when the library loads and left ready for the next call by every call, held until the
+ * process ends.
+ * Limit: the records of 512 heads, which every ring the library accepts fits (a call that did
+ * not fit would return KV_RING_ERR_SCRATCH with nothing launched).  The call allocates nothing.
+ * All calls on one GPU share its scratch: calls that may overlap on one GPU (different streams,
+ * or different host threads without ordering) race and must not be made.
  */
 int kv_ring_write_static(const kv_ring_desc *ring, const void *k_new, const void *v_new, int32_t n,
                          int32_t start_slot, int64_t pos0, const float *rope_table,

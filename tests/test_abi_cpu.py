@@ -84,11 +84,20 @@ def test_sizes(kv):
         assert kv.workspace_bytes(op, 24, 5788, 128, 757) > 0
         assert kv.workspace_bytes(op, 24, 5788, 128, 757) % 4 == 0
     assert kv.workspace_bytes(99, 24, 5788, 128, 757) == 0
+    # every workspace starts with the synchronisation records: 2 slots x 512 heads x 768 bytes
+    # plus the error word's 256 bytes
+    for op in (kv.OP_WRITE, kv.OP_DELTA_ROTATE, kv.OP_ATTENTION, kv.OP_WRITE_ATTEND):
+        assert kv.workspace_bytes(op, 3, 64, 64, 16) >= 786688
+        assert kv.workspace_bytes(op, 513, 64, 64, 16) == 0
+    assert kv.workspace_bytes(kv.OP_WRITE, 24, 5788, 128, 757) == 786688
+    assert kv.workspace_bytes(kv.OP_DELTA_ROTATE, 24, 5788, 128, 0) == 786688
+    assert kv.workspace_bytes(kv.OP_WRITE_ATTEND, 24, 5788, 128, 757) == \
+        kv.workspace_bytes(kv.OP_ATTENTION, 24, 5788, 128, 757)
 
 
 def test_status_strings(kv):
     assert kv.status_string(0) == "ok"
-    for s in range(-8, 0):
+    for s in range(-9, 0):
         assert kv.status_string(s) != "unknown status"
 
 
@@ -120,8 +129,15 @@ def test_argument_errors_are_reported_before_any_launch(kv):
     assert L.kv_ring_write_static(d(good), F + 2, F, 16, 0, 0, F, 128, None) == -2
     assert L.kv_ring_write_static(d(good), F, F, 65, 0, 0, F, 128, None) == -4
     assert L.kv_ring_write_static(d(good), F, F, 16, 0, 120, F, 128, None) == -5
-    big = _Desc(F, F, F, F, 8192, 1024, 64)   # 8192 heads x ceil(544 / 32) = 139,264 > 131,072
-    assert L.kv_ring_write_static(d(big), F, F, 544, 0, 0, F, 1024, None) == -8
+    # rings beyond 512 heads are refused by every call (the synchronisation records), so every
+    # ring a call accepts fits the static scratch
+    big = _Desc(F, F, F, F, 513, 1024, 64)
+    assert L.kv_ring_write_static(d(big), F, F, 544, 0, 0, F, 1024, None) == -3
+    assert L.kv_ring_write(d(big), F, F, 544, 0, 0, F, 1024, F, 1 << 30, None) == -3
+    assert kv.workspace_bytes(kv.OP_WRITE, 512, 1024, 64, 544) > 0
+    # the status word check: arguments first (nothing read)
+    assert L.kv_ring_sync_status(None, None) == -1
+    assert L.kv_ring_sync_status(F + 4, None) == -2
     # delta rotate
     wr = kv.workspace_bytes(kv.OP_DELTA_ROTATE, 2, 64, 64, 0)
     assert L.kv_ring_delta_rotate(d(good), 64, 10, 5, 10000.0, F, wr, None) == -4
@@ -174,7 +190,7 @@ def test_argument_errors_are_reported_before_any_launch(kv):
     assert L.kv_ring_delta_rotate_3d(d(good), 0, 10, dl.ctypes.data, None, 10000.0, F, wr - 4, None) == -6
     # write + attention in one call: the checks of both
     wf = kv.workspace_bytes(kv.OP_WRITE_ATTEND, 2, 64, 64, 16)
-    assert wf >= ws + wa - 16
+    assert wf >= wa   # the write shares the attention's synchronisation records
     def wa_call(*, desc=good, k=F, n=16, start=0, pos0=0, head=16, filled=16, q=F, nq=16, qpos=0,
                 ntab=128, scale=0.125, out=F, lse=F, wsp=F, wsb=wf):
         return L.kv_ring_write_attend(d(desc), k, F, n, start, pos0, head, filled, q, nq, qpos, F, ntab,

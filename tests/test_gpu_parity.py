@@ -438,8 +438,8 @@ def test_layer_calls_replay_from_a_captured_graph(kv, torch):
     k_new = [to_dev_bf16(normal_bf16(tensor_seed("graph", 10 + i, 1), (n, h, d))) for i in range(2)]
     v_new = [to_dev_bf16(normal_bf16(tensor_seed("graph", 10 + i, 2), (n, h, d))) for i in range(2)]
     q = [to_dev_bf16(normal_bf16(tensor_seed("graph", 10 + i, 0), (n, h, d))) for i in range(2)]
-    ws_w = torch.empty(kv.workspace_bytes(kv.OP_WRITE, h, s, d, n), dtype=torch.uint8, device="cuda")
-    ws_a = torch.empty(kv.workspace_bytes(kv.OP_ATTENTION, h, s, d, n), dtype=torch.uint8, device="cuda")
+    ws_w = torch.zeros(kv.workspace_bytes(kv.OP_WRITE, h, s, d, n), dtype=torch.uint8, device="cuda")
+    ws_a = torch.zeros(kv.workspace_bytes(kv.OP_ATTENTION, h, s, d, n), dtype=torch.uint8, device="cuda")
     outs = [torch.empty_like(q[0]) for _ in range(2)]
     lses = [torch.empty((h, n), dtype=torch.float32, device="cuda") for _ in range(2)]
     start, pos0 = (head - n) % s, 5 * n
