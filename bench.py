@@ -65,8 +65,8 @@ ATT_KERNEL = "attn_pp<128>"
 # (FETCH_SIZE, WRITE_SIZE) over this workload, each divided by the factor the same counter
 # reads for a torch copy of --calibrate-copy bytes.  Valid only for the kernel sources whose
 # hash is recorded; reported as null otherwise.
-ATT_TRAFFIC = {"sources": "ebf5bb7581dc77ff", "bytes": 99_040_000,
-               "read_bytes": 76_910_000, "write_bytes": 22_130_000}
+ATT_TRAFFIC = {"sources": "fe44ef93316fe390", "bytes": 97_470_000,
+               "read_bytes": 76_380_000, "write_bytes": 21_090_000}
 WRITE_BYTES = 2 * N * H * D * 2 + 2 * N * H * D + 2 * N * H * 4
 ROTATE_BYTES = 2 * (H * S * D + H * S * 4)
 

@@ -94,6 +94,8 @@ __global__ __launch_bounds__(kThreads) void rotate_requantize(
     uint8_t* __restrict__ kc, float* __restrict__ k_scale, RotGeom g, DeltaTable tab, void* sync) {
   __shared__ float sl[10];
   const int t = blockIdx.x, h = blockIdx.y;
+  char* rec = sync_record(sync, 0, h);
+  const unsigned gen = head_sync_generation(rec);
   uint8_t* tile = kc + ((int64_t)h * g.tiles + t) * kTile * D;
   float* srow = k_scale + (int64_t)h * g.slots;
   Units<D> x;
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(kThreads) void rotate_requantize(
   }
   // the head's new absmax; every thread's reads of the old slot scales (above) precede its
   // barrier, and so the writes below
-  head_sync(sync_record(sync, 0, h), sync_error_word(sync), int(g.tiles), false, m, unused, sl);
+  head_sync<kThreads>(rec, gen, sync_error_word(sync), int(g.tiles), false, m, unused, sl);
   float scale, inv;
   scale_from_absmax(m, scale, inv);
 #pragma unroll

@@ -95,6 +95,8 @@ __device__ inline void write_chunk(const WriteArgs& wa, const float* __restrict_
   float* __restrict__ k_scale = wa.k_scale;
   float* __restrict__ v_scale = wa.v_scale;
   const int chunk = blk < g.n_chunks_a ? g.chunk_a0 + blk : blk - g.n_chunks_a;
+  char* rec = sync_record(wa.sync, 0, h);
+  const unsigned gen = head_sync_generation(rec);
 
   const int t = threadIdx.x >> 3, cg = threadIdx.x & 7;
   const int slot = chunk * kChunk + t;
@@ -130,7 +132,7 @@ __device__ inline void write_chunk(const WriteArgs& wa, const float* __restrict_
     mk = absmax<CPT>(xk);
     mv = absmax<CPT>(xv);
   }
-  head_sync(sync_record(wa.sync, 0, h), sync_error_word(wa.sync), wa.blocks, true, mk, mv, sl);
+  head_sync<kThreads>(rec, gen, sync_error_word(wa.sync), wa.blocks, true, mk, mv, sl);
   float sk, ik, sv, iv;
   scale_from_absmax(mk, sk, ik);
   scale_from_absmax(mv, sv, iv);
@@ -200,6 +202,8 @@ __device__ inline void quantize_q_half(const QuantQArgs& qa_, const float* __res
   const int lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
   const int i = qt * 128 + w * 16 + li;
   const bool live = i < qa_.nq && (D == 128 || g < 2);
+  char* rec = sync_record(qa_.sync, 1, h);
+  const unsigned gen = head_sync_generation(rec);
   uint4 raw[4];
   float4 tab[8];
   if (live) {
@@ -228,7 +232,7 @@ __device__ inline void quantize_q_half(const QuantQArgs& qa_, const float* __res
     }
     m = absmax<32>(y);
   }
-  head_sync(sync_record(qa_.sync, 1, h), sync_error_word(qa_.sync), qa_.blocks, false, m, unused, sl);
+  head_sync<kThreads>(rec, gen, sync_error_word(qa_.sync), qa_.blocks, false, m, unused, sl);
   float scale, inv;
   scale_from_absmax(m, scale, inv);
   if (blk == 0 && threadIdx.x == 0) qa_.scale[h] = scale;

@@ -175,16 +175,27 @@ __host__ __device__ inline int* sync_error_word(void* ws) {
   return reinterpret_cast<int*>(reinterpret_cast<char*>(ws) + kSyncRecordsBytes);
 }
 
-// Called by every thread of a 256-thread work-group (uniformly): v0, v1 are this thread's partial
-// maxima (v1 only with two = true); on return they hold the head's maxima over all `expected`
-// work-groups.  `lds` is LDS scratch of >= 10 floats used by this call only.
-__device__ inline void head_sync(char* rec, int* err, int expected, bool two, float& v0, float& v1,
-                                 float* lds) {
+// The record's generation, read by thread 0 of a work-group as early as possible (at its start:
+// the read then overlaps the work-group's loads) and passed to head_sync.  Other threads get 0.
+__device__ inline unsigned head_sync_generation(const char* rec) {
+  if (threadIdx.x != 0) return 0u;
+  return __hip_atomic_load(reinterpret_cast<const unsigned*>(rec + kSyncLine), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Called by every thread of an NT-thread work-group (uniformly), with g from head_sync_generation:
+// v0, v1 are this thread's partial maxima (v1 only with two = true); on return they hold the
+// head's maxima over all `expected` work-groups.  `lds` is LDS scratch of >= 2 * NT/64 + 2 floats
+// used by this call only.
+template <int NT>
+__device__ inline void head_sync(char* rec, unsigned g, int* err, int expected, bool two, float& v0,
+                                 float& v1, float* lds) {
+  constexpr int NW = NT / 64;
   v0 = wave_max(v0);
   if (two) v1 = wave_max(v1);
   if ((threadIdx.x & 63) == 0) {
     lds[threadIdx.x >> 6] = v0;
-    lds[4 + (threadIdx.x >> 6)] = two ? v1 : 0.0f;
+    lds[NW + (threadIdx.x >> 6)] = two ? v1 : 0.0f;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -193,9 +204,12 @@ __device__ inline void head_sync(char* rec, int* err, int expected, bool two, fl
     auto maxima = [rec](unsigned p, int k) __attribute__((always_inline)) {
       return reinterpret_cast<unsigned*>(rec + (2 + 2 * p + k) * kSyncLine);
     };
-    const float m0 = __builtin_fmaxf(__builtin_fmaxf(lds[0], lds[1]), __builtin_fmaxf(lds[2], lds[3]));
-    const float m1 = __builtin_fmaxf(__builtin_fmaxf(lds[4], lds[5]), __builtin_fmaxf(lds[6], lds[7]));
-    const unsigned g = __hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    float m0 = lds[0], m1 = lds[NW];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      m0 = __builtin_fmaxf(m0, lds[w]);
+      m1 = __builtin_fmaxf(m1, lds[NW + w]);
+    }
     const unsigned p = g & 1u;
     unsigned o = __hip_atomic_fetch_max(maxima(p, 0), __float_as_uint(m0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (two) o |= __hip_atomic_fetch_max(maxima(p, 1), __float_as_uint(m1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -218,12 +232,12 @@ __device__ inline void head_sync(char* rec, int* err, int expected, bool two, fl
         __builtin_amdgcn_s_sleep(1);
       }
     }
-    lds[8] = __uint_as_float(__hip_atomic_load(maxima(p, 0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    lds[9] = two ? __uint_as_float(__hip_atomic_load(maxima(p, 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) : 0.0f;
+    lds[2 * NW] = __uint_as_float(__hip_atomic_load(maxima(p, 0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    lds[2 * NW + 1] = two ? __uint_as_float(__hip_atomic_load(maxima(p, 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) : 0.0f;
   }
   __syncthreads();
-  v0 = lds[8];
-  v1 = lds[9];
+  v0 = lds[2 * NW];
+  v1 = lds[2 * NW + 1];
 }
 
 // Whether `slot` holds a token of the ring whose valid interval is the `filled` slots just
