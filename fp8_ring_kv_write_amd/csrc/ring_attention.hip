@@ -4,23 +4,22 @@
 // FP8 attention with per-head scales).
 //
 // Launches per call:
-//   1. rope_absmax_partials (shared with the write): per-(head, 32-query group) max |RoPE(q)|;
-//      then quantize_pass (shared with the write): the queries rotated and encoded with their
-//      head's scale, stored in the order the QK product takes them.  kv_ring_write_attend runs
-//      both inside the write's own two launches;
+//   1. quantize_pass (shared with the write): the queries rotated, their head's absmax agreed
+//      on through the head's record in the workspace, and encoded with the head's scale in the
+//      order the QK product takes them.  kv_ring_write_attend does this inside the write's own
+//      launch;
 //   2. attn_pp: a persistent grid of one 8-wavefront work-group per compute unit.  The work is
 //      the set of units (row, tile), a row being 256 queries of one head and a tile 128 ring
 //      slots; each work-group takes a contiguous range of units of equal weight (a tile weighs
 //      one, the start of a row's segment kSegCost more), so a row may be split between
-//      work-groups.  A row held by one work-group is finished in place; the segments of a split
-//      row store their own output, normalised by their own sum, in half precision (a weighted
-//      mean of dequantised V rows: within 2^-11 relative), with their (max, sum).  When rows
-//      are short (a ring still filling up) and fit the grid, each work-group takes one whole
-//      row instead, and no merge pass is needed.  Consecutive work-groups of one XCD get
-//      consecutive units, so the rows of one head share that XCD's L2;
-//   3. attn_combine: log-sum-exp merge of the split rows (skipped when no row is split).  Doing
-//      the merge in a kernel of its own avoids device-scope fences inside attn_pp, which on
-//      this multi-XCD part write back and invalidate L2.
+//      work-groups.  A row held by one work-group is finished in place.  The segments of a
+//      split row store their own output, normalised by their own sum, in half precision (a
+//      weighted mean of dequantised V rows: within 2^-11 relative), with their (max, sum), and
+//      the last of them to finish merges the row (log-sum-exp) and writes its output (see
+//      store_partial and merge_items).  When rows are short (a ring still filling up) and fit
+//      the grid, each work-group takes one whole row instead, and nothing is merged.
+//      Consecutive work-groups of one XCD get consecutive units, so the rows of one head share
+//      that XCD's L2.
 //
 // Each wavefront owns 32 queries, as two groups of 16 that share every operand read from LDS:
 //   S^T = K Q^T           per group 8 MFMA 16x16x128 FP8 (fp32 accumulate)
@@ -65,12 +64,12 @@ constexpr int kRowQ = 2 * kGroupQ * kWaves;   // 256 queries per row, 32 per wav
 constexpr int kBufs = 3;                // LDS buffers of K tiles
 constexpr int kMaxGrid = 256;
 constexpr int kSegCost = 2;             // weight of a segment start in tiles (UnitSplit)
-constexpr int kCombineCost = 6;         // weight of the merge pass of split rows, in tiles
+constexpr int kMergeCost = 6;           // weight of splitting rows (partial stores, the merge), in tiles
+constexpr int kMaxSeg = 8;              // segments of a row, at most (make_plan)
 constexpr float kTau = 4.0f;            // lazy rescale threshold, log2 units
 constexpr float kPmax = 4096.0f;        // bound on a lane's probability sum in the fast path
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-typedef _Float16 v4h __attribute__((ext_vector_type(4)));   // split rows' partial outputs
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));   // fp16 operand of the PV product
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
@@ -84,8 +83,10 @@ struct AttnArgs {
   const float* q_scale;    // [heads]
   uint16_t* out;
   float* lse;
-  _Float16* part_o;        // [rows][max_seg][kRowQ][D]: segment output normalised by its l
-  float* part_ml;          // [rows][max_seg][kRowQ][2]
+  _Float16* part_o;        // per (row, segment): the segment's output normalised by its l
+  float* part_ml;          // per (row, segment): [kRowQ][2] (max, sum) of each query
+  int* merge_cnt;          // per split row (by its first work-group): arrival and ready counts
+  int* err;                // the workspace's error word
   int64_t tiles;           // ring tiles per head
   int64_t units;           // rows * tv
   int64_t cost;            // rows * (tv + seg_cost): the partition's total weight
@@ -146,12 +147,6 @@ __device__ inline v4f mfma_f16(const v8h& a, const v8h& b, const v4f& c) {
 // Two floats -> two fp16 values (round to nearest even), the first in the low half.
 __device__ inline uint32_t pack_f16(float a, float b) {
   return __builtin_bit_cast(uint32_t, v2h{(_Float16)a, (_Float16)b});
-}
-
-__device__ inline uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
 }
 
 // max over lanes l, l^16, l^32, l^48 (the four lane groups holding one query's scores)
@@ -557,6 +552,184 @@ __device__ __forceinline__ void softmax_group(const Smem<D>& sm, int bk, int g, 
   gr.l += lsum;
 }
 
+// ---- Split rows: partial results and their merge inside attn_pp.
+// Every segment of a split row stores its output (normalised by its own sum, half precision)
+// and each query's (max, sum) with accesses of device scope (cache policy sc1: coherent between
+// the XCDs without writing back or invalidating any L2), waits until those stores are complete,
+// and only then counts itself in the row's arrival count.  Once its range is done, each
+// work-group of the row waits until the count shows every segment stored, merges its share of
+// the row with loads of the same scope, writes that share's output, and counts itself in the
+// row's departure count; the last to depart sets both counts back to zero for the next launch.
+// A share is a set of items, an item being half the channels of a 16-query group (32 per row):
+// segment s takes the items s, s + nseg, ..., spread over all eight wavefronts.  A segment that
+// opens its work-group's range and is followed by more rows counts its arrival at the next row's
+// first barrier (its stores are complete by then) and merges its share after the range, in the
+// same passes as the share of the work-group's closing row.
+// Arrivals never wait, so a work-group only waits for work-groups that can finish: the grid never
+// exceeds the compute units, so on a device running nothing else all of it is resident, and with
+// other work present the wait still ends as long as every XCD can hold the work-groups of one row
+// at once (they are consecutive on one XCD, and an XCD starts its work-groups in order).  The
+// wait is bounded: past kSpinLimit polls a work-group sets the error word and carries on (the
+// row's output is then not to be trusted).  The two counts of a row sit on their own 128-byte
+// lines, picked by the row's first work-group (in one launch at most one split row starts in each
+// range).
+constexpr int kPolicySc1 = 16;            // cache policy operand of the buffer builtins: sc1
+constexpr int kRsrcWord3 = 0x00020000;    // buffer resource: 32-bit data format, untyped access
+constexpr int kCountInts = kSyncLine / 4;
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
+}
+__device__ inline int* merge_arrivals(const AttnArgs& a, int vf) { return a.merge_cnt + vf * 2 * kCountInts; }
+__device__ inline int* merge_departures(const AttnArgs& a, int vf) { return merge_arrivals(a, vf) + kCountInts; }
+
+// Thread 0: wait until all nseg segments of the row have arrived (bounded).
+__device__ inline void merge_wait(const AttnArgs& a, int vf, int nseg) {
+  const int* arr = merge_arrivals(a, vf);
+  int polls = 0;
+  while (__hip_atomic_load(arr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nseg) {
+    if (++polls > kSpinLimit) {
+      __hip_atomic_fetch_or(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// The partial result of query group q of this wavefront into block blk (= row * max_seg +
+// segment): output as [wavefront, group][piece j][lane] 16-byte pieces (one piece: channel
+// blocks 2j and 2j + 1 of the lane, 8 halves; each store instruction writes 1 KB contiguous),
+// and (max, sum) per query.
+template <int D>
+__device__ inline void store_partial(const AttnArgs& a, int64_t blk, const Group<D>& gr, float lt,
+                                     int w, int q, int lane) {
+  constexpr int NJ = D / 32;
+  const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(a.part_o + blk * (kRowQ * D), kRowQ * D * 2);
+  const float il = lt > 0.0f ? 1.0f / lt : 0.0f;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const v4f x = gr.acc[2 * j], y = gr.acc[2 * j + 1];
+    const v8h h = {(_Float16)(x[0] * il), (_Float16)(x[1] * il), (_Float16)(x[2] * il), (_Float16)(x[3] * il),
+                   (_Float16)(y[0] * il), (_Float16)(y[1] * il), (_Float16)(y[2] * il), (_Float16)(y[3] * il)};
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, h), ro,
+                                           (((w * 2 + q) * NJ + j) * 64 + lane) * 16, 0, kPolicySc1);
+  }
+  if ((lane >> 4) == 0) {
+    const __amdgpu_buffer_rsrc_t rm = buffer_rsrc(a.part_ml + blk * (kRowQ * 2), kRowQ * 8);
+    const v2u ml = {__float_as_uint(gr.m), __float_as_uint(lt)};
+    __builtin_amdgcn_raw_buffer_store_b64(ml, rm, (32 * w + 16 * q + (lane & 15)) * 8, 0, kPolicySc1);
+  }
+}
+
+// Merge of stored segments by one wavefront, for up to two items at once.  An item is half of a
+// query group of a split row: queries 16 gi .. 16 gi + 15 (stored by wavefront gi / 2 as its group
+// gi % 2) and channel blocks 4 hf .. 4 hf + 3 (half hf of the lane's pieces); a row has 32 items.
+// Each segment weighs 2^(m_s - m) times its sum, m being the largest max (the log-sum-exp merge).
+// Every load of both items is issued before any arithmetic (one memory round trip); the result
+// goes to the output like a row held by one work-group.
+struct MergeItem {
+  int row, nseg, gi, hf;
+  bool on;
+};
+
+template <int D>
+__device__ inline void write_out_blocks(const AttnArgs& a, const v4f* acc, int db0, int ndb, float m,
+                                        float l, int head, int qt, int ql, int g, bool with_lse);
+
+template <int D>
+__device__ inline void merge_items(const AttnArgs& a, const MergeItem (&it)[2], int lane) {
+  constexpr int NJ = D / 32;   // 16-byte pieces of a lane's group (channel blocks 2j, 2j + 1)
+  constexpr int NH = NJ / 2;   // pieces of one half
+  float ms[2][kMaxSeg], ls[2][kMaxSeg];
+  v4u o[2][kMaxSeg][NH];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    if (!it[k].on) continue;
+    const int64_t blk0 = (int64_t)it[k].row * a.max_seg;
+    // one resource per array over the row's blocks; the segment's block offset goes in soffset
+    const __amdgpu_buffer_rsrc_t rm = buffer_rsrc(a.part_ml + blk0 * (kRowQ * 2), a.max_seg * kRowQ * 8);
+    const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(a.part_o + blk0 * (kRowQ * D), a.max_seg * kRowQ * D * 2);
+    const int ql = 16 * it[k].gi + (lane & 15);
+#pragma unroll
+    for (int s = 0; s < kMaxSeg; ++s) {
+      ms[k][s] = -INFINITY;
+      ls[k][s] = 0.0f;
+      if (s < it[k].nseg) {
+        const v2u x = __builtin_amdgcn_raw_buffer_load_b64(rm, ql * 8, s * kRowQ * 8, kPolicySc1);
+        ms[k][s] = __uint_as_float(x[0]);
+        ls[k][s] = __uint_as_float(x[1]);
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+          o[k][s][h] = __builtin_amdgcn_raw_buffer_load_b128(
+              ro, ((it[k].gi * NJ + it[k].hf * NH + h) * 64 + lane) * 16, s * kRowQ * D * 2, kPolicySc1);
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    if (!it[k].on) continue;
+    float mt = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kMaxSeg; ++s) mt = __builtin_fmaxf(mt, ms[k][s]);
+    const float mr = mt == -INFINITY ? 0.0f : mt;   // no finite max: every weight below is 0
+    float lsum = 0.0f;
+    v4f acc[2 * NH];
+#pragma unroll
+    for (int b = 0; b < 2 * NH; ++b) acc[b] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < kMaxSeg; ++s) {
+      if (s >= it[k].nseg) continue;
+      const float ws = __builtin_amdgcn_exp2f(ms[k][s] - mr) * ls[k][s];
+      lsum += ws;
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const v8h x = __builtin_bit_cast(v8h, o[k][s][h]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          acc[2 * h][c] = __builtin_fmaf(ws, float(x[c]), acc[2 * h][c]);
+          acc[2 * h + 1][c] = __builtin_fmaf(ws, float(x[4 + c]), acc[2 * h + 1][c]);
+        }
+      }
+    }
+    write_out_blocks<D>(a, acc, 2 * NH * it[k].hf, 2 * NH, mt, lsum, it[k].row / a.qtiles,
+                        it[k].row % a.qtiles, 16 * it[k].gi + (lane & 15), lane >> 4, it[k].hf == 0);
+  }
+}
+
+// Every vector-memory operation of this thread complete (stores included); the asm's memory
+// clobber keeps the compiler from moving memory accesses across it.
+__device__ inline void wait_memory() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Final output of one query (ql of the row): channel blocks db0 .. db0 + ndb - 1 of this lane
+// (channels 16 db + 4g .. +3) as bf16 O / l, and, with with_lse, the log-sum-exp (natural log)
+// of its scores, m being in log2 units.
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+template <int D>
+__device__ inline void write_out_blocks(const AttnArgs& a, const v4f* acc, int db0, int ndb, float m,
+                                        float l, int head, int qt, int ql, int g, bool with_lse) {
+  const int i = qt * kRowQ + ql;
+  if (i >= a.nq) return;
+  const float il = l > 0.0f ? 1.0f / l : 0.0f;
+  uint16_t* dst = a.out + ((int64_t)i * a.heads + head) * D + 4 * g;
+  for (int b = 0; b < ndb; ++b) {
+    const v4f o = acc[b];
+    const v2bf lo = __builtin_convertvector(v2f{o[0] * il, o[1] * il}, v2bf);   // round to nearest even
+    const v2bf hi = __builtin_convertvector(v2f{o[2] * il, o[3] * il}, v2bf);
+    *reinterpret_cast<uint2*>(dst + 16 * (db0 + b)) =
+        make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+  }
+  if (with_lse && g == 0) a.lse[(int64_t)head * a.nq + i] = l > 0.0f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+}
+
+template <int D>
+__device__ inline void write_out(const AttnArgs& a, const v4f (&acc)[D / 16], float m, float l,
+                                 int head, int qt, int ql, int g) {
+  write_out_blocks<D>(a, acc, 0, D / 16, m, l, head, qt, ql, g, true);
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_pp(AttnArgs a) {
   constexpr int NDB = D / 16;
@@ -570,6 +743,10 @@ __global__ __launch_bounds__(kThreads) void attn_pp(AttnArgs a) {
   __shared__ __align__(16) float s_iv[kBufs][kTile];
   __shared__ __align__(16) int s_uni[kBufs][4];
   __shared__ __align__(16) float s_qs[4];
+  // split rows this work-group merges a share of after its range, as (row (-1: none), first
+  // work-group, segment count, its segment index): [0] the row of its closing segment, [1] that
+  // of its opening segment
+  __shared__ int s_merge[2][4];
   Smem<D> sm{s_k, s_v8, s_v16, s_ks, s_vs, s_ck, s_nb, s_iv, s_uni, s_qs};
 
   const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);   // wavefront (uniform)
@@ -591,6 +768,11 @@ __global__ __launch_bounds__(kThreads) void attn_pp(AttnArgs a) {
   // (and is then the row's first segment).  The 64-bit divisions happen once per work-group.
   int row = int(ub / a.tv), k0 = int(ub % a.tv);
   int seg = k0 > 0 ? v - split.owner((int64_t)row * a.tv) : 0;   // index of this segment in its row
+  // A split row's segment that opens this range and is followed by more rows is described in
+  // s_merge[1] (LDS rather than registers, which the tile loop needs); it counts its arrival at
+  // the next row's first barrier.
+  if (tid == 0) s_merge[0][0] = s_merge[1][0] = -1;
+  bool open_arrive = false;
   while (ub < ue) {
     const int k1 = int(min<int64_t>(a.tv, k0 + (ue - ub)));
     const int nt = k1 - k0;
@@ -621,6 +803,11 @@ __global__ __launch_bounds__(kThreads) void attn_pp(AttnArgs a) {
     }
     wait_vm(0);
     lds_sync();
+    if (open_arrive) {   // every thread's partial stores of the opening segment are complete
+      if (tid == 0)
+        __hip_atomic_fetch_add(merge_arrivals(a, s_merge[1][1]), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      open_arrive = false;
+    }
     const float c0 = a.score_scale * sm.qs[0];
     {
       const TileValid tvd = tile_valid(phys(k0), a.ring_head, a.filled, a.slots);
@@ -741,41 +928,35 @@ __global__ __launch_bounds__(kThreads) void attn_pp(AttnArgs a) {
     }
     if (grp == 0) lds_sync();   // the second group's M_nt
 
-    // ---- segment result: direct output, or partial for attn_combine
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      Group<D>& gr = q == 0 ? ga : gb;
-      float lt = gr.l;
-      lt += __shfl_xor(lt, 16, 64);
-      lt += __shfl_xor(lt, 32, 64);
-      const int ql = 32 * w + 16 * q + li;   // query within the row
-      if (row_split) {
-        const int64_t slot0 = ((int64_t)row * a.max_seg + seg) * kRowQ;
-        const float il = lt > 0.0f ? 1.0f / lt : 0.0f;
-        _Float16* po = a.part_o + (slot0 + ql) * D + 4 * g;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const v4f o = gr.acc[db];
-          const v4h oh = {(_Float16)(o[0] * il), (_Float16)(o[1] * il), (_Float16)(o[2] * il),
-                          (_Float16)(o[3] * il)};
-          *reinterpret_cast<v4h*>(po + 16 * db) = oh;
-        }
-        if (g == 0) *reinterpret_cast<float2*>(a.part_ml + (slot0 + ql) * 2) = make_float2(gr.m, lt);
-      } else {
-        const int i = qt * kRowQ + ql;
-        if (i < a.nq) {
-          const float il = lt > 0.0f ? 1.0f / lt : 0.0f;
-          uint16_t* dst = a.out + ((int64_t)i * a.heads + head) * D + 4 * g;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const v4f o = gr.acc[db];
-            const uint32_t lo16 = uint32_t(f32_to_bf16(o[0] * il)) | (uint32_t(f32_to_bf16(o[1] * il)) << 16);
-            const uint32_t hi16 = uint32_t(f32_to_bf16(o[2] * il)) | (uint32_t(f32_to_bf16(o[3] * il)) << 16);
-            *reinterpret_cast<uint2*>(dst + 16 * db) = make_uint2(lo16, hi16);
-          }
-          if (g == 0)
-            a.lse[(int64_t)head * a.nq + i] = lt > 0.0f ? (gr.m + __log2f(lt)) * kLn2 : -INFINITY;
-        }
+    // ---- segment result: the row's output, or this segment's part of a split row
+    float lt0 = ga.l, lt1 = gb.l;
+    lt0 += __shfl_xor(lt0, 16, 64);
+    lt0 += __shfl_xor(lt0, 32, 64);
+    lt1 += __shfl_xor(lt1, 16, 64);
+    lt1 += __shfl_xor(lt1, 32, 64);
+    if (!row_split) {
+      write_out<D>(a, ga.acc, ga.m, lt0, head, qt, 32 * w + li, g);
+      write_out<D>(a, gb.acc, gb.m, lt1, head, qt, 32 * w + 16 + li, g);
+    } else {
+      const int vf = v - seg;   // the row's first work-group
+      const int nseg = split.owner((int64_t)row * a.tv + a.tv - 1) - vf + 1;
+      const int64_t blk = (int64_t)row * a.max_seg + seg;
+      store_partial<D>(a, blk, ga, lt0, w, 0, lane);
+      store_partial<D>(a, blk, gb, lt1, w, 1, lane);
+      const int k = ub + nt < ue ? 1 : 0;   // 1: more rows follow in this range
+      if (tid == 0) {
+        s_merge[k][0] = row;
+        s_merge[k][1] = vf;
+        s_merge[k][2] = nseg;
+        s_merge[k][3] = seg;
+      }
+      if (k == 1) {
+        open_arrive = true;   // counted at the next row's start
+      } else {                // the range ends here
+        wait_memory();
+        lds_sync();           // every thread's stores are complete
+        if (tid == 0)
+          __hip_atomic_fetch_add(merge_arrivals(a, vf), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     ub += nt;
@@ -783,66 +964,53 @@ __global__ __launch_bounds__(kThreads) void attn_pp(AttnArgs a) {
     k0 = 0;
     seg = 0;
   }
-}
-
-// Merge of split rows: thread = (query of a row, 8 channels); rows held by one work-group were
-// written directly by attn_pp and are skipped.  A row has at most 8 segments (make_plan); every
-// load of a thread is issued before any arithmetic (one memory round trip), and the segments are
-// merged in order.
-typedef _Float16 v8hc __attribute__((ext_vector_type(8)));
-
-template <int D>
-__global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
-  constexpr int kMaxSeg = 8;
-  const int row = blockIdx.y;
-  const UnitSplit split{a.tv, a.seg_cost, a.cost, a.grid};
-  const int first = split.owner((int64_t)row * a.tv);
-  const int nseg = split.owner((int64_t)row * a.tv + a.tv - 1) - first + 1;
-  if (nseg <= 1) return;
-  const int item = blockIdx.x * 256 + threadIdx.x;
-  const int ql = item / (D / 8), c8 = item % (D / 8);
-  if (ql >= kRowQ) return;
-  const int head = row / a.qtiles, qt = row % a.qtiles;
-  const int i = qt * kRowQ + ql;
-  if (i >= a.nq) return;
-  const int64_t base = (int64_t)row * a.max_seg * kRowQ + ql;
-  float2 ml[kMaxSeg];
-  v8hc oz[kMaxSeg];
+  // this work-group's share of the merge of its split rows, once all their segments are stored:
+  // segment s of a row of nseg takes the row's items s, s + nseg, ..., wavefront w the items
+  // s + (w + 8r) nseg for r = 0, 1, ...; a pass merges one item of each row
+  lds_sync();
+  MergeItem it[2];
+  int seq[2];    // first item of this wavefront, per row (>= 32: none)
+  int step[2];
 #pragma unroll
-  for (int sgi = 0; sgi < kMaxSeg; ++sgi) {
-    if (sgi < nseg) {
-      const int64_t sl = base + (int64_t)sgi * kRowQ;
-      ml[sgi] = *reinterpret_cast<const float2*>(a.part_ml + sl * 2);
-      oz[sgi] = *reinterpret_cast<const v8hc*>(a.part_o + sl * D + 8 * c8);
+  for (int k = 0; k < 2; ++k) {
+    it[k].row = __builtin_amdgcn_readfirstlane(s_merge[k][0]);
+    it[k].nseg = __builtin_amdgcn_readfirstlane(s_merge[k][2]);
+    seq[k] = 2 * kRowQ / 16;
+    step[k] = 0;
+    if (it[k].row >= 0) {
+      if (tid == 0) merge_wait(a, s_merge[k][1], it[k].nseg);
+      seq[k] = __builtin_amdgcn_readfirstlane(s_merge[k][3]) + w * it[k].nseg;
+      step[k] = kWaves * it[k].nseg;
     }
   }
-  float mx = -INFINITY;
+  lds_sync();
+  if (tid == 0) {   // done with the counts: the last to leave a row clears them
 #pragma unroll
-  for (int sgi = 0; sgi < kMaxSeg; ++sgi)
-    if (sgi < nseg) mx = __builtin_fmaxf(mx, ml[sgi].x);
-  float l = 0.0f, o[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-  if (mx != -INFINITY) {
-#pragma unroll
-    for (int sgi = 0; sgi < kMaxSeg; ++sgi) {
-      if (sgi < nseg) {
-        const float wz = __builtin_amdgcn_exp2f(ml[sgi].x - mx) * ml[sgi].y;
-        l += wz;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) o[c] += wz * float(oz[sgi][c]);
+    for (int k = 0; k < 2; ++k) {
+      if (s_merge[k][0] < 0) continue;
+      const int vf = s_merge[k][1];
+      const int d = __hip_atomic_fetch_add(merge_departures(a, vf), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (d == s_merge[k][2] - 1) {
+        __hip_atomic_store(merge_arrivals(a, vf), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(merge_departures(a, vf), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
-  const float il = l > 0.0f ? 1.0f / l : 0.0f;
-  uint16_t* dst = a.out + ((int64_t)i * a.heads + head) * D + 8 * c8;
-  uint32_t wv[4];
+  constexpr int kItems = 2 * kRowQ / 16;   // 32 items per row
+#pragma nounroll
+  while (seq[0] < kItems || seq[1] < kItems) {
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
-    wv[c] = uint32_t(f32_to_bf16(o[2 * c] * il)) | (uint32_t(f32_to_bf16(o[2 * c + 1] * il)) << 16);
-  // out is 8-byte aligned (its documented alignment): two 8-byte stores
-  *reinterpret_cast<uint2*>(dst) = make_uint2(wv[0], wv[1]);
-  *reinterpret_cast<uint2*>(dst + 4) = make_uint2(wv[2], wv[3]);
-  if (c8 == 0) a.lse[(int64_t)head * a.nq + i] = l > 0.0f ? (mx + __log2f(l)) * kLn2 : -INFINITY;
+    for (int k = 0; k < 2; ++k) {
+      it[k].on = seq[k] < kItems;
+      it[k].gi = seq[k] >> 1;
+      it[k].hf = seq[k] & 1;
+      seq[k] += step[k];
+    }
+    merge_items<D>(a, it, lane);
+  }
 }
+
+
 
 struct Plan {
   int qtiles, rows, tv, grid, max_seg, first1, n1, first2, seg_cost;
@@ -900,17 +1068,18 @@ Plan make_plan(int32_t heads, int32_t slots, int32_t nq, int32_t ring_head, int3
   if (p.tv > 0) {
     const int64_t min_w = (span + 6) / 7;
     if (g > p.cost / min_w) g = p.cost / min_w;
-    // one work-group per row (no row split, so no merge pass) when a whole row weighs no more
-    // than a share of the split plan plus the merge pass, which costs about kCombineCost tiles
-    // (its launch and its reads): the case of a short ring, as while the ring fills up
+    // one work-group per row (no row split, so no merge) when a whole row weighs no more than a
+    // share of the split plan plus the cost of splitting, about kMergeCost tiles (the partial
+    // stores, the counts and the last arrival's merge): the case of a short ring, as while the
+    // ring fills up
     const int64_t cap = grid_cap < kMaxGrid ? grid_cap : kMaxGrid;
-    if (p.rows <= cap && g > 0 && span <= (p.cost + g - 1) / g + kCombineCost) g = p.rows;
+    if (p.rows <= cap && g > 0 && span <= (p.cost + g - 1) / g + kMergeCost) g = p.rows;
   }
   p.grid = int(g < 1 ? 1 : g);
   // a row of weight span is shared by at most ceil(span / floor(cost / grid)) + 1 work-groups
   const int64_t per = p.cost / p.grid;
   p.max_seg = p.units > 0 ? int((span + per - 1) / per) + 1 : 1;
-  if (p.max_seg > 8) p.max_seg = 8;
+  if (p.max_seg > kMaxSeg) p.max_seg = kMaxSeg;
   return p;
 }
 
@@ -930,9 +1099,12 @@ void set_attention_events(void* before, void* after) {
 namespace {
 
 // Workspace layout (floats, each part 16-byte aligned): the per-head synchronisation records
-// (kSyncBytes, head_sync; the query preparation takes slot 1) | split rows' partial outputs |
-// their (m, l) | quantised queries | query scales.  Sized for the largest plan
-// any (ring_head, filled) and any grid <= 256 can produce (<= 8 segments per row).
+// (kSyncBytes, head_sync; the query preparation takes slot 1) | the split rows' arrival and
+// departure counts (two 128-byte lines per work-group of the largest grid; at a fixed offset,
+// like the records, so that one zero-filled workspace serves calls of any shape) | split rows' partial
+// outputs | their (m, l) | quantised queries | query scales.  Sized for the largest plan any
+// (ring_head, filled) and any grid <= 256 can produce (<= 8 segments per row).
+constexpr int64_t kMergeCountBytes = (int64_t)kMaxGrid * 2 * kSyncLine;
 struct WsLayout {
   int64_t part_o, part_ml, q_codes, q_scale, total;
 };
@@ -941,7 +1113,7 @@ WsLayout ws_layout(int32_t heads, int32_t slots, int32_t head_dim, int32_t nq) {
   auto up4 = [](int64_t x) { return (x + 3) / 4 * 4; };
   const Plan p = make_plan(heads, slots, nq, 0, slots, kMaxGrid);
   WsLayout l;
-  l.part_o = kSyncBytes / 4;
+  l.part_o = (kSyncBytes + kMergeCountBytes) / 4;
   l.part_ml = l.part_o + (int64_t)p.rows * 8 * kRowQ * head_dim / 2;   // half precision
   l.q_codes = l.part_ml + (int64_t)p.rows * 8 * kRowQ * 2;
   l.q_scale = l.q_codes + (int64_t)p.rows * (kRowQ * 128) / 4;   // 128 bytes per query
@@ -983,6 +1155,8 @@ hipError_t launch_attention(const kv_ring_desc& r, int32_t ring_head, int32_t fi
   a.lse = lse;
   a.part_o = reinterpret_cast<_Float16*>(aw.part_o);
   a.part_ml = aw.part_ml;
+  a.merge_cnt = reinterpret_cast<int*>(ws + kSyncBytes / 4);
+  a.err = sync_error_word(ws);
   a.tiles = tile_count(r.slots);
   a.heads = r.heads;
   a.slots = r.slots;
@@ -1033,22 +1207,9 @@ hipError_t launch_attention(const kv_ring_desc& r, int32_t ring_head, int32_t fi
     hipLaunchKernelGGL(attn_pp<64>, dim3(a.grid), dim3(kThreads), 0, stream, a);
   e = hipGetLastError();
   if (e == hipSuccess && events) e = hipEventRecord(g_ev_after, stream);
-  if (e != hipSuccess) return e;
-  bool split = false;   // does any row span more than one work-group?
-  for (int row = 0; row < p.rows && !split; ++row) {
-    const UnitSplit us{a.tv, a.seg_cost, a.cost, a.grid};
-    split = us.owner((int64_t)row * a.tv + a.tv - 1) != us.owner((int64_t)row * a.tv);
-  }
-  if (!split) return e;
-  dim3 gc((kRowQ * r.head_dim / 8 + 255) / 256, p.rows);
-  if (r.head_dim == 128)
-    hipLaunchKernelGGL(attn_combine<128>, gc, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(attn_combine<64>, gc, dim3(256), 0, stream, a);
-  return hipGetLastError();
+  return e;
 }
 
-// Exposed E4M3 encoder (the one the kernels use), for exhaustive checking.
 __global__ void fp8_encode_kernel(const float* __restrict__ x, uint8_t* __restrict__ out, int64_t n) {
   const int64_t i4 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (i4 + 3 < n) {

@@ -14,12 +14,17 @@ from kvhelpers import to_dev_bf16
 pytestmark = pytest.mark.gpu
 
 MAX_HEADS, RECORD_BYTES = 512, 6 * 128
+# after the records and the error word: the split rows' arrival and departure counts of the
+# attention (two 128-byte lines for each of up to 256 work-groups)
+MERGE_OFFSET, MERGE_BYTES = 2 * MAX_HEADS * RECORD_BYTES + 256, 256 * 2 * 128
 
 
 def _counts_zero(ws):
-    """Every record's count word (the first int32 of each record) is zero."""
+    """Every record's count word (the first int32 of each record) is zero, and so is every
+    split-row count."""
     rec = ws[:2 * MAX_HEADS * RECORD_BYTES].view(2 * MAX_HEADS, RECORD_BYTES)[:, :4]
-    return int(rec.count_nonzero().item()) == 0
+    merge = ws[MERGE_OFFSET:MERGE_OFFSET + MERGE_BYTES]
+    return int(rec.count_nonzero().item()) == 0 and int(merge.count_nonzero().item()) == 0
 
 
 def _ring_state(r):
@@ -126,4 +131,52 @@ def test_rotation_and_write_replay_from_a_captured_graph():
         _same(_ring_state(ring), eager, f"replay {rep}")
         assert _counts_zero(ws)
         _ = (k.float() * 2).sum().item()   # eager work between replays
+    assert kv.sync_status(ws) == 0
+
+
+def test_split_row_attention_replays_from_a_captured_graph():
+    """Attention whose rows are split between work-groups (merged by the last one to finish),
+    captured once and replayed three times with eager work in between: every replay gives the
+    eager call's output bit for bit and leaves every count at zero."""
+    import torch
+    import fp8_ring_kv_write_amd as kv
+    h, s, d, n = 6, 900, 128, 300     # 12 rows of 8 tiles: split over about 60 work-groups
+    tab = torch.from_numpy(kv.rope_table(16384, d)).cuda()
+    ring = kv.Ring(h, s, d)
+    for c in range(3):
+        kv.kv_ring_write(ring, to_dev_bf16(normal_bf16(tensor_seed("sync_attn", c, 1), (n, h, d))),
+                         to_dev_bf16(normal_bf16(tensor_seed("sync_attn", c, 2), (n, h, d))),
+                         (c * n) % s, c * n, tab)
+    q = to_dev_bf16(normal_bf16(tensor_seed("sync_attn", 9, 0), (n, h, d)))
+    ws = torch.zeros(kv.workspace_bytes(kv.OP_ATTENTION, h, s, d, n), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((h, n), dtype=torch.float32, device="cuda")
+
+    def call():
+        kv.ring_attention(ring, 0, s, q, 2 * n, tab, 0.088, out=out, lse=lse, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    eager = [out.clone(), lse.clone()]
+    assert _counts_zero(ws)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        print(f"[sync] attention graph replay {rep}", flush=True)
+        out.zero_()
+        lse.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _same([out, lse], eager, f"attention replay {rep}")
+        assert _counts_zero(ws)
+        _ = (q.float() * 2).sum().item()   # eager work between replays
     assert kv.sync_status(ws) == 0
