@@ -65,8 +65,8 @@ ATT_KERNEL = "attn_pp<128>"
 # (FETCH_SIZE, WRITE_SIZE) over this workload, each divided by the factor the same counter
 # reads for a torch copy of --calibrate-copy bytes.  Valid only for the kernel sources whose
 # hash is recorded; reported as null otherwise.
-ATT_TRAFFIC = {"sources": "fe44ef93316fe390", "bytes": 97_470_000,
-               "read_bytes": 76_380_000, "write_bytes": 21_090_000}
+ATT_TRAFFIC = {"sources": "5d4f7c585d5e0437", "bytes": 122_020_000,
+               "read_bytes": 95_660_000, "write_bytes": 26_360_000}
 WRITE_BYTES = 2 * N * H * D * 2 + 2 * N * H * D + 2 * N * H * 4
 ROTATE_BYTES = 2 * (H * S * D + H * S * 4)
 

@@ -64,7 +64,7 @@ constexpr int kRowQ = 2 * kGroupQ * kWaves;   // 256 queries per row, 32 per wav
 constexpr int kBufs = 3;                // LDS buffers of K tiles
 constexpr int kMaxGrid = 256;
 constexpr int kSegCost = 2;             // weight of a segment start in tiles (UnitSplit)
-constexpr int kMergeCost = 6;           // weight of splitting rows (partial stores, the merge), in tiles
+constexpr int kMergeCost = 2;           // weight of splitting rows (partial stores, the merge), in tiles
 constexpr int kMaxSeg = 8;              // segments of a row, at most (make_plan)
 constexpr float kTau = 4.0f;            // lazy rescale threshold, log2 units
 constexpr float kPmax = 4096.0f;        // bound on a lane's probability sum in the fast path
@@ -1060,7 +1060,7 @@ Plan make_plan(int32_t heads, int32_t slots, int32_t nq, int32_t ring_head, int3
     p.tv = 0;
   }
   p.units = (int64_t)p.rows * p.tv;
-  p.seg_cost = p.tv >= 8 ? kSegCost : 0;
+  p.seg_cost = kSegCost;
   const int64_t span = (int64_t)p.tv + p.seg_cost;   // weight of a row
   p.cost = (int64_t)p.rows * span;
   // every work-group takes a weight of at least ceil(span / 7), so that at most 8 share a row
@@ -1070,8 +1070,8 @@ Plan make_plan(int32_t heads, int32_t slots, int32_t nq, int32_t ring_head, int3
     if (g > p.cost / min_w) g = p.cost / min_w;
     // one work-group per row (no row split, so no merge) when a whole row weighs no more than a
     // share of the split plan plus the cost of splitting, about kMergeCost tiles (the partial
-    // stores, the counts and the last arrival's merge): the case of a short ring, as while the
-    // ring fills up
+    // stores, the wait for the row's other segments and the merge): the case of a ring holding
+    // few tiles, as at the start of its fill-up
     const int64_t cap = grid_cap < kMaxGrid ? grid_cap : kMaxGrid;
     if (p.rows <= cap && g > 0 && span <= (p.cost + g - 1) / g + kMergeCost) g = p.rows;
   }
