@@ -38,8 +38,10 @@
  *     work-groups of one launch agree on a head's absmax (kv_ring_workspace_bytes counts them):
  *     the caller zero-fills a workspace once, before its first use, and every call leaves the
  *     records ready for the next (graph replays included), so one workspace serves every
- *     operation and every ring shape in turn.  A record wait that exceeds its bound (no such
- *     wait arises in correct use) sets a word of the workspace instead of hanging;
+ *     operation and every ring shape in turn.  An attention workspace also holds, right after
+ *     the records, the counts through which the work-groups sharing a query row merge their
+ *     partial results (left at zero by every call as well).  A wait that exceeds its bound (no
+ *     such wait arises in correct use) sets a word of the workspace instead of hanging;
  *     kv_ring_sync_status reads it.
  */
 #ifndef KVRING_H
@@ -62,7 +64,7 @@ enum {
   KV_RING_ERR_WORKSPACE = -6,  /* workspace NULL or smaller than required              */
   KV_RING_ERR_LAUNCH = -7,     /* a kernel launch failed (HIP error)                   */
   KV_RING_ERR_SCRATCH = -8,    /* kv_ring_write_static: the call does not fit its scratch */
-  KV_RING_ERR_SYNC = -9        /* kv_ring_sync_status: a record wait exceeded its bound */
+  KV_RING_ERR_SYNC = -9        /* kv_ring_sync_status: a wait exceeded its bound       */
 };
 
 enum {
@@ -138,12 +140,15 @@ int kv_ring_rope_table_3d(float *host_out, const int32_t *positions, int64_t n, 
 /* Workspace bytes for `op` (KV_RING_OP_*) with n = new tokens (write), unused (delta
  * rotate), nq = queries (attention) or the larger of the two (write + attention).  Returns 0
  * for an unknown op or invalid shape.  Every workspace starts with the same synchronisation
- * records (786,688 bytes), zero-filled by the caller before first use. */
+ * records (786,688 bytes), zero-filled by the caller before first use; attention workspaces
+ * (KV_RING_OP_ATTENTION, KV_RING_OP_WRITE_ATTEND) follow them with 65,536 bytes of split-row
+ * counts. */
 size_t kv_ring_workspace_bytes(int32_t op, int32_t heads, int32_t slots, int32_t head_dim,
                                int32_t n);
 
-/* Whether any record wait of the calls made with `workspace` (device memory) has exceeded its
- * bound: copies one word of it to the host, waiting for `stream` first.  KV_RING_OK, or
+/* Whether any wait of the calls made with `workspace` (device memory) on another work-group of
+ * the same launch (a head's record, a split row's count) has exceeded its bound: copies one word
+ * of it to the host, waiting for `stream` first.  KV_RING_OK, or
  * KV_RING_ERR_SYNC (the outputs of those calls are then not to be trusted), KV_RING_ERR_NULL,
  * KV_RING_ERR_ALIGN (workspace not 16-byte aligned), KV_RING_ERR_LAUNCH (a HIP error). */
 int kv_ring_sync_status(const void *workspace, void *stream);
@@ -217,6 +222,9 @@ int kv_ring_delta_rotate_3d(const kv_ring_desc *ring, int32_t ring_head, int32_t
  *   out          device bfloat16 [nq][heads][head_dim], 8-byte aligned;
  *   lse          device float32 [heads][nq]: natural-log softmax denominator plus row max.
  * With filled == 0 the output is 0 and lse is -inf.  nq == 0 is a no-op.
+ * The launch is a grid of at most one work-group per compute unit; work-groups sharing a query
+ * row wait for one another to merge it, which every device running nothing else (and any on
+ * which each XCD can hold the few consecutive work-groups of a row at once) lets finish.
  * Errors: NULL pointers, misalignment, nq < 0, ring_head/filled out of range, softmax_scale not
  * finite and positive, positions outside the table, workspace too small.
  */
