@@ -78,14 +78,20 @@ struct QuantQArgs {
   float* scale;           // [heads]
   int64_t pos0;
   int32_t nq, qtiles;
-  int32_t blocks;         // 2 * qtiles (a work-group takes 64 queries of a row); 0: none
+  int32_t blocks;         // 2 * qtiles (a work-group takes 64 queries of a row); 0: none (or
+                          // prepared by the write's work-groups, see write_chunk)
 };
 
-// The write's work-group: one aligned 32-slot chunk of the ring x one head.
-template <int D>
-__device__ inline void write_chunk(const WriteArgs& wa, const float* __restrict__ rope, int blk, int h) {
+// The write's work-group: one aligned 32-slot chunk of the ring x one head.  With WQ (head_dim
+// 128, the queries being the new tokens themselves: same count, same positions) it also prepares
+// the queries of its tokens: the rotary rows it loads serve both, and the queries' absmax joins
+// the write's exchange (head_sync_pair: the write's record and the queries' record at once).
+template <int D, bool WQ>
+__device__ inline void write_chunk(const WriteArgs& wa, const QuantQArgs& qa_, const float* __restrict__ rope,
+                                   int blk, int h) {
   constexpr int CPT = D / 8;
-  __shared__ float sl[10];
+  static_assert(!WQ || D == 128, "queries with the write: head_dim 128");
+  __shared__ float sl[16];
   __shared__ __align__(16) uint8_t vlds[kChunk][D];
   const WriteGeom& g = wa.g;
   const uint16_t* __restrict__ k_new = wa.k_new;
@@ -97,18 +103,21 @@ __device__ inline void write_chunk(const WriteArgs& wa, const float* __restrict_
   const int chunk = blk < g.n_chunks_a ? g.chunk_a0 + blk : blk - g.n_chunks_a;
   char* rec = sync_record(wa.sync, 0, h);
   const unsigned gen = head_sync_generation(rec);
+  char* rec_q = WQ ? sync_record(qa_.sync, 1, h) : nullptr;
+  const unsigned gen_q = WQ ? head_sync_generation(rec_q) : 0u;
 
   const int t = threadIdx.x >> 3, cg = threadIdx.x & 7;
   const int slot = chunk * kChunk + t;
   int i = slot - g.start;
   i = i < 0 ? i + g.slots : i;
   const bool mine = slot < g.slots && i < g.n;
-  float xk[CPT], xv[CPT];
+  float xk[CPT], xv[CPT], xq[WQ ? CPT : 1];
   float4 tab[CPT / 4];
   if (mine) {
     const int64_t src = ((int64_t)i * g.heads + h) * D + cg * CPT;
     load_bf16<CPT>(k_new + src, xk);
     load_bf16<CPT>(v_new + src, xv);
+    if constexpr (WQ) load_bf16<CPT>(qa_.q + src, xq);
     const float4* t4 = reinterpret_cast<const float4*>(rope + ((g.pos0 + i) * (D / 2) + cg * (CPT / 2)) * 2);
 #pragma unroll
     for (int j = 0; j < CPT / 4; ++j) tab[j] = t4[j];
@@ -116,7 +125,7 @@ __device__ inline void write_chunk(const WriteArgs& wa, const float* __restrict_
 
   // RoPE of K (pairs 2j, 2j+1 of this thread's channels), then the write's per-head absmax of
   // K' and V over every work-group of the head
-  float mk = 0.0f, mv = 0.0f;
+  float mk = 0.0f, mv = 0.0f, mq = 0.0f;
   if (mine) {
 #pragma unroll
     for (int j = 0; j < CPT / 4; ++j) {
@@ -127,15 +136,50 @@ __device__ inline void write_chunk(const WriteArgs& wa, const float* __restrict_
         const float xe = xk[2 * p], xo = xk[2 * p + 1];
         xk[2 * p] = xe * cs[e][0] - xo * cs[e][1];
         xk[2 * p + 1] = xe * cs[e][1] + xo * cs[e][0];
+        if constexpr (WQ) {
+          const float qe = xq[2 * p], qo = xq[2 * p + 1];
+          xq[2 * p] = qe * cs[e][0] - qo * cs[e][1];
+          xq[2 * p + 1] = qe * cs[e][1] + qo * cs[e][0];
+        }
       }
     }
     mk = absmax<CPT>(xk);
     mv = absmax<CPT>(xv);
+    if constexpr (WQ) mq = absmax<CPT>(xq);
   }
-  head_sync<kThreads>(rec, gen, sync_error_word(wa.sync), wa.blocks, true, mk, mv, sl);
+  if constexpr (WQ)
+    head_sync_pair<kThreads>(rec, gen, wa.blocks, mk, mv, rec_q, gen_q, wa.blocks, mq,
+                             sync_error_word(wa.sync), sl);
+  else
+    head_sync<kThreads>(rec, gen, sync_error_word(wa.sync), wa.blocks, true, mk, mv, sl);
   float sk, ik, sv, iv;
   scale_from_absmax(mk, sk, ik);
   scale_from_absmax(mv, sv, iv);
+  if constexpr (WQ) {
+    // the queries: query i = token i, channels 16cg .. 16cg + 15 are half of the 32 bytes that
+    // lane (g = cg/2, li = i % 16) of wavefront (i % 128) / 16 of 128-query tile i / 128 holds
+    float sq, iq;
+    scale_from_absmax(mq, sq, iq);
+    if (blk == 0 && threadIdx.x == 0) qa_.scale[h] = sq;
+    if (mine) {
+      uint32_t wq[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        wq[j] = e4m3x4(xq[4 * j] * iq, xq[4 * j + 1] * iq, xq[4 * j + 2] * iq, xq[4 * j + 3] * iq);
+      const int qt = i >> 7, w = (i >> 4) & 7, lane = 16 * (cg >> 1) + (i & 15);
+      *reinterpret_cast<uint4*>(qa_.codes + ((((int64_t)h * qa_.qtiles + qt) * 8 + w) * 64 + lane) * 32 +
+                                16 * (cg & 1)) = make_uint4(wq[0], wq[1], wq[2], wq[3]);
+    }
+    if (blk == 0) {   // the padding queries of the last tiles: zero codes
+      const int pad0 = g.n, pad1 = qa_.qtiles * 128;
+      for (int e = pad0 * 8 + int(threadIdx.x); e < pad1 * 8; e += kThreads) {
+        const int ii = e >> 3, part = e & 7;   // 8 x 16 bytes per query
+        const int qt = ii >> 7, w = (ii >> 4) & 7, lane = 16 * (part >> 1) + (ii & 15);
+        *reinterpret_cast<uint4*>(qa_.codes + ((((int64_t)h * qa_.qtiles + qt) * 8 + w) * 64 + lane) * 32 +
+                                  16 * (part & 1)) = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  }
 
   if (mine) {
     float (&x)[CPT] = xk;
@@ -247,14 +291,15 @@ __device__ inline void quantize_q_half(const QuantQArgs& qa_, const float* __res
   dst[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
 }
 
-// grid = (write blocks + query blocks, heads); each work-group does one or the other.  A head's
+// grid = (write blocks + query blocks, heads); each work-group does one or the other (WQ: the
+// write's work-groups prepare the queries too, and there are no query blocks).  A head's
 // work-groups have consecutive indices (x varies fastest), as head_sync requires.
-template <int D>
+template <int D, bool WQ>
 __global__ __launch_bounds__(kThreads) void quantize_pass(WriteArgs wa, QuantQArgs qa_,
                                                           const float* __restrict__ rope, int32_t heads) {
   const int h = blockIdx.y;
   if ((int)blockIdx.x < wa.blocks)
-    write_chunk<D>(wa, rope, blockIdx.x, h);
+    write_chunk<D, WQ>(wa, qa_, rope, blockIdx.x, h);
   else
     quantize_q_half<D>(qa_, rope, blockIdx.x - wa.blocks, h, heads);
 }
@@ -318,12 +363,19 @@ QuantQArgs quant_q_args(const uint16_t* q, int32_t nq, int64_t q_pos0, void* syn
 }
 
 hipError_t launch_quantize_pass(const WriteArgs& wa, const QuantQArgs& qa_, const float* rope,
-                                int32_t heads, int32_t head_dim, hipStream_t stream) {
+                                int32_t heads, int32_t head_dim, hipStream_t stream, bool merged = false) {
+  if (merged) {   // the queries with the write's work-groups (head_dim 128)
+    QuantQArgs qm = qa_;
+    qm.blocks = 0;
+    hipLaunchKernelGGL((quantize_pass<128, true>), dim3(wa.blocks, heads), dim3(kThreads), 0, stream, wa, qm,
+                       rope, heads);
+    return hipGetLastError();
+  }
   dim3 g2(wa.blocks + qa_.blocks, heads);
   if (head_dim == 128)
-    hipLaunchKernelGGL(quantize_pass<128>, g2, dim3(kThreads), 0, stream, wa, qa_, rope, heads);
+    hipLaunchKernelGGL((quantize_pass<128, false>), g2, dim3(kThreads), 0, stream, wa, qa_, rope, heads);
   else
-    hipLaunchKernelGGL(quantize_pass<64>, g2, dim3(kThreads), 0, stream, wa, qa_, rope, heads);
+    hipLaunchKernelGGL((quantize_pass<64, false>), g2, dim3(kThreads), 0, stream, wa, qa_, rope, heads);
   return hipGetLastError();
 }
 
@@ -360,9 +412,12 @@ hipError_t launch_write_and_q_prep(const kv_ring_desc& r, const uint16_t* k_new,
                                    int64_t pos0, const uint16_t* q, int32_t nq, int64_t q_pos0,
                                    const float* rope, float* ws, uint8_t* codes, float* scale,
                                    hipStream_t stream) {
+  // the queries are the new tokens themselves (the layer call of the method): the write's
+  // work-groups prepare them too
+  const bool merged = r.head_dim == 128 && nq == n && q_pos0 == pos0 && n > 0;
   return launch_quantize_pass(write_args(r, k_new, v_new, n, start_slot, pos0, ws),
                               quant_q_args(q, nq, q_pos0, ws, codes, scale), rope, r.heads,
-                              r.head_dim, stream);
+                              r.head_dim, stream, merged);
 }
 
 // ---- the write without a caller workspace (kv_ring_write_static) ---------------------------------

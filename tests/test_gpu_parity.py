@@ -490,6 +490,9 @@ def test_layer_calls_replay_from_a_captured_graph(kv, torch):
 
 @pytest.mark.parametrize("heads,slots,d,n,nq,writes", [
     (24, 5788, 128, 757, 757, 8),    # the steady-state layer call (the last write wraps)
+    (2, 100, 128, 77, 77, 3),        # queries = new tokens (prepared by the write's work-groups):
+    (3, 64, 128, 1, 1, 3),           #   a write that wraps, one token, one whole 256-query row
+    (2, 600, 128, 256, 256, 2),
     (3, 700, 128, 16, 129, 5),       # more queries than new tokens
     (2, 300, 64, 100, 1, 4),
     (2, 300, 128, 77, 0, 2),         # no queries: the write alone
