@@ -148,8 +148,7 @@ __device__ inline void write_chunk(const WriteArgs& wa, const QuantQArgs& qa_, c
     if constexpr (WQ) mq = absmax<CPT>(xq);
   }
   if constexpr (WQ)
-    head_sync_pair<kThreads>(rec, gen, wa.blocks, mk, mv, rec_q, gen_q, wa.blocks, mq,
-                             sync_error_word(wa.sync), sl);
+    head_sync_pair<kThreads>(rec, gen, wa.blocks, mk, mv, rec_q, gen_q, mq, sync_error_word(wa.sync), sl);
   else
     head_sync<kThreads>(rec, gen, sync_error_word(wa.sync), wa.blocks, true, mk, mv, sl);
   float sk, ik, sv, iv;

@@ -240,15 +240,17 @@ __device__ inline void head_sync(char* rec, unsigned g, int* err, int expected, 
   v1 = lds[2 * NW + 1];
 }
 
-// head_sync on two records at once, for work-groups that take part in both (a write that also
-// prepares the queries of its own tokens): record A with two maxima (v0, v1) and record B with one
-// (w0), each with its own generation and expected count.  Thread 0 adds to both records' maxima
-// and counts before waiting on either, so the two exchanges cost the round trips of one.  `lds`
-// is LDS scratch of >= 3 * NT/64 + 3 floats used by this call only.
+// head_sync for work-groups that exchange three maxima of one head over two records (a write
+// that also prepares the queries of its own tokens): record A with two maxima (v0, v1) and record
+// B with one (w0), the same work-groups taking part in both.  Each work-group adds to the three
+// maxima, then counts itself in at A only (the count-in depends on all three returned old
+// maxima, so they are in before it); the last one in readies both records for the next launch
+// (B's other set of maxima zeroed and its generation bumped as well; B's count is never used
+// here and stays zero) and releases the waiters, which poll A's generation alone.  `lds` is LDS
+// scratch of >= 3 * NT/64 + 3 floats used by this call only.
 template <int NT>
-__device__ inline void head_sync_pair(char* ra, unsigned ga, int expected_a, float& v0, float& v1,
-                                      char* rb, unsigned gb, int expected_b, float& w0, int* err,
-                                      float* lds) {
+__device__ inline void head_sync_pair(char* ra, unsigned ga, int expected, float& v0, float& v1,
+                                      char* rb, unsigned gb, float& w0, int* err, float* lds) {
   constexpr int NW = NT / 64;
   v0 = wave_max(v0);
   v1 = wave_max(v1);
@@ -272,40 +274,31 @@ __device__ inline void head_sync_pair(char* ra, unsigned ga, int expected_a, flo
     }
     const unsigned pa = ga & 1u, pb = gb & 1u;
     int* ca = reinterpret_cast<int*>(ra);
-    int* cb = reinterpret_cast<int*>(rb);
     unsigned* gena = reinterpret_cast<unsigned*>(ra + kSyncLine);
     unsigned* genb = reinterpret_cast<unsigned*>(rb + kSyncLine);
-    unsigned oa = __hip_atomic_fetch_max(maxima(ra, pa, 0), __float_as_uint(m0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    oa |= __hip_atomic_fetch_max(maxima(ra, pa, 1), __float_as_uint(m1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned ob = __hip_atomic_fetch_max(maxima(rb, pb, 0), __float_as_uint(m2), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // each count-in depends on its record's returned old maxima (never 0xFFFFFFFF: the
-    // increment is 1), which orders it after them
-    const int ba = __hip_atomic_fetch_add(ca, (oa != 0xFFFFFFFFu) ? 1 : 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int bb = __hip_atomic_fetch_add(cb, (ob != 0xFFFFFFFFu) ? 1 : 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last_a = ba == expected_a - 1, last_b = bb == expected_b - 1;
-    if (last_a) {   // ready record A for the next launch, release its waiters
+    unsigned o = __hip_atomic_fetch_max(maxima(ra, pa, 0), __float_as_uint(m0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    o |= __hip_atomic_fetch_max(maxima(ra, pa, 1), __float_as_uint(m1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    o |= __hip_atomic_fetch_max(maxima(rb, pb, 0), __float_as_uint(m2), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // o is never 0xFFFFFFFF (finite or +inf bit patterns), so the increment is 1; it depends on
+    // the three returned old maxima, which orders it after them
+    const int before = __hip_atomic_fetch_add(ca, (o != 0xFFFFFFFFu) ? 1 : 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (before == expected - 1) {   // the last one in: ready both records, release the others
       __hip_atomic_store(maxima(ra, pa ^ 1u, 0), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(maxima(ra, pa ^ 1u, 1), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(ca, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(gena, ga + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    if (last_b) {
       __hip_atomic_store(maxima(rb, pb ^ 1u, 0), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(maxima(rb, pb ^ 1u, 1), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(cb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(genb, gb + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    bool wait_a = !last_a, wait_b = !last_b;
-    int polls = 0;
-    while (wait_a || wait_b) {
-      if (wait_a) wait_a = __hip_atomic_load(gena, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ga;
-      if (wait_b) wait_b = __hip_atomic_load(genb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gb;
-      if (!(wait_a || wait_b)) break;
-      if (++polls > kSpinLimit) {
-        __hip_atomic_fetch_or(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
+      __hip_atomic_store(ca, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(gena, ga + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      int polls = 0;
+      while (__hip_atomic_load(gena, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ga) {
+        if (++polls > kSpinLimit) {
+          __hip_atomic_fetch_or(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
       }
-      __builtin_amdgcn_s_sleep(1);
     }
     lds[3 * NW] = __uint_as_float(__hip_atomic_load(maxima(ra, pa, 0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     lds[3 * NW + 1] = __uint_as_float(__hip_atomic_load(maxima(ra, pa, 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
