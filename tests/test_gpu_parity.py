@@ -570,6 +570,16 @@ def test_attention_many_segments_per_work_group(kv, torch):
     check_attention(*p.attend(q, 500, 1 / math.sqrt(128)), label="384 rows of 16 tiles")
 
 
+def test_attention_rows_split_seven_ways(kv, torch):
+    """One head, 300 queries over a full 5,788-slot ring: 2 rows of 46 tiles over a grid of 13
+    work-groups (no XCD renumbering: 13 is not a multiple of 8), so every row is split between
+    7 work-groups and its merge reads its segments in two batches."""
+    p = Pair(kv, torch, 1, 5788, 128)
+    _fill_steady(p, "seven_ways", 757, 8)             # 6,056 tokens: wraps, ring full
+    q = normal_bf16(tensor_seed("seven_ways", 9, 0), (300, 1, 128))
+    check_attention(*p.attend(q, 6000, 1 / math.sqrt(128)), label="rows split 7 ways")
+
+
 def test_chunk_passes_rewrite_the_same_slots(kv, torch):
     """A chunk of the method on two layers: each of four denoising passes rewrites the chunk's
     slots at the same positions and attends (through kv_ring_write_attend); the ring head moves
