@@ -24,6 +24,12 @@ namespace kvring {
 namespace {
 
 constexpr int kThreads = 256;
+// The codes and scales are stored non-temporal (streaming: written to memory rather than held
+// in L2 for the end of the launch); the attention that follows reads them from memory anyway.
+typedef uint32_t nt4_t __attribute__((ext_vector_type(4)));
+__device__ inline void store16_nt(void* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  __builtin_nontemporal_store(nt4_t{a, b, c, d}, reinterpret_cast<nt4_t*>(p));
+}
 
 // Load CPT bf16 channels starting at `p` (16-byte aligned) into floats.
 template <int CPT>
@@ -166,8 +172,8 @@ __device__ inline void write_chunk(const WriteArgs& wa, const QuantQArgs& qa_, c
       for (int j = 0; j < 4; ++j)
         wq[j] = e4m3x4(xq[4 * j] * iq, xq[4 * j + 1] * iq, xq[4 * j + 2] * iq, xq[4 * j + 3] * iq);
       const int qt = i >> 7, w = (i >> 4) & 7, lane = 16 * (cg >> 1) + (i & 15);
-      *reinterpret_cast<uint4*>(qa_.codes + ((((int64_t)h * qa_.qtiles + qt) * 8 + w) * 64 + lane) * 32 +
-                                16 * (cg & 1)) = make_uint4(wq[0], wq[1], wq[2], wq[3]);
+      store16_nt(qa_.codes + ((((int64_t)h * qa_.qtiles + qt) * 8 + w) * 64 + lane) * 32 + 16 * (cg & 1),
+                 wq[0], wq[1], wq[2], wq[3]);
     }
     if (blk == 0) {   // the padding queries of the last tiles: zero codes
       const int pad0 = g.n, pad1 = qa_.qtiles * 128;
@@ -190,7 +196,7 @@ __device__ inline void write_chunk(const WriteArgs& wa, const QuantQArgs& qa_, c
     uint8_t* dst = kc + (int64_t)h * g.tiles * kTile * D + k_code_offset(slot, (cg * CPT) & ~15, D) +
                    ((cg * CPT) & 15);
     if constexpr (CPT == 16) {
-      *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+      store16_nt(dst, w[0], w[1], w[2], w[3]);
     } else {
       *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
     }
@@ -201,8 +207,8 @@ __device__ inline void write_chunk(const WriteArgs& wa, const QuantQArgs& qa_, c
 #pragma unroll
     for (int j = 0; j < CPT / 4; ++j) vl[j] = w[j];
     if (cg == 0) {
-      k_scale[(int64_t)h * g.slots + slot] = sk;
-      v_scale[(int64_t)h * g.slots + slot] = sv;
+      __builtin_nontemporal_store(sk, &k_scale[(int64_t)h * g.slots + slot]);
+      __builtin_nontemporal_store(sv, &v_scale[(int64_t)h * g.slots + slot]);
     }
   }
   __syncthreads();
@@ -226,7 +232,7 @@ __device__ inline void write_chunk(const WriteArgs& wa, const QuantQArgs& qa_, c
       word[kk >> 2] |= uint32_t(vlds[16 * r + kk][d]) << (8 * (kk & 3));
     }
     if (nmine == 16) {
-      *reinterpret_cast<uint4*>(unit) = make_uint4(word[0], word[1], word[2], word[3]);
+      store16_nt(unit, word[0], word[1], word[2], word[3]);
     } else if (nmine > 0) {   // the write's first or last chunk: only its own slots
 #pragma unroll
       for (int kk = 0; kk < 16; ++kk)
