@@ -67,7 +67,7 @@ ATT_KERNEL = "attn_pp<128>"
 # (FETCH_SIZE, WRITE_SIZE) over this workload, each divided by the factor the same counter
 # reads for a torch copy of --calibrate-copy bytes.  Valid only for the kernel sources whose
 # hash is recorded; reported as null otherwise.
-ATT_TRAFFIC = {"sources": "c2501b4b05a473f8", "bytes": 124_850_000,
+ATT_TRAFFIC = {"sources": "1ca77da08170c0dc", "bytes": 124_850_000,
                "read_bytes": 98_490_000, "write_bytes": 26_360_000}
 WRITE_BYTES = 2 * N * H * D * 2 + 2 * N * H * D + 2 * N * H * 4
 CLOCK_RAMP_S = 0.5            # untimed layer calls before the warm-up steps (clock ramp)
