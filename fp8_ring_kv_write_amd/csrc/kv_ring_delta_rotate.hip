@@ -89,6 +89,8 @@ __device__ inline void load_units(const uint8_t* tile, const float* srow, int t,
 
 // grid = (tiles, heads), tiles varying fastest (a head's work-groups are consecutive, as
 // head_sync requires): one tile of one head, rotated, requantised with the head's new scale.
+typedef uint32_t nt4_t __attribute__((ext_vector_type(4)));
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void rotate_requantize(
     uint8_t* __restrict__ kc, float* __restrict__ k_scale, RotGeom g, DeltaTable tab, void* sync) {
@@ -122,8 +124,9 @@ __global__ __launch_bounds__(kThreads) void rotate_requantize(
     for (int e = 0; e < 4; ++e)
       o[e] = e4m3x4(v[j][4 * e] * inv, v[j][4 * e + 1] * inv, v[j][4 * e + 2] * inv, v[j][4 * e + 3] * inv);
     const int p = j * kThreads + int(threadIdx.x);
-    *reinterpret_cast<uint4*>(tile + p * 16) = make_uint4(o[0], o[1], o[2], o[3]);
-    if (x.q[j] == 0) srow[x.slot[j]] = scale;
+    // stored non-temporal: streamed to memory rather than held in L2 until the launch ends
+    __builtin_nontemporal_store(nt4_t{o[0], o[1], o[2], o[3]}, reinterpret_cast<nt4_t*>(tile + p * 16));
+    if (x.q[j] == 0) __builtin_nontemporal_store(scale, &srow[x.slot[j]]);
   }
 }
 
