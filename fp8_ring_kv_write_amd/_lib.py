@@ -198,8 +198,9 @@ def _ws(ws, need: int, device, stream_handle: int):
 
 def sync_status(workspace=None, device=None, stream=None) -> int:
     """0 unless a synchronisation wait of the calls made with `workspace` (default: every
-    workspace the binding has pooled for `device`) exceeded its bound (then -9, the outputs of
-    those calls are not to be trusted).  Waits for the device first."""
+    workspace the binding has pooled for `device`) exceeded its bound (then -9: the outputs of
+    those calls are not to be trusted, and the workspace must be zero-filled again before further
+    use).  Waits for the device first."""
     import torch
     dev = torch.device(device if device is not None else "cuda")
     idx = dev.index if dev.index is not None else torch.cuda.current_device()

@@ -149,7 +149,8 @@ size_t kv_ring_workspace_bytes(int32_t op, int32_t heads, int32_t slots, int32_t
 /* Whether any wait of the calls made with `workspace` (device memory) on another work-group of
  * the same launch (a head's record, a split row's count) has exceeded its bound: copies one word
  * of it to the host, waiting for `stream` first.  KV_RING_OK, or
- * KV_RING_ERR_SYNC (the outputs of those calls are then not to be trusted), KV_RING_ERR_NULL,
+ * KV_RING_ERR_SYNC (the outputs of those calls are then not to be trusted, and the workspace must
+ * be zero-filled again before further use: its counts may not be back at zero), KV_RING_ERR_NULL,
  * KV_RING_ERR_ALIGN (workspace not 16-byte aligned), KV_RING_ERR_LAUNCH (a HIP error). */
 int kv_ring_sync_status(const void *workspace, void *stream);
 
