@@ -8,7 +8,8 @@
 // registers and stores K and V codes into the tile layout (V transposed).  The attention's
 // queries are prepared the same way (rotation, the head's absmax, quantisation in the QK
 // product's operand order), in the same launch when the attention follows a write
-// (kv_ring_write_attend).
+// (kv_ring_write_attend): by the write's own work-groups when the queries are the new tokens
+// (same count and positions, head_dim 128), else by query work-groups beside them.
 //
 // Arithmetic is float32 with every product and sum rounded separately (the translation
 // unit is compiled with -ffp-contract=off) so the codes match the CPU oracle bit for bit.

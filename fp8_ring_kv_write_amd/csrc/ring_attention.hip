@@ -624,7 +624,8 @@ __device__ inline void store_partial(const AttnArgs& a, int64_t blk, const Group
 
 // Merge of stored segments by one wavefront, for up to two items at once.  An item is half of a
 // query group of a split row: queries 16 gi .. 16 gi + 15 (stored by wavefront gi / 2 as its group
-// gi % 2) and channel blocks 4 hf .. 4 hf + 3 (half hf of the lane's pieces); a row has 32 items.
+// gi % 2) and half hf of the lane's channel blocks (blocks (D/32) hf .. (D/32) hf + D/32 - 1 of
+// its D/16); a row has 32 items.
 // Each segment weighs 2^(m_s - m) times its sum, m being the largest max (the log-sum-exp merge).
 // Every load of both items is issued before any arithmetic (one memory round trip); the result
 // goes to the output like a row held by one work-group.
