@@ -297,17 +297,45 @@ __device__ inline void quantize_q_half(const QuantQArgs& qa_, const float* __res
   dst[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
 }
 
-// grid = (write blocks + query blocks, heads); each work-group does one or the other (WQ: the
-// write's work-groups prepare the queries too, and there are no query blocks).  A head's
-// work-groups have consecutive indices (x varies fastest), as head_sync requires.
+// Order of the work-groups (block b of head h, x blocks per head; the grid is x by heads and L is
+// its flat index, x varying fastest).  Work-groups are handed to the eight XCDs in turn in flat
+// index order (L to XCD L mod 8), and each XCD starts its own in that order, so XCD L mod 8
+// runs the (L / 8)-th item of its own list.  Each list is head-major (all of head h's items
+// before head h + 1's: head_sync's condition) and holds the same blocks for every head: block b < f (x rounded down to a multiple of 8) on XCD b mod 8, so
+// an XCD loads the rotary rows of its blocks once for all heads rather than every XCD loading
+// every row.  The r = x - f remaining blocks of head h go to XCDs (h r + j) mod 8, j < r, which
+// evens the lists' lengths: XCD c's list then holds exactly the indices L < x * heads with
+// L mod 8 = c.
+struct BlockOfHead { int b, h; };
+__device__ inline BlockOfHead block_of_head(int L, int x, int heads) {
+  const int c = L & 7, k = L >> 3;
+  const int f8 = x >> 3, r = x & 7;
+  // items of XCD c before head h: h * f8 fixed ones plus the remaining blocks m < h * r with
+  // m mod 8 = c
+  auto before = [&](int h) {
+    const int hr = h * r;
+    return h * f8 + (hr > c ? (hr - c + 7) >> 3 : 0);
+  };
+  int h = (int)((8LL * k) / x);
+  h = h < heads - 1 ? h : heads - 1;
+  while (h > 0 && before(h) > k) --h;
+  while (h + 1 < heads && before(h + 1) <= k) ++h;
+  const int o = k - before(h);
+  const int b = o < f8 ? c + 8 * o : 8 * f8 + ((c - h * r) & 7);
+  return {b, h};
+}
+
+// grid = (write blocks + query blocks, heads), taken in the order of block_of_head; each
+// does one or the other (WQ: the write's work-groups prepare the queries too, and there are no
+// query blocks).
 template <int D, bool WQ>
 __global__ __launch_bounds__(kThreads) void quantize_pass(WriteArgs wa, QuantQArgs qa_,
                                                           const float* __restrict__ rope, int32_t heads) {
-  const int h = blockIdx.y;
-  if ((int)blockIdx.x < wa.blocks)
-    write_chunk<D, WQ>(wa, qa_, rope, blockIdx.x, h);
+  const BlockOfHead bh = block_of_head(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x, heads);
+  if (bh.b < wa.blocks)
+    write_chunk<D, WQ>(wa, qa_, rope, bh.b, bh.h);
   else
-    quantize_q_half<D>(qa_, rope, blockIdx.x - wa.blocks, h, heads);
+    quantize_q_half<D>(qa_, rope, bh.b - wa.blocks, bh.h, heads);
 }
 
 }  // namespace
@@ -377,7 +405,7 @@ hipError_t launch_quantize_pass(const WriteArgs& wa, const QuantQArgs& qa_, cons
                        rope, heads);
     return hipGetLastError();
   }
-  dim3 g2(wa.blocks + qa_.blocks, heads);
+  const dim3 g2(wa.blocks + qa_.blocks, heads);
   if (head_dim == 128)
     hipLaunchKernelGGL((quantize_pass<128, false>), g2, dim3(kThreads), 0, stream, wa, qa_, rope, heads);
   else

@@ -151,9 +151,10 @@ __device__ inline float list_max(const float* __restrict__ p, int n, float* red)
 // the waiters.  (Acquire and release orderings would add cache write-backs and invalidations to
 // every poll, with no other data to publish.)
 //
-// The wait cannot deadlock: work-groups start in index order on each XCD and a head's are
-// consecutive, so the lowest unfinished head always has all of its work-groups started or able to
-// start; a head never has more work-groups than fit on one XCD at once.  The wait is bounded all
+// The wait cannot deadlock: work-groups start in index order on each XCD, and on each XCD a
+// head's work-groups all come before the next head's (a grid whose heads are consecutive, or the
+// write's XCD-aware order), so the lowest unfinished head always has all of its work-groups
+// started or able to start; a head never has more work-groups than fit on one XCD at once.  The wait is bounded all
 // the same: past kSpinLimit polls a work-group sets the error word, stops waiting and carries on
 // (its output is then not to be trusted), so every launch ends.
 //

@@ -167,6 +167,19 @@ def test_write_path_full_size_wraps(kv, torch):
     p.assert_same("second write")
 
 
+def test_write_whole_ring_more_work_groups_than_fit(kv, torch):
+    """A write of the whole 5,788-slot ring, 24 heads x d128, from slot 3,001 (it wraps; 181
+    chunks per head): 4,344 work-groups, more than the GPU holds at once, so every per-head
+    wait relies on each XCD starting its heads in order.  Bytes bit-exact, no wait at its
+    bound."""
+    p = Pair(kv, torch, 24, 5788, 128)
+    k = normal_bf16(tensor_seed("whole_ring", 0, 1), (5788, 24, 128))
+    v = normal_bf16(tensor_seed("whole_ring", 0, 2), (5788, 24, 128))
+    p.write(k, v, 3001, 4000)
+    p.assert_same("whole-ring write")
+    assert kv.sync_status() == 0
+
+
 @pytest.mark.parametrize("heads,slots,d,writes", [
     (3, 203, 128, [(1, 0, 0), (203, 5, 1), (7, 200, 300), (64, 101, 400), (130, 150, 600)]),
     (2, 64, 64, [(64, 0, 0), (1, 63, 64), (33, 17, 100)]),
