@@ -9,6 +9,10 @@
 // (each thread 4 (head_dim 128) or 2 (64) 16-byte units of 16 channels, all of its loads in
 // flight at once), rotates it in registers, meets the head's other work-groups (head_sync) for
 // the new absmax, and rewrites its codes and scales.  V is untouched.
+// The meeting needs all of a head's work-groups on the GPU at once (head_sync), so a head takes
+// at most kMaxRotGroups of them: a ring of more tiles per head gives each work-group a run of
+// consecutive tiles, rotated once for the absmax and, after the meeting, read and rotated again
+// to be encoded (two reads of the K codes).
 
 #include "kvring_common.hpp"
 #include "kvring_internal.hpp"
@@ -18,9 +22,11 @@ namespace kvring {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kMaxRotGroups = 1024;   // work-groups per head, at most (128 per XCD)
 
 struct RotGeom {
   int32_t head, filled, slots, heads, nchunks;
+  int32_t tpw;   // tiles per work-group: 1, or more for rings of more than kMaxRotGroups tiles
   int64_t tiles;
 };
 
@@ -87,23 +93,15 @@ __device__ inline void load_units(const uint8_t* tile, const float* srow, int t,
   }
 }
 
-// grid = (tiles, heads), tiles varying fastest (a head's work-groups are consecutive, as
-// head_sync requires): one tile of one head, rotated, requantised with the head's new scale.
+// grid = (work-groups per head, heads), the first varying fastest (a head's work-groups are
+// consecutive, as head_sync requires): g.tpw consecutive tiles of one head (normally one),
+// rotated, requantised with the head's new scale.
 typedef uint32_t nt4_t __attribute__((ext_vector_type(4)));
 
+// The rotated keys of a thread's units, and their absmax over the valid units.
 template <int D>
-__global__ __launch_bounds__(kThreads) void rotate_requantize(
-    uint8_t* __restrict__ kc, float* __restrict__ k_scale, RotGeom g, DeltaTable tab, void* sync) {
-  __shared__ float sl[10];
-  const int t = blockIdx.x, h = blockIdx.y;
-  char* rec = sync_record(sync, 0, h);
-  const unsigned gen = head_sync_generation(rec);
-  uint8_t* tile = kc + ((int64_t)h * g.tiles + t) * kTile * D;
-  float* srow = k_scale + (int64_t)h * g.slots;
-  Units<D> x;
-  load_units<D>(tile, srow, t, g, x);
-  float v[kUnitsPerThread<D>][16];
-  float m = 0.0f, unused = 0.0f;
+__device__ inline float rotate_units(const Units<D>& x, const DeltaTable& tab, float (&v)[kUnitsPerThread<D>][16]) {
+  float m = 0.0f;
 #pragma unroll
   for (int j = 0; j < kUnitsPerThread<D>; ++j) {
     dequant_rotate<16>(x.w[j], x.scale[j], tab, 8 * x.q[j], v[j]);
@@ -111,11 +109,13 @@ __global__ __launch_bounds__(kThreads) void rotate_requantize(
 #pragma unroll
     for (int e = 0; e < 16; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[j][e]));
   }
-  // the head's new absmax; every thread's reads of the old slot scales (above) precede its
-  // barrier, and so the writes below
-  head_sync<kThreads>(rec, gen, sync_error_word(sync), int(g.tiles), false, m, unused, sl);
-  float scale, inv;
-  scale_from_absmax(m, scale, inv);
+  return m;
+}
+
+// Codes and scales of a thread's valid units, encoded with the head's inverse scale.
+template <int D>
+__device__ inline void store_units(uint8_t* tile, float* srow, const Units<D>& x,
+                                   const float (&v)[kUnitsPerThread<D>][16], float scale, float inv) {
 #pragma unroll
   for (int j = 0; j < kUnitsPerThread<D>; ++j) {
     if (!x.ok[j]) continue;
@@ -127,6 +127,52 @@ __global__ __launch_bounds__(kThreads) void rotate_requantize(
     // stored non-temporal: streamed to memory rather than held in L2 until the launch ends
     __builtin_nontemporal_store(nt4_t{o[0], o[1], o[2], o[3]}, reinterpret_cast<nt4_t*>(tile + p * 16));
     if (x.q[j] == 0) __builtin_nontemporal_store(scale, &srow[x.slot[j]]);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void rotate_requantize(
+    uint8_t* __restrict__ kc, float* __restrict__ k_scale, RotGeom g, DeltaTable tab, void* sync) {
+  __shared__ float sl[10];
+  const int h = blockIdx.y;
+  char* rec = sync_record(sync, 0, h);
+  const unsigned gen = head_sync_generation(rec);
+  uint8_t* kh = kc + (int64_t)h * g.tiles * kTile * D;
+  float* srow = k_scale + (int64_t)h * g.slots;
+  float unused = 0.0f;
+  float v[kUnitsPerThread<D>][16];
+  if (g.tpw == 1) {   // one tile, held in registers across the meeting
+    const int t = blockIdx.x;
+    Units<D> x;
+    load_units<D>(kh + (int64_t)t * kTile * D, srow, t, g, x);
+    float m = rotate_units<D>(x, tab, v);
+    // the head's new absmax; every thread's reads of the old slot scales (above) precede its
+    // barrier, and so the writes below
+    head_sync<kThreads>(rec, gen, sync_error_word(sync), int(gridDim.x), false, m, unused, sl);
+    float scale, inv;
+    scale_from_absmax(m, scale, inv);
+    store_units<D>(kh + (int64_t)t * kTile * D, srow, x, v, scale, inv);
+    return;
+  }
+  // a run of tiles: the absmax over them, the meeting, then each tile read, rotated and
+  // encoded again (no other work-group touches these tiles, so the second read sees the codes
+  // and scales the first did)
+  const int64_t t0 = (int64_t)blockIdx.x * g.tpw;
+  const int64_t t1 = min<int64_t>(t0 + g.tpw, g.tiles);
+  float m = 0.0f;
+  for (int64_t t = t0; t < t1; ++t) {
+    Units<D> x;
+    load_units<D>(kh + t * kTile * D, srow, int(t), g, x);
+    m = __builtin_fmaxf(m, rotate_units<D>(x, tab, v));
+  }
+  head_sync<kThreads>(rec, gen, sync_error_word(sync), int(gridDim.x), false, m, unused, sl);
+  float scale, inv;
+  scale_from_absmax(m, scale, inv);
+  for (int64_t t = t0; t < t1; ++t) {
+    Units<D> x;
+    load_units<D>(kh + t * kTile * D, srow, int(t), g, x);
+    rotate_units<D>(x, tab, v);
+    store_units<D>(kh + t * kTile * D, srow, x, v, scale, inv);
   }
 }
 
@@ -144,7 +190,8 @@ hipError_t launch_delta_rotate(const kv_ring_desc& r, int32_t ring_head, int32_t
   g.heads = r.heads;
   g.nchunks = (r.slots + kChunk - 1) / kChunk;
   g.tiles = tile_count(r.slots);
-  dim3 grid(g.tiles, r.heads);
+  g.tpw = int((g.tiles + kMaxRotGroups - 1) / kMaxRotGroups);
+  dim3 grid(int((g.tiles + g.tpw - 1) / g.tpw), r.heads);
   if (r.head_dim == 128)
     hipLaunchKernelGGL(rotate_requantize<128>, grid, dim3(kThreads), 0, stream, r.k, r.k_scale, g, tab, ws);
   else

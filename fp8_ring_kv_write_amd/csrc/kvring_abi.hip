@@ -144,7 +144,8 @@ int kv_ring_write(const kv_ring_desc* ring, const void* k_new, const void* v_new
   if (st) return st;
   if (!k_new || !v_new || !rope_table) return KV_RING_ERR_NULL;
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(rope_table, 16)) return KV_RING_ERR_ALIGN;
-  if (n < 1 || n > ring->slots || start_slot < 0 || start_slot >= ring->slots) return KV_RING_ERR_RANGE;
+  if (n < 1 || n > ring->slots || n > KV_RING_MAX_TOKENS || start_slot < 0 || start_slot >= ring->slots)
+    return KV_RING_ERR_RANGE;
   if (pos0 < 0 || rope_n_pos < 1 || pos0 > rope_n_pos - n) return KV_RING_ERR_POSITION;
   st = check_workspace(workspace, workspace_bytes,
                        kv_ring_workspace_bytes(KV_RING_OP_WRITE, ring->heads, ring->slots, ring->head_dim, n));
@@ -162,7 +163,8 @@ int kv_ring_write_static(const kv_ring_desc* ring, const void* k_new, const void
   if (st) return st;
   if (!k_new || !v_new || !rope_table) return KV_RING_ERR_NULL;
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(rope_table, 16)) return KV_RING_ERR_ALIGN;
-  if (n < 1 || n > ring->slots || start_slot < 0 || start_slot >= ring->slots) return KV_RING_ERR_RANGE;
+  if (n < 1 || n > ring->slots || n > KV_RING_MAX_TOKENS || start_slot < 0 || start_slot >= ring->slots)
+    return KV_RING_ERR_RANGE;
   if (pos0 < 0 || rope_n_pos < 1 || pos0 > rope_n_pos - n) return KV_RING_ERR_POSITION;
   if (kvring::write_workspace_floats(ring->heads, n) > kvring::kWriteStaticScratchFloats)
     return KV_RING_ERR_SCRATCH;
@@ -252,7 +254,8 @@ int ring_attention(const kv_ring_desc* ring, int32_t ring_head, int32_t filled, 
                    size_t workspace_bytes, void* stream) {
   int st = check_ring(ring);
   if (st) return st;
-  if (nq < 0 || ring_head < 0 || ring_head >= ring->slots || filled < 0 || filled > ring->slots)
+  if (nq < 0 || nq > KV_RING_MAX_TOKENS || ring_head < 0 || ring_head >= ring->slots || filled < 0 ||
+      filled > ring->slots)
     return KV_RING_ERR_RANGE;
   if (nq == 0) return KV_RING_OK;   // empty tensors may carry NULL data pointers
   if (!q || !rope_table || !out || !lse) return KV_RING_ERR_NULL;
@@ -278,10 +281,12 @@ int kv_ring_write_attend(const kv_ring_desc* ring, const void* k_new, const void
   // the write's checks
   if (!k_new || !v_new || !rope_table) return KV_RING_ERR_NULL;
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(rope_table, 16)) return KV_RING_ERR_ALIGN;
-  if (n < 1 || n > ring->slots || start_slot < 0 || start_slot >= ring->slots) return KV_RING_ERR_RANGE;
+  if (n < 1 || n > ring->slots || n > KV_RING_MAX_TOKENS || start_slot < 0 || start_slot >= ring->slots)
+    return KV_RING_ERR_RANGE;
   if (pos0 < 0 || rope_n_pos < 1 || pos0 > rope_n_pos - n) return KV_RING_ERR_POSITION;
   // the attention's checks
-  if (nq < 0 || ring_head < 0 || ring_head >= ring->slots || filled < 0 || filled > ring->slots)
+  if (nq < 0 || nq > KV_RING_MAX_TOKENS || ring_head < 0 || ring_head >= ring->slots || filled < 0 ||
+      filled > ring->slots)
     return KV_RING_ERR_RANGE;
   if (nq > 0) {
     if (!q || !out || !lse) return KV_RING_ERR_NULL;

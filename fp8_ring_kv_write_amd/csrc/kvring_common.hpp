@@ -154,7 +154,9 @@ __device__ inline float list_max(const float* __restrict__ p, int n, float* red)
 // The wait cannot deadlock: work-groups start in index order on each XCD, and on each XCD a
 // head's work-groups all come before the next head's (a grid whose heads are consecutive, or the
 // write's XCD-aware order), so the lowest unfinished head always has all of its work-groups
-// started or able to start; a head never has more work-groups than fit on one XCD at once.  The wait is bounded all
+// started or able to start; a head never has more work-groups than fit on one XCD at once (a
+// write or query preparation takes at most KV_RING_MAX_TOKENS tokens, about 130 work-groups per
+// head on each XCD; a rotation gives each head at most 1,024 work-groups, 128 per XCD).  The wait is bounded all
 // the same: past kSpinLimit polls a work-group sets the error word, stops waiting and carries on
 // (its output is then not to be trusted), so every launch ends.
 //

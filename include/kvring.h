@@ -67,6 +67,12 @@ enum {
   KV_RING_ERR_SYNC = -9        /* kv_ring_sync_status: a wait exceeded its bound       */
 };
 
+/* The most new tokens one write takes, and the most queries one attention call takes.  Their
+ * work-groups agree on each head's absmax inside one launch, which needs all of a head's
+ * work-groups on the GPU at once; this bound keeps them within what every XCD holds together
+ * (a delta rotation of any ring the library accepts stays within it by itself). */
+#define KV_RING_MAX_TOKENS 16384
+
 enum {
   KV_RING_OP_WRITE = 1,
   KV_RING_OP_DELTA_ROTATE = 2,
@@ -163,8 +169,8 @@ int kv_ring_sync_status(const void *workspace, void *stream);
  * K is rotated, K and V each get one scale per head over this write, codes and scales are
  * stored.  The caller then sets ring_head = (start_slot + n) % slots and
  * filled = min(filled + n, slots).
- * Errors: NULL pointers, misalignment, 1 <= n <= slots, 0 <= start_slot < slots,
- * 0 <= pos0 and pos0 + n <= rope_n_pos, workspace too small.
+ * Errors: NULL pointers, misalignment, 1 <= n <= min(slots, KV_RING_MAX_TOKENS),
+ * 0 <= start_slot < slots, 0 <= pos0 and pos0 + n <= rope_n_pos, workspace too small.
  */
 int kv_ring_write(const kv_ring_desc *ring, const void *k_new, const void *v_new, int32_t n,
                   int32_t start_slot, int64_t pos0, const float *rope_table, int64_t rope_n_pos,
@@ -190,7 +196,9 @@ int kv_ring_write_static(const kv_ring_desc *ring, const void *k_new, const void
  * Delta rotation when positions reset (abstract: a delta rotation of the cache instead of
  * re-rotating it): every valid K slot is dequantised, rotated by delta positions (cos/sin of
  * delta * theta_i from the C library, in double, rounded to float) and requantised with one
- * new scale per head over all valid slots.  V and invalid slots are untouched.
+ * new scale per head over all valid slots.  V and invalid slots are untouched.  One launch, one
+ * read of the K codes; a ring of more than 1,024 tiles (131,072 slots) is read twice (once for
+ * the absmax, once to encode).
  *   ring_head, filled  the ring's valid interval (0 <= ring_head < slots, 0 <= filled <= slots);
  *   delta              position offset, |delta| < 2^31; rope_base > 0.
  * The caller continues positions from old + delta.
@@ -226,8 +234,9 @@ int kv_ring_delta_rotate_3d(const kv_ring_desc *ring, int32_t ring_head, int32_t
  * The launch is a grid of at most one work-group per compute unit; work-groups sharing a query
  * row wait for one another to merge it, which every device running nothing else (and any on
  * which each XCD can hold the few consecutive work-groups of a row at once) lets finish.
- * Errors: NULL pointers, misalignment, nq < 0, ring_head/filled out of range, softmax_scale not
- * finite and positive, positions outside the table, workspace too small.
+ * Errors: NULL pointers, misalignment, nq < 0 or nq > KV_RING_MAX_TOKENS, ring_head/filled out
+ * of range, softmax_scale not finite and positive, positions outside the table, workspace too
+ * small.
  */
 int ring_attention(const kv_ring_desc *ring, int32_t ring_head, int32_t filled, const void *q,
                    int32_t nq, int64_t q_pos0, const float *rope_table, int64_t rope_n_pos,

@@ -209,6 +209,16 @@ def test_argument_errors_are_reported_before_any_launch(kv):
     assert wa_call(scale=0.0) == -4
     assert wa_call(wsb=wf - 4) == -6
     assert wa_call(desc=_Desc(F, F, F, F, 2, 64, 96)) == -3
+    # more than KV_RING_MAX_TOKENS (16,384) tokens in one write or queries in one attention call:
+    # their per-head meeting would need more work-groups at once than the XCDs hold
+    long_ring = _Desc(F, F, F, F, 2, 1 << 20, 64)
+    ntab = 1 << 16
+    assert L.kv_ring_write(d(long_ring), F, F, 16385, 0, 0, F, ntab, F, 1 << 30, None) == -4
+    assert L.kv_ring_write_static(d(long_ring), F, F, 16385, 0, 0, F, ntab, None) == -4
+    assert L.ring_attention(d(long_ring), 0, 10, F, 16385, 0, F, ntab, 0.125, F, F, F, 1 << 30, None) == -4
+    assert wa_call(desc=long_ring, n=16385, ntab=ntab, wsb=1 << 30) == -4
+    assert wa_call(desc=long_ring, nq=16385, ntab=ntab, wsb=1 << 30) == -4
+    assert wa_call(desc=long_ring, n=16384, nq=16384, ntab=ntab, pos0=ntab) == -5   # checks pass up to the positions
     # window copy of the read-time baseline (src, dst, fresh: 10 rows of 64 bytes each)
     S0, D0, N0 = F, F + (1 << 16), F + (2 << 16)
     assert L.kv_window_advance(S0, D0, N0, 0, 0, 64, None) == -4

@@ -368,6 +368,48 @@ def test_large_ring_long_writes_and_rotation(kv, torch):
     check_attention(*p.attend(q, 6000, 1 / math.sqrt(D)), label="large ring after rotation")
 
 
+def test_largest_head_count(kv, torch):
+    """512 heads (the most the synchronisation records hold) x 300 slots x d64: every head's record
+    in use, writes of 3,584 and 3,072 work-groups taken in the write's XCD order, a rotation, and
+    an attention whose 512 rows outnumber the work-groups.  Bytes bit-exact, attention within the bar, no wait at
+    its bound."""
+    H, S, D = 512, 300, 64
+    p = Pair(kv, torch, H, S, D)
+    for c, (n, start, pos0) in enumerate([(200, 0, 0), (150, 200, 500)]):   # the second wraps
+        k = normal_bf16(tensor_seed("max_heads", c, 1), (n, H, D))
+        v = normal_bf16(tensor_seed("max_heads", c, 2), (n, H, D))
+        p.write(k, v, start, pos0)
+    assert (p.head, p.filled) == (50, 300)
+    p.assert_same("512 heads")
+    kv.kv_ring_delta_rotate(p.g, p.head, p.filled, -50)
+    oracle.ring_delta_rotate(p.o, p.head, p.filled, -50)
+    p.assert_same("512 heads after delta -50")
+    q = normal_bf16(tensor_seed("max_heads", 9, 0), (17, H, D))
+    check_attention(*p.attend(q, 600, 1 / math.sqrt(D)), label="512 heads")
+    assert kv.sync_status() == 0
+
+
+def test_largest_slot_count(kv, torch):
+    """A ring of 2^20 slots (the most a ring may have; 8,192 tiles per head), 2 heads x d128,
+    written near its end so that the last write wraps to slot 0: slot and byte offsets at the
+    top of their range, a rotation and an attention over the wrapped valid interval."""
+    H, S, D, n = 2, 1 << 20, 128, 4000
+    p = Pair(kv, torch, H, S, D)
+    start = S - 6000
+    for c in range(3):                     # slots S-6000 .. S-1, then 0 .. 5,999
+        k = normal_bf16(tensor_seed("max_slots", c, 1), (n, H, D))
+        v = normal_bf16(tensor_seed("max_slots", c, 2), (n, H, D))
+        p.write(k, v, (start + n * c) % S, n * c)
+    assert (p.head, p.filled) == (6000, 12000)
+    p.assert_same("2^20 slots")
+    kv.kv_ring_delta_rotate(p.g, p.head, p.filled, -700)
+    oracle.ring_delta_rotate(p.o, p.head, p.filled, -700)
+    p.assert_same("2^20 slots after delta -700")
+    q = normal_bf16(tensor_seed("max_slots", 9, 0), (5, H, D))
+    check_attention(*p.attend(q, 11000, 1 / math.sqrt(D)), label="2^20 slots")
+    assert kv.sync_status() == 0
+
+
 def test_attention_empty_ring_and_no_queries(kv, torch):
     g = kv.Ring(2, 300, 128)
     tab_dev, _ = tables(kv, torch, 128)
