@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     OP_DELTA_ROTATE,
     OP_ATTENTION,
     OP_WRITE_ATTEND,
+    MAX_TOKENS,
     TILE,
     library_path,
     codes_bytes,

@@ -12,6 +12,7 @@ _LIB_PATH = os.path.join(HERE, "libkvring.so")
 
 OP_WRITE, OP_DELTA_ROTATE, OP_ATTENTION, OP_WRITE_ATTEND = 1, 2, 3, 4
 TILE = 128
+MAX_TOKENS = 16384   # KV_RING_MAX_TOKENS: tokens per write, queries per attention call
 
 
 class KvRingError(RuntimeError):

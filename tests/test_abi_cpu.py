@@ -32,6 +32,15 @@ def test_header_declares_the_three_entry_points():
         assert n in names
 
 
+def test_binding_constants_match_the_header(kv):
+    """The binding's operation codes and token limit are the header's."""
+    text = open(HEADER).read()
+    assert re.search(r"#define KV_RING_MAX_TOKENS (\d+)", text).group(1) == str(kv.MAX_TOKENS)
+    for name, value in (("WRITE", kv.OP_WRITE), ("DELTA_ROTATE", kv.OP_DELTA_ROTATE),
+                        ("ATTENTION", kv.OP_ATTENTION), ("WRITE_ATTEND", kv.OP_WRITE_ATTEND)):
+        assert re.search(rf"KV_RING_OP_{name} = (\d+)", text).group(1) == str(value)
+
+
 def test_library_exports_every_declared_function(kv):
     lib = ctypes.CDLL(kv.library_path())
     missing = [n for n in declared_functions() if not hasattr(lib, n)]
