@@ -410,6 +410,22 @@ def test_largest_slot_count(kv, torch):
     assert kv.sync_status() == 0
 
 
+def test_write_and_attention_at_the_token_limit(kv, torch):
+    """One write of KV_RING_MAX_TOKENS = 16,384 tokens (8 heads x d64 into a 20,000-slot ring,
+    wrapping): 513 work-groups per head, about 65 on each XCD, 4,104 in all, more than the GPU
+    holds at once; then an attention of 16,384 queries (64 rows per head), checked on two heads."""
+    H, S, D, n = 8, 20000, 64, kv.MAX_TOKENS
+    p = Pair(kv, torch, H, S, D)
+    k = normal_bf16(tensor_seed("token_limit", 0, 1), (n, H, D))
+    v = normal_bf16(tensor_seed("token_limit", 0, 2), (n, H, D))
+    p.write(k, v, 10000, 0)
+    assert (p.head, p.filled) == ((10000 + n) % S, n)
+    p.assert_same("16,384-token write")
+    q = normal_bf16(tensor_seed("token_limit", 9, 0), (n, H, D))
+    check_attention(*p.attend(q, 0, 1 / math.sqrt(D), heads=[0, 5]), heads=[0, 5], label="16,384 queries")
+    assert kv.sync_status() == 0
+
+
 def test_attention_empty_ring_and_no_queries(kv, torch):
     g = kv.Ring(2, 300, 128)
     tab_dev, _ = tables(kv, torch, 128)
