@@ -180,3 +180,32 @@ def test_split_row_attention_replays_from_a_captured_graph():
         assert _counts_zero(ws)
         _ = (q.float() * 2).sum().item()   # eager work between replays
     assert kv.sync_status(ws) == 0
+
+
+def test_a_wait_past_its_bound_is_reported_and_cleared_by_zero_fill():
+    """The failure path of the per-head meeting, forced from the host: a zero-filled workspace
+    whose head-0 record holds a stale count of 7 (which no call leaves behind), so the single
+    work-group of a small write never finds itself the last to count in.  It polls until its
+    bound (2^20 polls, about a second), sets the workspace's error word and finishes;
+    kv_ring_sync_status reports it (-9).  Zero-filled again, the workspace serves the same write
+    cleanly, and the ring matches one written with a fresh workspace."""
+    import torch
+    import fp8_ring_kv_write_amd as kv
+    h, s, d, n = 1, 64, 64, 16
+    tab = torch.from_numpy(kv.rope_table(16384, d)).cuda()
+    k = to_dev_bf16(normal_bf16(tensor_seed("sync_bound", 0, 1), (n, h, d)))
+    v = to_dev_bf16(normal_bf16(tensor_seed("sync_bound", 0, 2), (n, h, d)))
+    ws = torch.zeros(kv.workspace_bytes(kv.OP_WRITE, h, s, d, n), dtype=torch.uint8, device="cuda")
+    ws[0] = 7   # the count word (first int32) of slot 0's record for head 0
+    ring = kv.Ring(h, s, d)
+    print("[sync] stale count: one wait runs to its bound", flush=True)
+    kv.kv_ring_write(ring, k, v, 0, 0, tab, workspace=ws)
+    assert kv.sync_status(ws) == -9
+    ws.zero_()
+    kv.kv_ring_write(ring, k, v, 0, 0, tab, workspace=ws)
+    ref = kv.Ring(h, s, d)
+    kv.kv_ring_write(ref, k, v, 0, 0, tab)
+    torch.cuda.synchronize()
+    _same(_ring_state(ring), _ring_state(ref), "the write after the zero-fill")
+    assert kv.sync_status(ws) == 0
+    assert _counts_zero(ws)
