@@ -567,6 +567,7 @@ def test_layer_calls_replay_from_a_captured_graph(kv, torch):
     (3, 700, 128, 16, 129, 5),       # more queries than new tokens
     (2, 300, 64, 100, 1, 4),
     (2, 300, 128, 77, 0, 2),         # no queries: the write alone
+    (8, 20000, 128, 16384, 16384, 1),  # the token limit, the queries prepared by the write's work-groups
 ])
 def test_write_attend_equals_write_then_attention(kv, torch, heads, slots, d, n, nq, writes):
     """kv_ring_write_attend leaves the same ring bytes, outputs and LSE, bit for bit, as
