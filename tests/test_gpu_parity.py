@@ -309,6 +309,20 @@ def test_attention_partial_and_ragged(kv, torch, slots, n, writes, nq):
                     label=f"S={slots} filled={p.filled} nq={nq}")
 
 
+@pytest.mark.parametrize("scale", [1e-3, 2.0, 8.0])
+def test_attention_softmax_scale_extremes(kv, torch, scale):
+    """Softmax scales far from 1/sqrt(d): nearly uniform weights (1e-3) and sharp ones (2 and 8,
+    where a few slots carry almost all the weight and the running max moves by far more than
+    the lazy rescale's threshold), over a wrapped 700-slot ring, 3 heads x d128, 129 queries."""
+    p = Pair(kv, torch, 3, 700, 128)
+    sched = _fill_steady(p, "scale_extremes", 100, 8)
+    q = normal_bf16(tensor_seed("scale_extremes", 9, 0), (129, 3, 128))
+    # The LSE is in units of scaled scores: the bar holds the error of the unscaled score q.k to
+    # what 1e-3 allows at the standard scale 1/sqrt(d), i.e. 1e-3 * scale * sqrt(d) above it.
+    lse_tol = LSE_TOL * max(1.0, scale * math.sqrt(128))
+    check_attention(*p.attend(q, sched[-1].pos0, scale), label=f"softmax scale {scale}", lse_tol=lse_tol)
+
+
 def test_attention_ignores_poisoned_free_slots(kv, torch):
     p = Pair(kv, torch, 2, 700, 128)
     sched = _fill_steady(p, "poison", 100, 4)     # 400 of 700 slots
