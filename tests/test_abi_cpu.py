@@ -53,6 +53,11 @@ def test_rope_table_matches_oracle_bit_for_bit(kv):
         ours = kv.rope_table(300, d)
         ref = rope_table(300, d)
         assert ours.tobytes() == ref.tobytes()
+    # other bases (long-context rotary bases among them), and positions far out in the table
+    for base in (500.0, 500000.0, 1e6):
+        assert kv.rope_table(40, 128, base).tobytes() == rope_table(40, 128, base).tobytes()
+    far = kv.rope_table(16384, 64)[16300:]
+    assert far.tobytes() == rope_table(16384, 64)[16300:].tobytes()
 
 
 def test_rope_table_3d_matches_oracle_bit_for_bit(kv):

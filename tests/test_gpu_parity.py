@@ -223,18 +223,20 @@ def _fill_steady(p, name, n, writes, pos_offset=0, dist="normal", outliers=None)
     return steady_ring_schedule(S, n, writes, pos_offset)
 
 
-@pytest.mark.parametrize("slots,n,writes,delta", [
-    (203, 48, 3, -100),     # partially filled ring
-    (203, 48, 7, 37),       # full, wrapped
-    (203, 48, 2, 0),        # delta 0
+@pytest.mark.parametrize("slots,n,writes,delta,base", [
+    (203, 48, 3, -100, 10000.0),     # partially filled ring
+    (203, 48, 7, 37, 10000.0),       # full, wrapped
+    (203, 48, 2, 0, 10000.0),        # delta 0
+    (203, 48, 7, -1234, 500000.0),   # another rotary base
+    (203, 48, 7, (1 << 31) - 1, 10000.0),   # the largest delta (angles of about 2^31 radians)
 ])
-def test_delta_rotate_small(kv, torch, slots, n, writes, delta):
+def test_delta_rotate_small(kv, torch, slots, n, writes, delta, base):
     p = Pair(kv, torch, 3, slots, 128)
     _fill_steady(p, f"drs{slots}{writes}", n, writes, pos_offset=500)
     p.assert_same("before rotation")
-    kv.kv_ring_delta_rotate(p.g, p.head, p.filled, delta)
-    oracle.ring_delta_rotate(p.o, p.head, p.filled, delta)
-    p.assert_same(f"after delta {delta}")
+    kv.kv_ring_delta_rotate(p.g, p.head, p.filled, delta, rope_base=base)
+    oracle.ring_delta_rotate(p.o, p.head, p.filled, delta, base=base)
+    p.assert_same(f"after delta {delta} (base {base})")
 
 
 def test_reset_outliers_one_layer_full_size(kv, torch):
