@@ -144,6 +144,51 @@ def _ptr(t) -> int:
     return int(t.data_ptr())
 
 
+def _same_device(t, device) -> bool:
+    d = t.device
+    if isinstance(device, str):
+        import torch
+        device = torch.device(device)
+    return d.type == device.type and (device.index is None or d.index == device.index)
+
+
+def _need(name: str, t, dtype, shape: tuple, device) -> None:
+    """Raise ValueError unless tensor t has the dtype, the shape, a contiguous layout and the
+    device the call will hand to the library: the kernels read and write exactly that many
+    elements at the tensor's address."""
+    try:
+        ok = t.dtype == dtype
+        got = t.shape
+    except AttributeError:
+        raise ValueError(f"{name}: expected a torch tensor") from None
+    if not ok:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if got != shape:
+        raise ValueError(f"{name}: shape {tuple(got)}, expected {shape}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: contiguous tensors only")
+    if t.device != device and not _same_device(t, device):
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+
+
+def _need_rope(rope, head_dim: int, device) -> None:
+    """A rotary table of this head_dim: float32 [n_pos, head_dim/2, 2] or [n_pos, head_dim]."""
+    import torch
+    try:
+        n_pos = rope.shape[0]
+        shape = (n_pos, head_dim // 2, 2) if rope.dim() == 3 else (n_pos, head_dim)
+    except (AttributeError, IndexError):
+        raise ValueError("rope: expected a [n_pos, head_dim/2, 2] float32 tensor") from None
+    _need("rope", rope, torch.float32, shape, device)
+
+
+def _need_workspace(ws, device) -> None:
+    if ws is None:
+        return
+    if not ws.is_contiguous() or not _same_device(ws, device):
+        raise ValueError(f"workspace: a contiguous tensor on {device} expected")
+
+
 class Ring:
     """Device buffers of one ring (one layer, `heads` heads), allocated with torch.
 
@@ -162,6 +207,7 @@ class Ring:
         self.v = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
         self.k_scale = torch.ones((heads, slots), dtype=torch.float32, device=self.device)
         self.v_scale = torch.ones((heads, slots), dtype=torch.float32, device=self.device)
+        self.device = self.k.device   # with its index (cuda:N), as the tensors handed in report it
         self._desc = _Desc(_ptr(self.k), _ptr(self.v), _ptr(self.k_scale), _ptr(self.v_scale),
                            heads, slots, head_dim)
 
@@ -222,7 +268,12 @@ def sync_status(workspace=None, device=None, stream=None) -> int:
 def kv_ring_write(ring: Ring, k_new, v_new, start_slot: int, pos0: int, rope, workspace=None,
                   stream=None) -> None:
     """k_new, v_new: bfloat16 [n, heads, head_dim] device tensors; rope: device float32 table."""
+    import torch
     n = int(k_new.shape[0])
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _need(name, t, torch.bfloat16, (n, ring.heads, ring.head_dim), ring.device)
+    _need_rope(rope, ring.head_dim, ring.device)
+    _need_workspace(workspace, ring.device)
     need = workspace_bytes(OP_WRITE, ring.heads, ring.slots, ring.head_dim, max(n, 1))
     st = _stream(stream, ring.device)
     ws, wsb = _ws(workspace, need, ring.device, st)
@@ -233,7 +284,11 @@ def kv_ring_write(ring: Ring, k_new, v_new, start_slot: int, pos0: int, rope, wo
 
 def kv_ring_write_static(ring: Ring, k_new, v_new, start_slot: int, pos0: int, rope, stream=None) -> None:
     """kv_ring_write with the library's static scratch instead of a workspace (allocates nothing)."""
+    import torch
     n = int(k_new.shape[0])
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _need(name, t, torch.bfloat16, (n, ring.heads, ring.head_dim), ring.device)
+    _need_rope(rope, ring.head_dim, ring.device)
     _check("kv_ring_write_static", lib.kv_ring_write_static(
         ring.desc, _ptr(k_new), _ptr(v_new), n, start_slot, pos0, _ptr(rope), int(rope.shape[0]),
         _stream(stream, ring.device)))
@@ -241,6 +296,7 @@ def kv_ring_write_static(ring: Ring, k_new, v_new, start_slot: int, pos0: int, r
 
 def kv_ring_delta_rotate(ring: Ring, ring_head: int, filled: int, delta: int,
                          rope_base: float = 10000.0, workspace=None, stream=None) -> None:
+    _need_workspace(workspace, ring.device)
     need = workspace_bytes(OP_DELTA_ROTATE, ring.heads, ring.slots, ring.head_dim, 0)
     st = _stream(stream, ring.device)
     ws, wsb = _ws(workspace, need, ring.device, st)
@@ -253,6 +309,7 @@ def kv_ring_delta_rotate_3d(ring: Ring, ring_head: int, filled: int, delta, band
     """Delta rotation by the (frame, row, column) offset triple `delta`."""
     d = np.ascontiguousarray(np.asarray(delta, dtype=np.int64).reshape(3))
     keep, bp = _bands_arg(band_pairs)
+    _need_workspace(workspace, ring.device)
     need = workspace_bytes(OP_DELTA_ROTATE, ring.heads, ring.slots, ring.head_dim, 0)
     st = _stream(stream, ring.device)
     ws, wsb = _ws(workspace, need, ring.device, st)
@@ -267,10 +324,15 @@ def ring_attention(ring: Ring, ring_head: int, filled: int, q, q_pos0: int, rope
     lse float32 [heads, nq])."""
     import torch
     nq = int(q.shape[0])
+    _need("q", q, torch.bfloat16, (nq, ring.heads, ring.head_dim), ring.device)
+    _need_rope(rope, ring.head_dim, ring.device)
+    _need_workspace(workspace, ring.device)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((ring.heads, nq), dtype=torch.float32, device=q.device)
+    _need("out", out, torch.bfloat16, (nq, ring.heads, ring.head_dim), ring.device)
+    _need("lse", lse, torch.float32, (ring.heads, nq), ring.device)
     need = workspace_bytes(OP_ATTENTION, ring.heads, ring.slots, ring.head_dim, max(nq, 1))
     st = _stream(stream, ring.device)
     ws, wsb = _ws(workspace, need, ring.device, st)
@@ -287,10 +349,17 @@ def kv_ring_write_attend(ring: Ring, k_new, v_new, start_slot: int, pos0: int, r
     write).  Returns (out, lse) like ring_attention."""
     import torch
     n, nq = int(k_new.shape[0]), int(q.shape[0])
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _need(name, t, torch.bfloat16, (n, ring.heads, ring.head_dim), ring.device)
+    _need("q", q, torch.bfloat16, (nq, ring.heads, ring.head_dim), ring.device)
+    _need_rope(rope, ring.head_dim, ring.device)
+    _need_workspace(workspace, ring.device)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((ring.heads, nq), dtype=torch.float32, device=q.device)
+    _need("out", out, torch.bfloat16, (nq, ring.heads, ring.head_dim), ring.device)
+    _need("lse", lse, torch.float32, (ring.heads, nq), ring.device)
     need = workspace_bytes(OP_WRITE_ATTEND, ring.heads, ring.slots, ring.head_dim, max(n, nq, 1))
     st = _stream(stream, ring.device)
     ws, wsb = _ws(workspace, need, ring.device, st)
@@ -304,8 +373,12 @@ def kv_ring_write_attend(ring: Ring, k_new, v_new, start_slot: int, pos0: int, r
 def fp8_encode(x, out=None, stream=None):
     """E4M3 codes of a float32 device tensor with the kernels' encoder."""
     import torch
+    _need("x", x, torch.float32, tuple(x.shape), x.device)
+    if x.device.type != "cuda":
+        raise ValueError("x: a device tensor expected")
     if out is None:
         out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _need("out", out, torch.uint8, tuple(x.shape), x.device)
     _check("kv_ring_fp8_encode", lib.kv_ring_fp8_encode(_ptr(x), _ptr(out), int(x.numel()),
                                                         _stream(stream, x.device)))
     return out

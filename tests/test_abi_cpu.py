@@ -291,3 +291,36 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_binding_rejects_tensors_the_kernels_would_overrun(kv):
+    """The binding checks every tensor's dtype, shape, layout and device before it hands the
+    pointer to the library (which trusts it): a wrong head count, head_dim or rotary table
+    would make the kernels read or write past the tensor.  Host tensors stand in for device ones
+    here, and a ring on the device, so every call below must raise before the library is
+    called."""
+    import types
+    import torch
+    ring = types.SimpleNamespace(heads=2, slots=64, head_dim=64, device=torch.device("cuda"), desc=None)
+    k = torch.zeros((16, 2, 64), dtype=torch.bfloat16)
+    q = torch.zeros((8, 2, 64), dtype=torch.bfloat16)
+    rope = torch.zeros((128, 32, 2), dtype=torch.float32)
+    bad_calls = [
+        lambda: kv.kv_ring_write(ring, k.float(), k, 0, 0, rope),                 # dtype
+        lambda: kv.kv_ring_write(ring, k[:, :1].contiguous(), k, 0, 0, rope),     # head count
+        lambda: kv.kv_ring_write(ring, k, torch.zeros((16, 2, 32), dtype=torch.bfloat16), 0, 0, rope),
+        lambda: kv.kv_ring_write(ring, k.transpose(1, 2), k, 0, 0, rope),         # layout
+        lambda: kv.kv_ring_write(ring, k, k, 0, 0, rope),                         # device
+        lambda: kv.kv_ring_write(ring, k, k, 0, 0, torch.zeros((128, 64, 2))),    # table width
+        lambda: kv.kv_ring_write_static(ring, k, k[:8], 0, 0, rope),              # token counts
+        lambda: kv.ring_attention(ring, 0, 16, q.half(), 0, rope, 0.125),
+        lambda: kv.ring_attention(ring, 0, 16, q, 0, rope, 0.125, out=torch.empty((4, 2, 64), dtype=torch.bfloat16)),
+        lambda: kv.ring_attention(ring, 0, 16, q, 0, rope, 0.125, lse=torch.empty((2, 4))),
+        lambda: kv.kv_ring_write_attend(ring, k, k, 0, 0, 16, 16, q[:, :1], 0, rope, 0.125),
+        lambda: kv.kv_ring_delta_rotate(ring, 0, 16, 5, workspace=torch.zeros(64, dtype=torch.uint8)),
+        lambda: kv.fp8_encode(torch.zeros(16)),                                   # host tensor
+    ]
+    for i, call in enumerate(bad_calls):
+        with pytest.raises(ValueError):
+            call()
+            pytest.fail(f"call {i} was not rejected")
